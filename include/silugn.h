@@ -1,0 +1,178 @@
+/*
+ * silugn.h -- C ABI of libsilugn.so: GroupNorm + SiLU and the causal / upsample /
+ * head convolutions of a Wan2.2-style video VAE decoder, as gfx950 (MI355X) HIP
+ * kernels.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Activations are bf16 (passed as uint16_t bit patterns), channels-last
+ *   (N, T, H, W, C), dense, with C the contiguous dimension. C % 8 == 0 so that
+ *   a position's channels split into 16-byte packets of 8 channels; every
+ *   tensor pointer must be 16-byte aligned.
+ * - All tensor pointers are DEVICE pointers owned by the caller; inputs are
+ *   read only. Except for upsample2x_prepare_weights (host memory, host
+ *   compute), the library allocates nothing, keeps no state between calls and
+ *   never synchronises the host: work is enqueued on the caller's stream and
+ *   ordered by it.
+ * - Return value: 0 on success, a negative SGN_E* code otherwise. Arguments are
+ *   validated on the host before anything is enqueued, so an error leaves every
+ *   output untouched. sgn_last_error() gives the calling thread's last message.
+ * - Results are deterministic: partial sums are combined in a fixed order and
+ *   no floating-point atomics are used.
+ */
+#ifndef SILUGN_H
+#define SILUGN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  SGN_OK = 0,
+  SGN_EINVAL = -1,      /* bad size, null required pointer, unsupported shape */
+  SGN_EALIGN = -2,      /* a tensor pointer is not 16-byte aligned */
+  SGN_EALIAS = -3,      /* an output overlaps an input it may not overlap */
+  SGN_ELAUNCH = -4,     /* the HIP runtime refused a launch (message has the HIP error) */
+  SGN_EWORKSPACE = -5   /* workspace missing or smaller than *_workspace() asks for */
+};
+
+/* Dimensions of a channels-last activation tensor. */
+typedef struct {
+  int64_t n, t, h, w, c;
+} sgn_dims;
+
+/*
+ * GroupNorm parameters for a convolution that applies silu(group_norm(x)) to
+ * its input while loading it (see causal_conv3d). stats is the output of
+ * gn_silu_stats for the same x; gamma/beta are fp32 [C]; eps as in gn_silu_apply.
+ */
+typedef struct {
+  const double* stats;
+  const float* gamma;
+  const float* beta;
+  float eps;
+  int groups;
+} sgn_gn;
+
+/* Message of the calling thread's last failed call ("" if none). Never NULL. */
+const char* sgn_last_error(void);
+
+/*
+ * Bytes of device workspace gn_silu_stats needs for dims d and `groups`
+ * (per-block fp64 partial sums). 0 if the arguments are invalid.
+ */
+size_t gn_silu_stats_workspace(sgn_dims d, int groups);
+
+/*
+ * gn_silu_stats -- GroupNorm statistics of x.
+ * Defined by: WanGP group_norm_silu.py page, module docstring (per-group sums
+ * of a span in compensated fp32, reduced in fp64 in a fixed order) and its
+ * apply kernel (variance = mean of squared deviations, divided by the length).
+ *
+ * For every sample n and group g (channels [g*C/G, (g+1)*C/G), all T*H*W
+ * positions of this call's x -- statistics never include a causal cache):
+ *   stats[(n*G + g)*2 + 0] = mean,  stats[(n*G + g)*2 + 1] = biased variance,
+ * both fp64. x: bf16 (N,T,H,W,C). ws: device workspace of at least
+ * gn_silu_stats_workspace(d, groups) bytes, overwritten. C % groups == 0 and
+ * C/groups must be 1, 2, 4 or a multiple of 8; C <= 2048.
+ */
+int gn_silu_stats(const uint16_t* x, sgn_dims d, int groups, double* stats,
+                  void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * gn_silu_apply -- y = silu(group_norm(x)), one rounding to bf16.
+ * Defined by: WanGP group_norm_silu.py page, module docstring ("GroupNorm and
+ * SiLU in FP32, one rounding to the output dtype") and its third pass.
+ *
+ *   z = (x - mean_g) * gamma_c / sqrt(var_g + eps) + beta_c   (computed in fp64)
+ *   y = RNE_bf16( z * sigmoid(z) )
+ * stats from gn_silu_stats; gamma, beta fp32 [C] (device); eps > 0 is used as
+ * the exact fp64 value of the given float. y may equal x (in place); any other
+ * overlap is SGN_EALIAS. Accuracy: within 1 bf16 ulp of the fp64 result rounded
+ * once (finite inputs).
+ */
+int gn_silu_apply(const uint16_t* x, sgn_dims d, int groups, const double* stats,
+                  const float* gamma, const float* beta, float eps, uint16_t* y,
+                  hipStream_t stream);
+
+/*
+ * causal_conv3d -- causal 3x3x3 convolution with a 2-frame temporal cache.
+ * Defined by: FastVideo wan22_vae_decode binding.cpp page, Decoder::conv (front
+ * temporal padding of kt-1 = 2 frames taken from the per-conv cache, spatial
+ * zero padding kh/2 = kw/2 = 1, the cache keeps the last 2 frames of the padded
+ * input) and Decoder::resnet (bias and residual added to the conv output).
+ *
+ *   P = cat_T(cache_in, a),  a = x, or silu(group_norm(x)) when fuse != NULL
+ *   y[n,t,h,w,k] = RNE_bf16( bias[k] + residual[n,t,h,w,k]
+ *        + sum_{dt,dh,dw in 0..2} sum_c w[k,dt,dh,dw,c] * P[n, t+dt, h+dh-1, w+dw-1, c] )
+ * with P zero outside the frame, bf16 products accumulated in fp32.
+ *   x         bf16 (N,T,H,W,C), T >= 1
+ *   cache_in  bf16 (N,2,H,W,C) already-activated frames preceding x, or NULL (zeros)
+ *   w         bf16 (K,3,3,3,C): tap (dt,dh,dw) with dt = 0 the oldest frame
+ *   bias      fp32 [K] or NULL; residual bf16 (N,T,H,W,K) or NULL
+ *   fuse      NULL, or the GroupNorm of x to apply in the operand load; the
+ *             result is bitwise equal to gn_silu_apply followed by this call
+ *             with fuse == NULL
+ *   y         bf16 (N,T,H,W,K); must not overlap x, cache_in, residual or w
+ *   cache_out bf16 (N,2,H,W,C) = P[:, T:T+2] (activated when fused), or NULL;
+ *             must not overlap cache_in, x or y
+ * Requires C % 64 == 0, 1 <= K <= 4096.
+ */
+int causal_conv3d(const uint16_t* x, sgn_dims d, const uint16_t* cache_in,
+                  const uint16_t* w, int k, const float* bias, const uint16_t* residual,
+                  const sgn_gn* fuse, uint16_t* y, uint16_t* cache_out, hipStream_t stream);
+
+/*
+ * upsample2x_prepare_weights -- HOST function: the four 2x2 phase kernels of a
+ * nearest-x2 + 3x3 convolution.
+ * Defined by: binding.cpp page, prepare() ("Nearest-x2 + 3x3 convolution equals
+ * four 2x2 low-resolution phases"; sums formed in fp32, stored in bf16).
+ *
+ * For output phase (a,b) in {0,1}^2 and phase tap (u,v) in {0,1}^2:
+ *   w_phase[a][b][k][u][v][c] = RNE_bf16( sum of w3x3[k][r][s][c] over the taps
+ *       with floor((a+r-1)/2) == u+a-1 and floor((b+s-1)/2) == v+b-1 ),
+ * the sum taken in fp32. w3x3: host bf16 (K,3,3,C); w_phase: host bf16
+ * (2,2,K,2,2,C), i.e. 16*K*C values.
+ */
+int upsample2x_prepare_weights(const uint16_t* w3x3, int k, int c, uint16_t* w_phase);
+
+/*
+ * upsample2x_conv_phases -- nearest-x2 upsample + 3x3 convolution, computed as
+ * four 2x2 convolutions at the low resolution.
+ * Defined by: binding.cpp page, prepare() (phase weights) and Decoder::up (the
+ * four phase convolutions, then the interleave with the bias).
+ *
+ *   y[n,t,2i+a,2j+b,k] = RNE_bf16( bias[k] + sum_{u,v,c}
+ *        w_phase[a][b][k][u][v][c] * x[n, t, i+u+a-1, j+v+b-1, c] ),  zero outside.
+ * Per frame (no temporal taps, no cache). x bf16 (N,T,H,W,C); w_phase device bf16
+ * from upsample2x_prepare_weights; bias fp32 [K] or NULL; y bf16 (N,T,2H,2W,K),
+ * written interleaved, must not overlap x or w_phase. Requires C % 64 == 0.
+ */
+int upsample2x_conv_phases(const uint16_t* x, sgn_dims d, const uint16_t* w_phase, int k,
+                           const float* bias, uint16_t* y, hipStream_t stream);
+
+/*
+ * head_conv_d2s -- the decoder's output head: causal 3x3x3 convolution to 12
+ * channels followed by a 2x2 depth-to-space into an RGB video.
+ * Defined by: binding.cpp page, Decoder::output_head (norm + SiLU + causal pad,
+ * the convolution to 12 = 3 x 2 x 2 channels, bias and clamp) and the video
+ * write of decode_video.
+ *
+ *   o = causal_conv3d(x, cache_in, w, K=12, bias, fuse) in fp32 (before rounding)
+ *   video[n, c, t, 2h+dy, 2w+dx] = RNE_bf16( clamp?( o[n,t,h,w, 4c+2dy+dx] ) )
+ * with clamp to [-1, 1] when clamp != 0. video: bf16 (N,3,T,2H,2W) dense
+ * (channels-first). cache_out as in causal_conv3d. Requires C % 64 == 0.
+ */
+int head_conv_d2s(const uint16_t* x, sgn_dims d, const uint16_t* cache_in, const uint16_t* w,
+                  const float* bias, const sgn_gn* fuse, int clamp, uint16_t* video,
+                  uint16_t* cache_out, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SILUGN_H */

@@ -1,0 +1,662 @@
+// Implicit-GEMM convolutions on bf16 MFMA (gfx950): the causal 3x3x3 convolution with
+// its 2-frame cache, the nearest-x2 upsample as four 2x2 phase convolutions, and the
+// output head with its 2x2 depth-to-space.
+//
+// GEMM view (per sample, per upsample phase):
+//   D[k][m] = sum_{tap, c} W[k][tap][c] * P[src(m, tap)][c]
+// with m an output position, k an output channel and src(m, tap) the input position a
+// tap reads (or a zero row for padding). A workgroup of 4 waves computes a BN x BM
+// tile of D; each k-step moves BN weight rows and BM position rows of 64 channels
+// (128 bytes each) from global memory straight into LDS (global_load_lds_dwordx4: no
+// VGPR round trip), double buffered, and every wave runs v_mfma_f32_32x32x16_bf16 on
+// its sub-tile. The 16-byte chunks of each 128-byte LDS row are XOR-swizzled by the
+// row index so that the MFMA operand reads (ds_read_b128) are bank-conflict free.
+// With GroupNorm fused, position rows of the current frames go through VGPRs instead:
+// loaded, activated by the same activate_packet() as gn_silu_apply (so the result is
+// bitwise that of apply-then-convolve), and written to the same swizzled slots.
+//
+// Pages: FastVideo wan22_vae_decode binding.cpp -- Decoder::conv (causal front padding
+// of kt-1 frames from the cache, 1-pixel spatial zero padding, the cache keeps the last
+// 2 frames of the padded input, bias and residual in the epilogue), prepare() and
+// Decoder::up (the four 2x2 phase convolutions of nearest-x2 + 3x3, interleaved with the
+// bias), Decoder::output_head (the head convolution to 12 = 3 x 2 x 2 channels, bias,
+// clamp) and decode_video's write of the 2x2-unfolded RGB video.
+#include <math.h>
+#include <stdio.h>
+
+#include "common.hpp"
+#include "host.hpp"
+#include "silugn.h"
+
+namespace sgn {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+
+constexpr int kBK = 64;          // channels per k-step
+constexpr int kCMax = 4096;      // largest C: the zero row below covers one position
+constexpr int kConvThreads = 256;
+
+// One position's worth of zeros: padding rows are loaded from here.
+__device__ __align__(256) uint16_t g_zero_row[kCMax];
+
+enum Mode { kCausal = 0, kPhase = 1, kHead = 2 };
+
+struct ConvParams {
+  const uint16_t* x;
+  const uint16_t* cache;     // (N,2,H,W,C) or null
+  const uint16_t* w;         // (K,taps,C), or for phases (4,K,4,C)
+  const float* bias;         // [K] or null
+  const uint16_t* res;       // (N,T,H,W,K) or null
+  uint16_t* y;
+  const double* stats;       // fused GroupNorm (null when not fused)
+  const float* gamma;
+  const float* beta;
+  double eps;
+  int groups;
+  int T, H, W, C, K;
+  int tiles_m, tiles_n;
+  int64_t mper;              // output positions per sample (and per phase)
+  int nblocks;
+  int clamp;
+};
+
+__device__ __forceinline__ void lds_dma16(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+}
+
+template <int BM, int BN, int WGM, int WGN, int MODE, bool FUSE>
+__global__ __launch_bounds__(kConvThreads, 1) void conv_kernel(ConvParams p) {
+  constexpr int TAPS = MODE == kPhase ? 4 : 27;
+  constexpr int WTM = BM / WGM, WTN = BN / WGN;
+  constexpr int TM = WTM / 32, TN = WTN / 32;
+  static_assert(TM * 32 * WGM == BM && TN * 32 * WGN == BN && WGM * WGN == 4, "tile shape");
+  constexpr int STAGE = (BN + BM) * 128;
+  constexpr int IA = BN / 8, IB = BM / 8;            // 64-lane DMA instructions per k-step
+  constexpr int IAW = (IA + 3) / 4, IBW = (IB + 3) / 4;
+
+  extern __shared__ __align__(16) char smem[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+  // Workgroup -> tile. Workgroups are dealt to the 8 XCDs round-robin; renumber so that
+  // each XCD works through a contiguous run of tiles (neighbouring tiles share input
+  // rows and weights in that XCD's L2). Order inside a run: N tile, phase, M tile, sample.
+  int tile;
+  {
+    const int bid = blockIdx.x, nb = p.nblocks;
+    const int xcd = bid & 7, idx = bid >> 3, q = nb >> 3, r = nb & 7;
+    tile = xcd < r ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
+  }
+  const int ntile = tile % p.tiles_n;
+  tile /= p.tiles_n;
+  int phase = 0;
+  if (MODE == kPhase) {
+    phase = tile & 3;
+    tile >>= 2;
+  }
+  const int mtile = tile % p.tiles_m;
+  const int n = tile / p.tiles_m;
+  const int pa = phase >> 1, pb = phase & 1;
+
+  const int C = p.C, K = p.K, H = p.H, W = p.W, T = p.T;
+  const int kpt = C / kBK;
+  const int KS = TAPS * kpt;
+  const int lc = (lane & 7) ^ (lane >> 3);           // logical 16-byte chunk this lane moves
+
+  // Weight rows: consecutive k-steps are consecutive 64-channel slices of a row.
+  const uint16_t* wbase = p.w + (MODE == kPhase ? (int64_t)phase * K * 4 * C : 0);
+  int woff[IAW];
+#pragma unroll
+  for (int j = 0; j < IAW; ++j) {
+    const int qi = wave + 4 * j;
+    int row = qi * 8 + (lane >> 3);
+    int k = ntile * BN + row;
+    if (k > K - 1) k = K - 1;                        // columns past K are computed, never stored
+    woff[j] = k * TAPS * C + lc * 8;
+  }
+
+  // Position rows of this lane: (t, h, w) of output position m.
+  int rt[IBW], rhw[IBW];
+#pragma unroll
+  for (int j = 0; j < IBW; ++j) {
+    const int qi = wave + 4 * j;
+    int64_t m = (int64_t)mtile * BM + qi * 8 + (lane >> 3);
+    if (m > p.mper - 1) m = p.mper - 1;              // rows past the end: computed, never stored
+    const int w_ = (int)(m % W);
+    const int64_t th = m / W;
+    const int h_ = (int)(th % H);
+    rt[j] = (int)(th / H);
+    rhw[j] = (h_ << 16) | w_;
+  }
+
+  const uint16_t* rptr[IBW];
+  int rkind[IBW];                                    // 0 activate, 1 copy, 2 zero (fused path)
+  auto set_tap = [&](int tap) {
+    int dt, dh, dw;
+    if (MODE == kPhase) {
+      dt = 2;
+      dh = (tap >> 1) + pa;                          // row offset u + a - 1, stored +1
+      dw = (tap & 1) + pb;
+    } else {
+      dt = tap / 9;
+      dh = (tap / 3) % 3;
+      dw = tap % 3;
+    }
+#pragma unroll
+    for (int j = 0; j < IBW; ++j) {
+      const int tt = rt[j] + dt - 2;
+      const int hh = (rhw[j] >> 16) + dh - 1;
+      const int ww = (rhw[j] & 0xffff) + dw - 1;
+      const bool inside = (unsigned)hh < (unsigned)H && (unsigned)ww < (unsigned)W;
+      const uint16_t* ptr = g_zero_row + lc * 8;
+      int kind = 2;
+      if (inside && tt >= 0) {
+        ptr = p.x + ((((int64_t)n * T + tt) * H + hh) * W + ww) * C + lc * 8;
+        kind = 0;
+      } else if (inside && p.cache) {
+        ptr = p.cache + ((((int64_t)n * 2 + tt + 2) * H + hh) * W + ww) * C + lc * 8;
+        kind = 1;
+      }
+      rptr[j] = ptr;
+      rkind[j] = kind;
+    }
+  };
+
+  // Fused GroupNorm: per-channel fp64 affines of this sample, kept in LDS.
+  double* tab = reinterpret_cast<double*>(smem + 2 * STAGE);
+  if (FUSE) {
+    const int cg = C / p.groups;
+    for (int c = tid; c < C; c += kConvThreads) {
+      const Affine a = channel_affine(p.stats, p.gamma, p.beta, p.eps, p.groups, cg, n, c);
+      tab[2 * c] = a.s;
+      tab[2 * c + 1] = a.b;
+    }
+  }
+
+  uint4 held[FUSE ? IBW : 1];
+  auto issue = [&](int ks, int stage) {
+    char* lw = smem + stage * STAGE;
+    char* lp = lw + BN * 128;
+    const int c0 = (ks % kpt) * kBK;
+#pragma unroll
+    for (int j = 0; j < IAW; ++j) {
+      const int qi = wave + 4 * j;
+      if (qi < IA) lds_dma16(wbase + woff[j] + ks * kBK, lw + qi * 1024);
+    }
+#pragma unroll
+    for (int j = 0; j < IBW; ++j) {
+      const int qi = wave + 4 * j;
+      if (qi < IB) {
+        if (FUSE)
+          held[j] = *reinterpret_cast<const uint4*>(rptr[j] + c0);
+        else
+          lds_dma16(rptr[j] + c0, lp + qi * 1024);
+      }
+    }
+  };
+  // Fused path: activate the held position packets and store them into the stage.
+  auto commit = [&](int ks, int stage) {
+    if (!FUSE) return;
+    char* lp = smem + stage * STAGE + BN * 128;
+    const int c0 = (ks % kpt) * kBK + lc * 8;
+    Affine a[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      a[i].s = tab[2 * (c0 + i)];
+      a[i].b = tab[2 * (c0 + i) + 1];
+    }
+#pragma unroll
+    for (int j = 0; j < IBW; ++j) {
+      const int qi = wave + 4 * j;
+      if (qi < IB) {
+        uint4 v = held[j];
+        if (rkind[j] == 0) v = activate_packet(v, a);
+        *reinterpret_cast<uint4*>(lp + qi * 1024 + lane * 16) = v;
+      }
+    }
+  };
+
+  f32x16 acc[TN][TM];
+#pragma unroll
+  for (int i = 0; i < TN; ++i)
+#pragma unroll
+    for (int j = 0; j < TM; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  const int wm = wave % WGM, wn = wave / WGM;
+  if (FUSE) __syncthreads();                         // affine table visible
+  set_tap(0);
+  issue(0, 0);
+  if (FUSE) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    commit(0, 0);
+  }
+
+  for (int ks = 0; ks < KS; ++ks) {
+    const int stage = ks & 1;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    const bool more = ks + 1 < KS;
+    if (more) {
+      if ((ks + 1) % kpt == 0) set_tap((ks + 1) / kpt);
+      issue(ks + 1, stage ^ 1);
+    }
+    const char* la = smem + stage * STAGE;
+    const char* lb = la + BN * 128;
+#pragma unroll
+    for (int kk = 0; kk < kBK / 16; ++kk) {
+      const int chunk = ((kk * 2 + (lane >> 5)) ^ (lane & 7)) * 16;
+      bf16x8 af[TN], bfr[TM];
+#pragma unroll
+      for (int i = 0; i < TN; ++i)
+        af[i] = *reinterpret_cast<const bf16x8*>(la + (wn * WTN + i * 32 + (lane & 31)) * 128 + chunk);
+#pragma unroll
+      for (int j = 0; j < TM; ++j)
+        bfr[j] = *reinterpret_cast<const bf16x8*>(lb + (wm * WTM + j * 32 + (lane & 31)) * 128 + chunk);
+#pragma unroll
+      for (int i = 0; i < TN; ++i)
+#pragma unroll
+        for (int j = 0; j < TM; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+    if (FUSE && more) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      commit(ks + 1, stage ^ 1);
+    }
+  }
+
+  // Epilogue. Lane l of a 32x32 tile holds column m = l % 32 and rows
+  // k = 8 * (r / 4) + 4 * (l / 32) + r % 4 of accumulator element r.
+#pragma unroll
+  for (int j = 0; j < TM; ++j) {
+    const int64_t m = (int64_t)mtile * BM + wm * WTM + j * 32 + (lane & 31);
+    if (m >= p.mper) continue;
+    const int w_ = (int)(m % W);
+    const int64_t th = m / W;
+    const int h_ = (int)(th % H);
+    const int t_ = (int)(th / H);
+#pragma unroll
+    for (int i = 0; i < TN; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int k0 = ntile * BN + wn * WTN + i * 32 + 8 * q + 4 * (lane >> 5);
+        if (k0 >= K) continue;
+        float v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = acc[i][j][4 * q + r];
+        if (p.bias) {
+          const float4 b = *reinterpret_cast<const float4*>(p.bias + k0);
+          v[0] += b.x;
+          v[1] += b.y;
+          v[2] += b.z;
+          v[3] += b.w;
+        }
+        if (MODE == kCausal) {
+          const int64_t off = ((int64_t)n * p.mper + m) * K + k0;
+          if (p.res) {
+            const uint2 rr = *reinterpret_cast<const uint2*>(p.res + off);
+            v[0] += bf16_lo(rr.x);
+            v[1] += bf16_hi(rr.x);
+            v[2] += bf16_lo(rr.y);
+            v[3] += bf16_hi(rr.y);
+          }
+          uint2 o;
+          o.x = pack_bf16x2(v[0], v[1]);
+          o.y = pack_bf16x2(v[2], v[3]);
+          *reinterpret_cast<uint2*>(p.y + off) = o;
+        } else if (MODE == kPhase) {
+          const int64_t yy = 2 * h_ + pa, xx = 2 * w_ + pb;
+          const int64_t off = ((((int64_t)n * T + t_) * (2 * H) + yy) * (2 * W) + xx) * K + k0;
+          uint2 o;
+          o.x = pack_bf16x2(v[0], v[1]);
+          o.y = pack_bf16x2(v[2], v[3]);
+          *reinterpret_cast<uint2*>(p.y + off) = o;
+        } else {
+          // K = 12: k0 = 4c, the four values are (dy, dx) = (0,0), (0,1), (1,0), (1,1).
+          if (p.clamp) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) v[r] = fminf(fmaxf(v[r], -1.0f), 1.0f);
+          }
+          const int c = k0 >> 2;
+          const int64_t W2 = 2 * (int64_t)W;
+          const int64_t base = (((int64_t)n * 3 + c) * T + t_) * (2 * (int64_t)H) * W2;
+          *reinterpret_cast<uint32_t*>(p.y + base + (2 * h_) * W2 + 2 * w_) = pack_bf16x2(v[0], v[1]);
+          *reinterpret_cast<uint32_t*>(p.y + base + (2 * h_ + 1) * W2 + 2 * w_) = pack_bf16x2(v[2], v[3]);
+        }
+      }
+  }
+}
+
+// cache_out = the last 2 frames of P = cat(cache_in, a); frames of x are activated when
+// fused (same per-thread column layout and activate_packet as gn_silu_apply).
+__global__ __launch_bounds__(256) void cache_out_kernel(
+    const uint4* x, const uint4* cache_in, uint4* cache_out, int T, int64_t hw, int cp, int rstep,
+    int64_t rows_per_block, const double* stats, const float* gamma, const float* beta, double eps,
+    int groups) {
+  const int tid = threadIdx.x, n = blockIdx.y;
+  if (tid >= rstep * cp) return;
+  const int col = tid % cp;
+  Affine a[8];
+  if (stats) {
+    const int cg = cp * 8 / groups;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a[i] = channel_affine(stats, gamma, beta, eps, groups, cg, n, col * 8 + i);
+  }
+  const int64_t positions = 2 * hw;
+  const int64_t start = (int64_t)blockIdx.x * rows_per_block;
+  int64_t end = start + rows_per_block;
+  if (end > positions) end = positions;
+  for (int64_t q = start + tid / cp; q < end; q += rstep) {
+    const int f = (int)(q / hw);                     // 0 or 1
+    const int64_t s = q - f * hw;
+    const int pf = T + f;                            // frame of P = cat(cache_in, x)
+    uint4 v;
+    if (pf >= 2) {
+      v = x[(((int64_t)n * T + pf - 2) * hw + s) * cp + col];
+      if (stats) v = activate_packet(v, a);
+    } else if (cache_in) {
+      v = cache_in[(((int64_t)n * 2 + pf) * hw + s) * cp + col];
+    } else {
+      v = make_uint4(0, 0, 0, 0);
+    }
+    cache_out[(((int64_t)n * 2 + f) * hw + s) * cp + col] = v;
+  }
+}
+
+// ---------------------------------------------------------------- host side
+
+typedef void (*ConvFn)(ConvParams);
+
+struct TileCfg {
+  int bm, bn;
+  ConvFn fn;
+  int lds;
+};
+
+template <int BM, int BN, int WGM, int WGN, int MODE, bool FUSE>
+static TileCfg make_cfg(int c) {
+  TileCfg t;
+  t.bm = BM;
+  t.bn = BN;
+  t.fn = conv_kernel<BM, BN, WGM, WGN, MODE, FUSE>;
+  t.lds = 2 * (BM + BN) * 128 + (FUSE ? c * 16 : 0);
+  return t;
+}
+
+// Candidate tiles for N-tile width bn (largest M tile first).
+template <int MODE, bool FUSE>
+static int candidates(int bn, int c, TileCfg* out) {
+  int n = 0;
+  switch (bn) {
+    case 256:
+      out[n++] = make_cfg<256, 256, 2, 2, MODE, FUSE>(c);
+      out[n++] = make_cfg<224, 256, 1, 4, MODE, FUSE>(c);
+      out[n++] = make_cfg<192, 256, 2, 2, MODE, FUSE>(c);
+      out[n++] = make_cfg<128, 256, 2, 2, MODE, FUSE>(c);
+      break;
+    case 128:
+      out[n++] = make_cfg<256, 128, 2, 2, MODE, FUSE>(c);
+      break;
+    case 64:
+      out[n++] = make_cfg<256, 64, 4, 1, MODE, FUSE>(c);
+      break;
+    default:
+      out[n++] = make_cfg<256, 32, 4, 1, MODE, FUSE>(c);
+      break;
+  }
+  return n;
+}
+
+// Pick the M tile that minimises (waves of workgroups over 256 CUs) x (work per tile).
+template <int MODE, bool FUSE>
+static TileCfg choose_tile(int64_t mper, int k, int c, int64_t groups_of_tiles) {
+  const int bn = k > 128 ? 256 : k > 64 ? 128 : k > 32 ? 64 : 32;
+  TileCfg cand[4];
+  const int nc = candidates<MODE, FUSE>(bn, c, cand);
+  TileCfg best = cand[0];
+  double best_cost = 1e300;
+  for (int i = 0; i < nc; ++i) {
+    const int64_t tiles_m = (mper + cand[i].bm - 1) / cand[i].bm;
+    const int64_t tiles = tiles_m * ((k + bn - 1) / bn) * groups_of_tiles;
+    const double cost = (double)((tiles + 255) / 256) * cand[i].bm;
+    if (cost < best_cost * 0.999) {
+      best_cost = cost;
+      best = cand[i];
+    }
+  }
+  return best;
+}
+
+static bool launch_conv(const TileCfg& cfg, ConvParams& p, int64_t n_samples, int phases,
+                        hipStream_t stream, const char* fn) {
+  p.tiles_n = (p.K + cfg.bn - 1) / cfg.bn;
+  const int64_t tiles_m = (p.mper + cfg.bm - 1) / cfg.bm;
+  const int64_t nb = tiles_m * p.tiles_n * phases * n_samples;
+  if (tiles_m > (1 << 30) || nb > (int64_t)1 << 31) {
+    set_error("%s: problem too large for one launch", fn);
+    return false;
+  }
+  p.tiles_m = (int)tiles_m;
+  p.nblocks = (int)nb;
+  hipError_t e = hipFuncSetAttribute((const void*)cfg.fn, hipFuncAttributeMaxDynamicSharedMemorySize, cfg.lds);
+  if (e != hipSuccess) {
+    set_error("%s: cannot reserve %d bytes of LDS: %s", fn, cfg.lds, hipGetErrorString(e));
+    return false;
+  }
+  void* args[] = {&p};
+  e = hipLaunchKernel((const void*)cfg.fn, dim3((unsigned)nb), dim3(kConvThreads), args, cfg.lds, stream);
+  if (e != hipSuccess) {
+    set_error("%s: launch failed: %s", fn, hipGetErrorString(e));
+    return false;
+  }
+  return launch_ok(fn);
+}
+
+static bool launch_cache_out(const uint16_t* x, sgn_dims d, const uint16_t* cache_in,
+                             const sgn_gn* fuse, uint16_t* cache_out, hipStream_t stream) {
+  const int cp = (int)(d.c / 8);
+  int rstep = 256 / cp;
+  if (rstep < 1) rstep = 1;
+  const int64_t hw = d.h * d.w;
+  const int64_t positions = 2 * hw;
+  int64_t blocks = (positions + rstep * 8 - 1) / (rstep * 8);
+  if (blocks > 1024) blocks = 1024;
+  int64_t rows = (positions + blocks - 1) / blocks;
+  rows = (rows + rstep - 1) / rstep * rstep;
+  blocks = (positions + rows - 1) / rows;
+  cache_out_kernel<<<dim3((unsigned)blocks, (unsigned)d.n), 256, 0, stream>>>(
+      reinterpret_cast<const uint4*>(x), reinterpret_cast<const uint4*>(cache_in),
+      reinterpret_cast<uint4*>(cache_out), (int)d.t, hw, cp, rstep, rows,
+      fuse ? fuse->stats : nullptr, fuse ? fuse->gamma : nullptr, fuse ? fuse->beta : nullptr,
+      fuse ? (double)fuse->eps : 0.0, fuse ? fuse->groups : 1);
+  return launch_ok("cache_out");
+}
+
+static bool conv_common_checks(const uint16_t* x, sgn_dims d, const uint16_t* w, int k,
+                               uint16_t* y, const char* fn) {
+  if (!dims_ok(d, fn)) return false;
+  if (!x || !w || !y) {
+    set_error("%s: x, w and the output are required", fn);
+    return false;
+  }
+  if (d.c % 64 != 0 || d.c > kCMax) {
+    set_error("%s: C=%lld must be a multiple of 64 and at most %d", fn, (long long)d.c, kCMax);
+    return false;
+  }
+  if (k < 4 || k > 4096 || k % 4 != 0) {
+    set_error("%s: K=%d must be a multiple of 4 in [4, 4096]", fn, k);
+    return false;
+  }
+  if (d.t * d.h * d.w >= ((int64_t)1 << 40)) {
+    set_error("%s: too many positions per sample", fn);
+    return false;
+  }
+  return true;
+}
+
+static int check_fuse(const sgn_gn* f, sgn_dims d, const char* fn) {
+  if (!f) return SGN_OK;
+  if (!f->stats || !f->gamma || !f->beta) {
+    set_error("%s: fuse needs stats, gamma and beta", fn);
+    return SGN_EINVAL;
+  }
+  if (f->groups <= 0 || d.c % f->groups != 0) {
+    set_error("%s: fuse groups=%d must divide C=%lld", fn, f->groups, (long long)d.c);
+    return SGN_EINVAL;
+  }
+  if (!(f->eps > 0.0f) || !isfinite(f->eps)) {
+    set_error("%s: fuse eps must be a positive finite number", fn);
+    return SGN_EINVAL;
+  }
+  if (d.c > 2048) {
+    set_error("%s: fused GroupNorm supports C <= 2048", fn);
+    return SGN_EINVAL;
+  }
+  if (((uintptr_t)f->stats & 7) || ((uintptr_t)f->gamma & 3) || ((uintptr_t)f->beta & 3)) {
+    set_error("%s: fuse stats must be 8-byte, gamma/beta 4-byte aligned", fn);
+    return SGN_EALIGN;
+  }
+  return SGN_OK;
+}
+
+}  // namespace sgn
+
+using namespace sgn;
+
+extern "C" int causal_conv3d(const uint16_t* x, sgn_dims d, const uint16_t* cache_in,
+                             const uint16_t* w, int k, const float* bias, const uint16_t* residual,
+                             const sgn_gn* fuse, uint16_t* y, uint16_t* cache_out,
+                             hipStream_t stream) {
+  const char* fn = "causal_conv3d";
+  clear_error();
+  if (!conv_common_checks(x, d, w, k, y, fn)) return SGN_EINVAL;
+  int rc = check_fuse(fuse, d, fn);
+  if (rc) return rc;
+  if (!aligned16(x) || !aligned16(w) || !aligned16(y) || (cache_in && !aligned16(cache_in)) ||
+      (residual && !aligned16(residual)) || (cache_out && !aligned16(cache_out)) ||
+      (bias && !aligned16(bias))) {
+    set_error("%s: tensors (and bias) must be 16-byte aligned", fn);
+    return SGN_EALIGN;
+  }
+  const size_t xb = (size_t)(d.n * d.t * d.h * d.w * d.c) * 2;
+  const size_t yb = (size_t)(d.n * d.t * d.h * d.w) * k * 2;
+  const size_t cb = (size_t)(d.n * 2 * d.h * d.w * d.c) * 2;
+  const size_t wb = (size_t)k * 27 * d.c * 2;
+  if (overlap(y, yb, x, xb) || overlap(y, yb, w, wb) || (cache_in && overlap(y, yb, cache_in, cb)) ||
+      (residual && overlap(y, yb, residual, yb)) ||
+      (cache_out && (overlap(cache_out, cb, x, xb) || overlap(cache_out, cb, y, yb) ||
+                     overlap(cache_out, cb, w, wb) ||
+                     (cache_in && overlap(cache_out, cb, cache_in, cb)) ||
+                     (residual && overlap(cache_out, cb, residual, yb))))) {
+    set_error("%s: an output overlaps an input or the other output", fn);
+    return SGN_EALIAS;
+  }
+  ConvParams p = {};
+  p.x = x;
+  p.cache = cache_in;
+  p.w = w;
+  p.bias = bias;
+  p.res = residual;
+  p.y = y;
+  if (fuse) {
+    p.stats = fuse->stats;
+    p.gamma = fuse->gamma;
+    p.beta = fuse->beta;
+    p.eps = (double)fuse->eps;
+    p.groups = fuse->groups;
+  }
+  p.T = (int)d.t;
+  p.H = (int)d.h;
+  p.W = (int)d.w;
+  p.C = (int)d.c;
+  p.K = k;
+  p.mper = d.t * d.h * d.w;
+  const TileCfg cfg = fuse ? choose_tile<kCausal, true>(p.mper, k, p.C, d.n)
+                           : choose_tile<kCausal, false>(p.mper, k, p.C, d.n);
+  if (!launch_conv(cfg, p, d.n, 1, stream, fn)) return SGN_ELAUNCH;
+  if (cache_out && !launch_cache_out(x, d, cache_in, fuse, cache_out, stream)) return SGN_ELAUNCH;
+  return SGN_OK;
+}
+
+extern "C" int upsample2x_conv_phases(const uint16_t* x, sgn_dims d, const uint16_t* w_phase, int k,
+                                      const float* bias, uint16_t* y, hipStream_t stream) {
+  const char* fn = "upsample2x_conv_phases";
+  clear_error();
+  if (!conv_common_checks(x, d, w_phase, k, y, fn)) return SGN_EINVAL;
+  if (!aligned16(x) || !aligned16(w_phase) || !aligned16(y) || (bias && !aligned16(bias))) {
+    set_error("%s: tensors (and bias) must be 16-byte aligned", fn);
+    return SGN_EALIGN;
+  }
+  const size_t xb = (size_t)(d.n * d.t * d.h * d.w * d.c) * 2;
+  const size_t yb = (size_t)(d.n * d.t * 4 * d.h * d.w) * k * 2;
+  const size_t wb = (size_t)16 * k * d.c * 2;
+  if (overlap(y, yb, x, xb) || overlap(y, yb, w_phase, wb)) {
+    set_error("%s: y overlaps x or w_phase", fn);
+    return SGN_EALIAS;
+  }
+  ConvParams p = {};
+  p.x = x;
+  p.w = w_phase;
+  p.bias = bias;
+  p.y = y;
+  p.T = (int)d.t;
+  p.H = (int)d.h;
+  p.W = (int)d.w;
+  p.C = (int)d.c;
+  p.K = k;
+  p.mper = d.t * d.h * d.w;
+  const TileCfg cfg = choose_tile<kPhase, false>(p.mper, k, p.C, d.n * 4);
+  if (!launch_conv(cfg, p, d.n, 4, stream, fn)) return SGN_ELAUNCH;
+  return SGN_OK;
+}
+
+extern "C" int head_conv_d2s(const uint16_t* x, sgn_dims d, const uint16_t* cache_in, const uint16_t* w,
+                             const float* bias, const sgn_gn* fuse, int clamp, uint16_t* video,
+                             uint16_t* cache_out, hipStream_t stream) {
+  const char* fn = "head_conv_d2s";
+  clear_error();
+  const int k = 12;
+  if (!conv_common_checks(x, d, w, k, video, fn)) return SGN_EINVAL;
+  int rc = check_fuse(fuse, d, fn);
+  if (rc) return rc;
+  if (!aligned16(x) || !aligned16(w) || !aligned16(video) || (cache_in && !aligned16(cache_in)) ||
+      (cache_out && !aligned16(cache_out)) || (bias && !aligned16(bias))) {
+    set_error("%s: tensors (and bias) must be 16-byte aligned", fn);
+    return SGN_EALIGN;
+  }
+  const size_t xb = (size_t)(d.n * d.t * d.h * d.w * d.c) * 2;
+  const size_t vb = (size_t)(d.n * 3 * d.t * 4 * d.h * d.w) * 2;
+  const size_t cb = (size_t)(d.n * 2 * d.h * d.w * d.c) * 2;
+  const size_t wb = (size_t)k * 27 * d.c * 2;
+  if (overlap(video, vb, x, xb) || overlap(video, vb, w, wb) || (cache_in && overlap(video, vb, cache_in, cb)) ||
+      (cache_out && (overlap(cache_out, cb, x, xb) || overlap(cache_out, cb, video, vb) ||
+                     overlap(cache_out, cb, w, wb) || (cache_in && overlap(cache_out, cb, cache_in, cb))))) {
+    set_error("%s: an output overlaps an input or the other output", fn);
+    return SGN_EALIAS;
+  }
+  ConvParams p = {};
+  p.x = x;
+  p.cache = cache_in;
+  p.w = w;
+  p.bias = bias;
+  p.y = video;
+  if (fuse) {
+    p.stats = fuse->stats;
+    p.gamma = fuse->gamma;
+    p.beta = fuse->beta;
+    p.eps = (double)fuse->eps;
+    p.groups = fuse->groups;
+  }
+  p.T = (int)d.t;
+  p.H = (int)d.h;
+  p.W = (int)d.w;
+  p.C = (int)d.c;
+  p.K = k;
+  p.mper = d.t * d.h * d.w;
+  p.clamp = clamp ? 1 : 0;
+  const TileCfg cfg = fuse ? make_cfg<256, 32, 4, 1, kHead, true>(p.C) : make_cfg<256, 32, 4, 1, kHead, false>(p.C);
+  if (!launch_conv(cfg, p, d.n, 1, stream, fn)) return SGN_ELAUNCH;
+  if (cache_out && !launch_cache_out(x, d, cache_in, fuse, cache_out, stream)) return SGN_ELAUNCH;
+  return SGN_OK;
+}

@@ -1,0 +1,123 @@
+"""The C ABI on the host: the library loads, exports every declared entry point, and
+rejects invalid arguments before enqueuing anything (no GPU needed, no kernel runs).
+Every call below is invalid by construction and must come back with an error code."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+
+import silu_gn_amd as sga
+from oracle import bf16 as obf16
+from oracle import conv as oconv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "silugn.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(sga.LIB_PATH), reason="libsilugn.so not built")
+
+FAKE = 0x7f0000000000          # 16-byte aligned, never dereferenced: validation fails first
+EINVAL, EALIGN, EALIAS, EWORKSPACE = -1, -2, -3, -5
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w]+\**\s+\**(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_exports_every_declared_symbol():
+    lib = sga.load_library()
+    names = declared_functions()
+    assert set(names) == set(sga.EXPORTS), names
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_last_error_is_a_string():
+    lib = sga.load_library()
+    assert isinstance(lib.sgn_last_error(), bytes)
+
+
+def D(n=1, t=2, h=4, w=4, c=64):
+    return sga.sgn_dims(n, t, h, w, c)
+
+
+def _err(rc, code):
+    lib = sga.load_library()
+    msg = lib.sgn_last_error().decode()
+    assert rc == code, (rc, msg)
+    assert msg
+
+
+def test_stats_workspace_size():
+    lib = sga.load_library()
+    assert lib.gn_silu_stats_workspace(D(), 32) > 0
+    assert lib.gn_silu_stats_workspace(D(c=60), 32) == 0         # C % 8
+    assert lib.gn_silu_stats_workspace(D(c=64), 48) == 0         # groups does not divide C
+    assert lib.gn_silu_stats_workspace(D(c=96), 8) == 0          # C/G = 12 not supported
+    assert lib.gn_silu_stats_workspace(D(t=0), 32) == 0
+
+
+def test_stats_rejects():
+    lib = sga.load_library()
+    _err(lib.gn_silu_stats(FAKE, D(c=64), 48, FAKE, FAKE, 1 << 20, None), EINVAL)
+    _err(lib.gn_silu_stats(None, D(), 32, FAKE, FAKE, 1 << 20, None), EINVAL)
+    _err(lib.gn_silu_stats(FAKE + 2, D(), 32, FAKE, FAKE, 1 << 20, None), EALIGN)
+    _err(lib.gn_silu_stats(FAKE, D(), 32, FAKE, FAKE, 8, None), EWORKSPACE)
+    _err(lib.gn_silu_stats(FAKE, D(), 32, FAKE, None, 1 << 20, None), EWORKSPACE)
+    _err(lib.gn_silu_stats(FAKE, D(c=4096), 32, FAKE, FAKE, 1 << 30, None), EINVAL)
+
+
+def test_apply_rejects():
+    lib = sga.load_library()
+    _err(lib.gn_silu_apply(FAKE, D(), 32, FAKE, FAKE, FAKE, 0.0, FAKE + 4096, None), EINVAL)     # eps
+    _err(lib.gn_silu_apply(FAKE, D(), 32, None, FAKE, FAKE, 1e-5, FAKE + 4096, None), EINVAL)
+    _err(lib.gn_silu_apply(FAKE, D(), 32, FAKE, FAKE, FAKE, 1e-5, FAKE + 16, None), EALIAS)      # partial overlap
+    _err(lib.gn_silu_apply(FAKE, D(), 32, FAKE, FAKE, FAKE, 1e-5, FAKE + 4104, None), EALIGN)
+
+
+def test_conv_rejects():
+    lib = sga.load_library()
+    far = FAKE + (1 << 32)
+    _err(lib.causal_conv3d(FAKE, D(c=72), None, FAKE + (1 << 30), 64, None, None, None, far, None, None), EINVAL)
+    _err(lib.causal_conv3d(FAKE, D(), None, FAKE + (1 << 30), 6, None, None, None, far, None, None), EINVAL)
+    _err(lib.causal_conv3d(FAKE, D(), None, None, 64, None, None, None, far, None, None), EINVAL)
+    _err(lib.causal_conv3d(FAKE, D(), None, FAKE + (1 << 30), 64, None, None, None, FAKE + 64, None, None), EALIAS)
+    _err(lib.causal_conv3d(FAKE, D(), None, FAKE + (1 << 30), 64, None, None, None, far, far + 64, None), EALIAS)
+    _err(lib.causal_conv3d(FAKE, D(), None, FAKE + (1 << 30), 64, None, None, None, far + 8, None, None), EALIGN)
+    bad = sga.sgn_gn(FAKE, FAKE, FAKE, 1e-5, 48)
+    _err(lib.causal_conv3d(FAKE, D(), None, FAKE + (1 << 30), 64, None, None, ctypes.pointer(bad), far, None, None),
+         EINVAL)
+    bad = sga.sgn_gn(FAKE, FAKE, FAKE, -1.0, 32)
+    _err(lib.causal_conv3d(FAKE, D(), None, FAKE + (1 << 30), 64, None, None, ctypes.pointer(bad), far, None, None),
+         EINVAL)
+
+
+def test_upsample_and_head_reject():
+    lib = sga.load_library()
+    far = FAKE + (1 << 32)
+    _err(lib.upsample2x_conv_phases(FAKE, D(c=32), FAKE + (1 << 30), 64, None, far, None), EINVAL)
+    _err(lib.upsample2x_conv_phases(FAKE, D(), FAKE + (1 << 30), 64, None, FAKE + 128, None), EALIAS)
+    _err(lib.head_conv_d2s(FAKE, D(c=48), None, FAKE + (1 << 30), None, None, 0, far, None, None), EINVAL)
+    _err(lib.head_conv_d2s(FAKE, D(), None, FAKE + (1 << 30), None, None, 0, FAKE + 256, None, None), EALIAS)
+
+
+@pytest.mark.parametrize("k,c", [(4, 8), (16, 64)])
+def test_prepare_phase_weights_matches_oracle(k, c):
+    w = torch.randn(k, 3, 3, c, generator=torch.Generator().manual_seed(k + c)).to(torch.bfloat16)
+    got = sga.upsample2x_prepare_weights(w)
+    want = oconv.phase_weights(w.float().numpy().astype(np.float64))     # fp64 sums [a,b,k,u,v,c]
+    gb = got.view(torch.int16).numpy().view(np.uint16)
+    d = obf16.ulp_distance(gb, obf16.round_rne(want))
+    # fp32 sums of at most four bf16 values, rounded once: at most one ulp from the fp64 sum's rounding
+    assert d.max() <= 1
+    assert (d == 0).mean() > 0.99
+
+
+def test_prepare_phase_weights_rejects():
+    lib = sga.load_library()
+    _err(lib.upsample2x_prepare_weights(None, 4, 8, FAKE), EINVAL)
+    buf = (ctypes.c_uint16 * (16 * 4 * 8))()
+    _err(lib.upsample2x_prepare_weights(ctypes.addressof(buf), 4, 8, ctypes.addressof(buf) + 16), EALIAS)

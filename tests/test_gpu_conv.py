@@ -1,0 +1,205 @@
+"""Causal 3x3x3 convolution on the GPU vs the fp64 oracle (causal_conv3d).
+
+Gate (unit-scale data): relative L2 error <= 1e-2 and max abs error <= 4e-2 against
+the unrounded fp64 oracle; the fused GroupNorm variant must equal apply-then-conv
+bitwise; cache_out must equal the last 2 frames of the padded input bitwise.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import silu_gn_amd as sga
+import synthgen as sg
+from oracle import bf16 as obf16
+from oracle import conv as oconv
+from oracle import groupnorm as ogn
+from synthgen.workloads import WORKLOADS
+from tests.helpers import assert_conv_close, bits, sample_positions, vals, vals32
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _w(k, c, seed, tid=sg.W1):
+    return sg.normal((k, 3, 3, 3, c), seed, tid, std=1 / math.sqrt(27 * c))
+
+
+def _gn_params(c, seed):
+    return (sg.normal((c,), seed, sg.GAMMA1, std=0.1, mean=1.0, dtype=torch.float32),
+            sg.normal((c,), seed, sg.BETA1, std=0.1, dtype=torch.float32))
+
+
+@pytest.mark.parametrize("n,t,h,w,c,k,cache,bias,res", [
+    (1, 3, 16, 16, 64, 64, False, False, False),     # the tiny block's shape
+    (1, 1, 5, 7, 64, 4, True, True, False),          # T = 1: both taps back into the cache
+    (1, 2, 9, 33, 128, 12, True, False, True),       # ragged tiles, K = 12
+    (2, 3, 11, 13, 192, 96, True, True, True),       # two samples, K not a tile multiple
+    (1, 4, 6, 70, 256, 256, True, True, True),
+    (1, 2, 7, 9, 512, 520, False, True, False),      # K past one 256 tile
+])
+def test_conv_small(n, t, h, w, c, k, cache, bias, res):
+    print("case", (n, t, h, w, c, k, cache, bias, res), flush=True)
+    seed = n + t + h + w + c + k
+    a = sg.normal((n, t, h, w, c), seed, sg.X)
+    wt = _w(k, c, seed)
+    ci = sg.normal((n, 2, h, w, c), seed, sg.X_PREV) if cache else None
+    b = sg.normal((k,), seed, sg.BETA2, std=0.5, dtype=torch.float32) if bias else None
+    r = sg.normal((n, t, h, w, k), seed, sg.GAMMA2) if res else None
+    co = torch.empty((n, 2, h, w, c), dtype=torch.bfloat16, device=DEV)
+    y = sga.causal_conv3d(a.to(DEV), wt.to(DEV), ci.to(DEV) if cache else None,
+                          b.to(DEV) if bias else None, r.to(DEV) if res else None, cache_out=co)
+    torch.cuda.synchronize()
+    o, cache_o = oconv.causal_conv3d(vals(a), vals(wt), vals(ci) if cache else None,
+                                     b.numpy() if bias else None, vals(r) if res else None)
+    assert_conv_close(bits(y), o, "conv")
+    assert np.array_equal(vals(co), cache_o)
+
+
+def _fused_case(shape, k, groups, seed, cache=True):
+    n, t, h, w, c = shape
+    x = sg.normal(shape, seed, sg.X, mean=0.2)
+    gamma, beta = _gn_params(c, seed)
+    wt = _w(k, c, seed)
+    ci = sg.normal((n, 2, h, w, c), seed, sg.X_PREV) if cache else None
+    return x, gamma, beta, wt, ci
+
+
+@pytest.mark.parametrize("shape,k,groups", [
+    ((1, 3, 16, 16, 64), 64, 32),
+    ((2, 1, 7, 9, 256), 32, 32),
+    ((1, 3, 5, 37, 1024), 256, 32),
+])
+def test_fused_equals_apply_then_conv_and_oracle(shape, k, groups):
+    print("case fused", shape, k, groups, flush=True)
+    x, gamma, beta, wt, ci = _fused_case(shape, k, groups, sum(shape) + k)
+    xd, gd, bd, wd, cd = (v.to(DEV) for v in (x, gamma, beta, wt, ci))
+    eps = 1e-5
+    stats = sga.gn_silu_stats(xd, groups)
+    a = sga.gn_silu_apply(xd, groups, stats, gd, bd, eps)
+    co1 = torch.empty_like(cd)
+    co2 = torch.empty_like(cd)
+    y1 = sga.causal_conv3d(a, wd, cd, cache_out=co1)
+    y2 = sga.causal_conv3d(xd, wd, cd, fuse=(stats, gd, bd, eps, groups), cache_out=co2)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    assert torch.equal(co1.view(torch.int16), co2.view(torch.int16))
+    # oracle: GroupNorm+SiLU in fp64, rounded once to bf16, then the conv
+    act, st = ogn.gn_silu(vals(x), groups, gamma.numpy(), beta.numpy(), eps)
+    act = obf16.decode(obf16.round_rne(act))
+    o, cache_o = oconv.causal_conv3d(act, vals(wt), vals(ci))
+    assert_conv_close(bits(y2), o, "fused")
+    # the cache holds activated frames; they are bf16 results of the same apply
+    assert np.array_equal(vals(co2), cache_o) or obf16.ulp_distance(
+        bits(co2), obf16.round_rne(cache_o)).max() <= 1
+
+
+def test_conv_deterministic_causal_and_pass_split():
+    n, t, h, w, c, k = 1, 5, 12, 40, 256, 256
+    seed = 77
+    a = sg.normal((n, t, h, w, c), seed, sg.X).to(DEV)
+    wt = _w(k, c, seed).to(DEV)
+    c0 = sg.normal((n, 2, h, w, c), seed, sg.X_PREV).to(DEV)
+    y = sga.causal_conv3d(a, wt, c0)
+    y_again = sga.causal_conv3d(a, wt, c0)
+    assert torch.equal(y.view(torch.int16), y_again.view(torch.int16))
+    # causality: a change in frame 3 leaves frames 0..2 bitwise unchanged
+    b = a.clone()
+    b[:, 3] = sg.normal((n, 1, h, w, c), seed, sg.GAMMA2).to(DEV)[:, 0]
+    yb = sga.causal_conv3d(b, wt, c0)
+    assert torch.equal(yb[:, :3].view(torch.int16), y[:, :3].view(torch.int16))
+    assert not torch.equal(yb[:, 3:].view(torch.int16), y[:, 3:].view(torch.int16))
+    # pass split: frames [0,2) then [2,5) with the carried cache == one pass
+    c1 = torch.empty_like(c0)
+    y01 = sga.causal_conv3d(a[:, :2].contiguous(), wt, c0, cache_out=c1)
+    y25 = sga.causal_conv3d(a[:, 2:].contiguous(), wt, c1)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat([y01, y25], 1).view(torch.int16), y.view(torch.int16))
+
+
+def test_latent_block_two_passes():
+    """The latent-resolution block [1,4,44,78,1024] with 2 cached frames from a previous pass."""
+    wl = WORKLOADS[2]
+    g, eps = wl.groups, wl.eps
+    xp, x = wl.x_prev(), wl.x()
+    gamma, beta, wt = wl.gamma(), wl.beta(), wl.conv_weight()
+    xpd, xd, gd, bd, wd = (v.to(DEV) for v in (xp, x, gamma, beta, wt))
+    print("case latent pass 0", flush=True)
+    cache1 = torch.empty((1, 2, wl.h, wl.w, wl.c), dtype=torch.bfloat16, device=DEV)
+    sp = sga.gn_silu_stats(xpd, g)
+    sga.causal_conv3d(xpd, wd, None, fuse=(sp, gd, bd, eps, g), cache_out=cache1)
+    print("case latent pass 1", flush=True)
+    s = sga.gn_silu_stats(xd, g)
+    cache2 = torch.empty_like(cache1)
+    y = sga.causal_conv3d(xd, wd, cache1, fuse=(s, gd, bd, eps, g), cache_out=cache2)
+    torch.cuda.synchronize()
+    # oracle: the same two passes
+    ap, _ = ogn.gn_silu(vals(xp), g, gamma.numpy(), beta.numpy(), eps)
+    ap = obf16.decode(obf16.round_rne(ap))
+    _, oc1 = oconv.causal_conv3d(ap, vals(wt), None)
+    act, _ = ogn.gn_silu(vals(x), g, gamma.numpy(), beta.numpy(), eps)
+    act = obf16.decode(obf16.round_rne(act))
+    o, oc2 = oconv.causal_conv3d(act, vals(wt), oc1)
+    assert obf16.ulp_distance(bits(cache1), obf16.round_rne(oc1)).max() <= 1
+    assert_conv_close(bits(y), o, "latent")
+
+
+def _sampled_fused_check(x, wt, ci, gamma, beta, groups, eps, y, residual=None, n_interior=16384, seed=0):
+    """Oracle at sampled positions of a large fused conv (all K channels each)."""
+    n, t, h, w, c = x.shape
+    pos = sample_positions(t, h, w, n_interior, seed)
+    xv = vals32(x)
+    mean, var = ogn.group_stats(xv, groups)
+    g64, b64 = gamma.numpy(), beta.numpy()
+
+    def act(v, nidx):
+        z = ogn.normalize(v[None], mean, var, g64, b64, eps, groups)[0]
+        return obf16.decode(obf16.round_rne(ogn.silu(z)))
+
+    yb = y.cpu()
+    civ = vals32(ci) if ci is not None else None
+    wv = vals(wt)
+    outs, gots = [], []
+    for s in range(0, len(pos), 4096):
+        p = pos[s:s + 4096]
+        idx = tuple(torch.from_numpy(p[:, i]) for i in range(4))
+        patches = oconv.causal_patches(xv, civ, p, act=act)
+        o = oconv.conv_at(patches, wv)
+        if residual is not None:
+            o = o + vals(residual[idx])
+        outs.append(o)
+        gots.append(bits(yb[idx]))
+    return assert_conv_close(np.concatenate(gots), np.concatenate(outs), "sampled")
+
+
+@pytest.mark.slow
+def test_upsample_block_conv_full_size_sampled():
+    """The 512->512 conv at [1,8,176,312,512] (fused GroupNorm, zero cache), sampled."""
+    wl = WORKLOADS[3]
+    shape = (1, wl.t, 2 * wl.h, 2 * wl.w, wl.c)
+    x = sg.normal(shape, wl.seed, sg.X_PREV, device=DEV)
+    gamma, beta, wt = wl.gamma(), wl.beta(), sg.normal((wl.c, 3, 3, 3, wl.c), wl.seed, sg.W1,
+                                                       std=1 / math.sqrt(27 * wl.c))
+    gd, bd, wd = gamma.to(DEV), beta.to(DEV), wt.to(DEV)
+    print("case upsample-block conv", flush=True)
+    s = sga.gn_silu_stats(x, wl.groups)
+    y = sga.causal_conv3d(x, wd, None, fuse=(s, gd, bd, wl.eps, wl.groups))
+    torch.cuda.synchronize()
+    _sampled_fused_check(x.cpu(), wt, None, gamma, beta, wl.groups, wl.eps, y, seed=3)
+
+
+@pytest.mark.slow
+def test_fullres_conv_full_size_sampled():
+    """One conv of the full-res block at [1,16,352,624,256] with offsets, a cache and a residual."""
+    wl = WORKLOADS[4]
+    x = wl.x(device=DEV)
+    ci = sg.normal((1, 2, wl.h, wl.w, wl.c), wl.seed, sg.GAMMA2, device=DEV)
+    gamma, beta, wt = wl.gamma(), wl.beta(), wl.conv_weight()
+    gd, bd, wd = gamma.to(DEV), beta.to(DEV), wt.to(DEV)
+    print("case full-res conv", flush=True)
+    s = sga.gn_silu_stats(x, wl.groups)
+    y = sga.causal_conv3d(x, wd, ci, residual=x, fuse=(s, gd, bd, wl.eps, wl.groups))
+    torch.cuda.synchronize()
+    xc = x.cpu()
+    _sampled_fused_check(xc, wt, ci.cpu(), gamma, beta, wl.groups, wl.eps, y, residual=xc, seed=4)

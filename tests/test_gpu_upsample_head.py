@@ -1,0 +1,161 @@
+"""Upsample phases, the output head and the full-res block chain on the GPU vs the oracle.
+
+The upsample is compared with the oracle's DIRECT form (nearest-x2, then a 3x3
+conv with the original bf16 weights): the GPU's bf16 phase weights (fp32 sums of
+the taps, rounded once) are part of what is checked.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import silu_gn_amd as sga
+import synthgen as sg
+from oracle import bf16 as obf16
+from oracle import conv as oconv
+from oracle import groupnorm as ogn
+from synthgen.workloads import WORKLOADS
+from tests.helpers import assert_conv_close, bits, sample_positions, vals, vals32
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.mark.parametrize("n,t,h,w,c,k,bias", [
+    (1, 2, 5, 7, 64, 64, False),
+    (1, 3, 11, 20, 128, 256, True),
+    (2, 1, 9, 13, 512, 512, True),
+    (1, 1, 1, 1, 64, 8, False),           # a single pixel: every tap but one is padding
+])
+def test_upsample_small(n, t, h, w, c, k, bias):
+    print("case upsample", (n, t, h, w, c, k, bias), flush=True)
+    seed = t + h + w + c + k
+    x = sg.normal((n, t, h, w, c), seed, sg.X)
+    w3 = sg.normal((k, 3, 3, c), seed, sg.W_UP, std=1 / math.sqrt(9 * c))
+    b = sg.normal((k,), seed, sg.BETA2, std=0.5, dtype=torch.float32) if bias else None
+    wp = sga.upsample2x_prepare_weights(w3).to(DEV)
+    y = sga.upsample2x_conv_phases(x.to(DEV), wp, b.to(DEV) if bias else None)
+    torch.cuda.synchronize()
+    o = oconv.upsample2x_conv(vals(x), vals(w3), b.numpy() if bias else None)
+    assert_conv_close(bits(y), o, "upsample")
+
+
+@pytest.mark.slow
+def test_upsample_workload_sampled():
+    """x [1,8,88,156,512] -> y [1,8,176,312,512], sampled against the direct form."""
+    wl = WORKLOADS[3]
+    x = wl.x(device=DEV)
+    w3 = wl.up_weight()
+    wp = sga.upsample2x_prepare_weights(w3).to(DEV)
+    print("case upsample workload", flush=True)
+    y = sga.upsample2x_conv_phases(x, wp)
+    torch.cuda.synchronize()
+    pos = sample_positions(wl.t, 2 * wl.h, 2 * wl.w, 16384, seed=5)
+    o = oconv.upsample2x_conv_at(vals32(x), vals(w3), pos)
+    idx = tuple(torch.from_numpy(pos[:, i]) for i in range(4))
+    assert_conv_close(bits(y.cpu()[idx]), o, "upsample sampled")
+
+
+@pytest.mark.parametrize("n,t,h,w,c,cache,bias,clamp,fused", [
+    (1, 3, 8, 10, 64, False, False, False, False),
+    (1, 2, 9, 31, 256, True, True, False, True),
+    (2, 1, 5, 6, 128, True, True, True, False),
+    (1, 4, 7, 9, 256, False, True, True, True),
+])
+def test_head_small(n, t, h, w, c, cache, bias, clamp, fused):
+    print("case head", (n, t, h, w, c, cache, bias, clamp, fused), flush=True)
+    seed = t + h + w + c
+    x = sg.normal((n, t, h, w, c), seed, sg.X)
+    wt = sg.normal((12, 3, 3, 3, c), seed, sg.W1, std=1 / math.sqrt(27 * c))
+    ci = sg.normal((n, 2, h, w, c), seed, sg.X_PREV) if cache else None
+    b = sg.normal((12,), seed, sg.BETA2, std=0.5, dtype=torch.float32) if bias else None
+    gamma = sg.normal((c,), seed, sg.GAMMA1, std=0.1, mean=1.0, dtype=torch.float32)
+    beta = sg.normal((c,), seed, sg.BETA1, std=0.1, dtype=torch.float32)
+    xd = x.to(DEV)
+    co = torch.empty((n, 2, h, w, c), dtype=torch.bfloat16, device=DEV)
+    fuse = None
+    if fused:
+        st = sga.gn_silu_stats(xd, 32)
+        fuse = (st, gamma.to(DEV), beta.to(DEV), 1e-5, 32)
+    scale = 3.0 if clamp else 1.0           # push some outputs past +-1 so the clamp acts
+    video = sga.head_conv_d2s(xd, (wt.float() * scale).to(torch.bfloat16).to(DEV),
+                              ci.to(DEV) if cache else None, b.to(DEV) if bias else None,
+                              fuse=fuse, clamp=clamp, cache_out=co)
+    torch.cuda.synchronize()
+    a = vals(x)
+    if fused:
+        act, _ = ogn.gn_silu(a, 32, gamma.numpy(), beta.numpy(), 1e-5)
+        a = obf16.decode(obf16.round_rne(act))
+    wv = vals((wt.float() * scale).to(torch.bfloat16))
+    ov, oc = oconv.head_conv_d2s(a, wv, vals(ci) if cache else None, b.numpy() if bias else None, clamp=clamp)
+    assert_conv_close(bits(video), ov, "head")
+    if clamp:
+        assert np.abs(obf16.decode(bits(video))).max() <= 1.0
+        assert (np.abs(ov) >= 1.0).mean() > 0.01
+    assert obf16.ulp_distance(bits(co), obf16.round_rne(oc)).max() <= 1
+
+
+@pytest.mark.slow
+def test_head_workload_sampled():
+    """[1,16,352,624,256] -> video [1,3,16,704,1248], fused GroupNorm, sampled."""
+    wl = WORKLOADS[5]
+    x = wl.x(device=DEV)
+    gamma, beta, wt = wl.gamma(), wl.beta(), wl.conv_weight()
+    print("case head workload", flush=True)
+    st = sga.gn_silu_stats(x, wl.groups)
+    video = sga.head_conv_d2s(x, wt.to(DEV), None, None,
+                              fuse=(st, gamma.to(DEV), beta.to(DEV), wl.eps, wl.groups))
+    torch.cuda.synchronize()
+    xv = vals32(x)
+    mean, var = ogn.group_stats(xv, wl.groups)
+
+    def act(v, nidx):
+        z = ogn.normalize(v[None], mean, var, gamma.numpy(), beta.numpy(), wl.eps, wl.groups)[0]
+        return obf16.decode(obf16.round_rne(ogn.silu(z)))
+
+    pos = sample_positions(wl.t, wl.h, wl.w, 16384, seed=6)
+    o = oconv.conv_at(oconv.causal_patches(xv, None, pos, act=act), vals(wt))      # (S, 12)
+    vc = video.cpu()
+    got = []
+    for c in range(3):
+        for dy in range(2):
+            for dx in range(2):
+                got.append(bits(vc[pos[:, 0], c, pos[:, 1], 2 * pos[:, 2] + dy, 2 * pos[:, 3] + dx]))
+    got = np.stack(got, axis=1)                      # channel order 4c + 2dy + dx
+    assert_conv_close(got, o, "head sampled")
+
+
+def test_fullres_block_chain_reduced():
+    """out = x + conv2(gnsilu2(conv1(gnsilu1(x)))) with two passes, at [1,T,24,40,256] per pass."""
+    wl = WORKLOADS[4].scaled(t=4, h=24, w=40)
+    g, eps = wl.groups, wl.eps
+    params = [(wl.gamma(1), wl.beta(1), wl.conv_weight(1)), (wl.gamma(2), wl.beta(2), wl.conv_weight(2))]
+    dev_params = [tuple(v.to(DEV) for v in p) for p in params]
+    caches = [None, None]
+    ocaches = [None, None]
+    for pas, x in enumerate([wl.x_prev(), wl.x()]):
+        print("case chain pass", pas, flush=True)
+        xd = x.to(DEV)
+        h = xd
+        new_caches = []
+        for i, (gm, bt, wt) in enumerate(dev_params):
+            st = sga.gn_silu_stats(h, g)
+            co = torch.empty((1, 2, wl.h, wl.w, wl.c), dtype=torch.bfloat16, device=DEV)
+            h = sga.causal_conv3d(h, wt, caches[i], residual=xd if i == 1 else None,
+                                  fuse=(st, gm, bt, eps, g), cache_out=co)
+            new_caches.append(co)
+        caches = new_caches
+        torch.cuda.synchronize()
+        # oracle chain
+        hv = vals(x)
+        onew = []
+        for i, (gm, bt, wt) in enumerate(params):
+            act, _ = ogn.gn_silu(hv, g, gm.numpy(), bt.numpy(), eps)
+            act = obf16.decode(obf16.round_rne(act))
+            o, oc = oconv.causal_conv3d(act, vals(wt), ocaches[i], residual=vals(x) if i == 1 else None)
+            onew.append(oc)
+            if i == 0:
+                hv = obf16.decode(obf16.round_rne(o))
+        ocaches = onew
+        assert_conv_close(bits(h), o, "chain pass %d" % pas)
