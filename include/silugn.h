@@ -120,7 +120,8 @@ int gn_silu_apply(const uint16_t* x, sgn_dims d, int groups, const double* stats
  *   y         bf16 (N,T,H,W,K); must not overlap x, cache_in, residual or w
  *   cache_out bf16 (N,2,H,W,C) = P[:, T:T+2] (activated when fused), or NULL;
  *             must not overlap cache_in, x or y
- * Requires C % 64 == 0, 1 <= K <= 4096.
+ * Requires C % 64 == 0 with C <= 4096 (C <= 2048 when fused), K % 4 == 0 with
+ * 4 <= K <= 4096; any other shape is SGN_EINVAL.
  */
 int causal_conv3d(const uint16_t* x, sgn_dims d, const uint16_t* cache_in,
                   const uint16_t* w, int k, const float* bias, const uint16_t* residual,
@@ -150,7 +151,8 @@ int upsample2x_prepare_weights(const uint16_t* w3x3, int k, int c, uint16_t* w_p
  *        w_phase[a][b][k][u][v][c] * x[n, t, i+u+a-1, j+v+b-1, c] ),  zero outside.
  * Per frame (no temporal taps, no cache). x bf16 (N,T,H,W,C); w_phase device bf16
  * from upsample2x_prepare_weights; bias fp32 [K] or NULL; y bf16 (N,T,2H,2W,K),
- * written interleaved, must not overlap x or w_phase. Requires C % 64 == 0.
+ * written interleaved, must not overlap x or w_phase. Requires C % 64 == 0 with
+ * C <= 4096, K % 4 == 0 with 4 <= K <= 4096.
  */
 int upsample2x_conv_phases(const uint16_t* x, sgn_dims d, const uint16_t* w_phase, int k,
                            const float* bias, uint16_t* y, hipStream_t stream);
@@ -165,7 +167,8 @@ int upsample2x_conv_phases(const uint16_t* x, sgn_dims d, const uint16_t* w_phas
  *   o = causal_conv3d(x, cache_in, w, K=12, bias, fuse) in fp32 (before rounding)
  *   video[n, c, t, 2h+dy, 2w+dx] = RNE_bf16( clamp?( o[n,t,h,w, 4c+2dy+dx] ) )
  * with clamp to [-1, 1] when clamp != 0. video: bf16 (N,3,T,2H,2W) dense
- * (channels-first). cache_out as in causal_conv3d. Requires C % 64 == 0.
+ * (channels-first). cache_out as in causal_conv3d. Requires C % 64 == 0 with
+ * C <= 4096 (C <= 2048 when fused).
  */
 int head_conv_d2s(const uint16_t* x, sgn_dims d, const uint16_t* cache_in, const uint16_t* w,
                   const float* bias, const sgn_gn* fuse, int clamp, uint16_t* video,
