@@ -37,113 +37,122 @@ PEAK_HBM_GBPS = 8000.0
 METRIC = "causal conv3d TFLOP/s + GroupNorm+SiLU GB/s (% of MI355X roofline)"
 
 
-def build_step(wl, dev):
-    """Allocate inputs for workload ``wl`` and return (step_fn, conv_only_fn, gn_fns, flops, info)."""
+class GnConv:
+    """silu(group_norm(src)) -> causal conv on the GPU, with its buffers.
+
+    Unfused (default): gn_silu_stats, gn_silu_apply into ``act``, causal_conv3d on ``act``.
+    Fused: gn_silu_stats, then causal_conv3d applying the norm in its operand load."""
+
+    def __init__(self, shape, k, groups, eps, gamma, beta, w, dev, fused, head=False):
+        n, t, h, w_, c = shape
+        self.g, self.eps, self.gamma, self.beta, self.w = groups, eps, gamma, beta, w
+        self.fused, self.head = fused, head
+        self.stats = torch.empty((n, groups, 2), dtype=torch.float64, device=dev)
+        self.ws = torch.empty(sga.gn_silu_stats_workspace(shape, groups), dtype=torch.uint8, device=dev)
+        self.act = None if fused else torch.empty(shape, dtype=torch.bfloat16, device=dev)
+
+    def fuse(self):
+        return (self.stats, self.gamma, self.beta, self.eps, self.g)
+
+    def __call__(self, src, y, cache_in=None, cache_out=None, residual=None, timer=None):
+        sga.gn_silu_stats(src, self.g, self.stats, self.ws)
+        mark(timer, "gn_silu_stats")
+        if self.fused:
+            a, fuse = src, self.fuse()
+        else:
+            sga.gn_silu_apply(src, self.g, self.stats, self.gamma, self.beta, self.eps, y=self.act)
+            mark(timer, "gn_silu_apply")
+            a, fuse = self.act, None
+        if self.head:
+            sga.head_conv_d2s(a, self.w, cache_in, None, fuse=fuse, video=y, cache_out=cache_out)
+            mark(timer, "head_conv_d2s" + (" (fused)" if fuse else ""))
+        else:
+            sga.causal_conv3d(a, self.w, cache_in, residual=residual, fuse=fuse, y=y, cache_out=cache_out)
+            mark(timer, "causal_conv3d" + (" (fused)" if fuse else ""))
+
+    def conv_only(self, src, y, cache_in=None, residual=None):
+        """The dominant kernel alone: the conv of the step (no cache write)."""
+        a, fuse = (src, self.fuse()) if self.fused else (self.act, None)
+        if self.head:
+            sga.head_conv_d2s(a, self.w, cache_in, None, fuse=fuse, video=y)
+        else:
+            sga.causal_conv3d(a, self.w, cache_in, residual=residual, fuse=fuse, y=y)
+
+
+def build_step(wl, dev, fused):
+    """Allocate inputs for workload ``wl``; return (step, conv_only, gn_inputs, flops, info)."""
     g, eps = wl.groups, wl.eps
     gamma, beta = wl.gamma(1, dev), wl.beta(1, dev)
+    conv_name = "causal_conv3d" + (" (fused GroupNorm+SiLU)" if fused else "")
     if wl.kind in ("block", "latent"):
         x = wl.x(dev)
         w = wl.conv_weight(1, dev)
+        gc = GnConv(wl.shape, wl.k, g, eps, gamma, beta, w, dev, fused)
         cache = torch.empty((wl.n, 2, wl.h, wl.w, wl.c), dtype=torch.bfloat16, device=dev)
         cache_next = torch.empty_like(cache)
-        if wl.cache_from_prev:           # previous pass, untimed: its activated last 2 frames
-            xp = wl.x_prev(dev)
-            sp = sga.gn_silu_stats(xp, g)
-            sga.causal_conv3d(xp, w, None, fuse=(sp, gamma, beta, eps, g), cache_out=cache)
-            cin = cache
-        else:
-            cin = None
         y = torch.empty((wl.n, wl.t, wl.h, wl.w, wl.k), dtype=torch.bfloat16, device=dev)
-        stats = torch.empty((wl.n, g, 2), dtype=torch.float64, device=dev)
-        ws = torch.empty(sga.gn_silu_stats_workspace(wl.shape, g), dtype=torch.uint8, device=dev)
+        cin = None
+        if wl.cache_from_prev:           # previous pass, untimed: its activated last 2 frames
+            gc(wl.x_prev(dev), y, None, cache)
+            cin = cache
 
         def step(timer=None):
-            sga.gn_silu_stats(x, g, stats, ws)
-            mark(timer, "gn_silu_stats")
-            sga.causal_conv3d(x, w, cin, fuse=(stats, gamma, beta, eps, g), y=y, cache_out=cache_next)
-            mark(timer, "causal_conv3d (fused)")
-
-        def conv_only():
-            sga.causal_conv3d(x, w, cin, fuse=(stats, gamma, beta, eps, g), y=y)
+            gc(x, y, cin, cache_next, timer=timer)
 
         flops = conv_flops(wl.n, wl.t, wl.h, wl.w, wl.k, wl.c)
-        return step, conv_only, (x, stats, ws, gamma, beta), flops, {"conv": "%d->%d 3x3x3 causal" % (wl.c, wl.k)}
+        return (step, lambda: gc.conv_only(x, y, cin), (x, gc), flops, flops,
+                {"conv": "%d->%d 3x3x3 causal" % (wl.c, wl.k)}, conv_name)
     if wl.kind == "upsample":
         x = wl.x(dev)
         wp = sga.upsample2x_prepare_weights(wl.up_weight()).to(dev)
-        u = torch.empty((wl.n, wl.t, 2 * wl.h, 2 * wl.w, wl.c), dtype=torch.bfloat16, device=dev)
+        ushape = (wl.n, wl.t, 2 * wl.h, 2 * wl.w, wl.c)
+        u = torch.empty(ushape, dtype=torch.bfloat16, device=dev)
         w = sg.normal((wl.c, 3, 3, 3, wl.c), wl.seed, sg.W1, std=1 / math.sqrt(27 * wl.c), device=dev)
+        gc = GnConv(ushape, wl.c, g, eps, gamma, beta, w, dev, fused)
         y = torch.empty_like(u)
-        ushape = tuple(u.shape)
-        stats = torch.empty((wl.n, g, 2), dtype=torch.float64, device=dev)
-        ws = torch.empty(sga.gn_silu_stats_workspace(ushape, g), dtype=torch.uint8, device=dev)
+        sga.upsample2x_conv_phases(x, wp, y=u)
 
         def step(timer=None):
             sga.upsample2x_conv_phases(x, wp, y=u)
             mark(timer, "upsample2x_conv_phases")
-            sga.gn_silu_stats(u, g, stats, ws)
-            mark(timer, "gn_silu_stats")
-            sga.causal_conv3d(u, w, None, fuse=(stats, gamma, beta, eps, g), y=y)
-            mark(timer, "causal_conv3d (fused)")
+            gc(u, y, timer=timer)
 
-        def conv_only():
-            sga.causal_conv3d(u, w, None, fuse=(stats, gamma, beta, eps, g), y=y)
-
-        n2, t2, h2, w2, c2 = ushape
-        flops = conv_flops(n2, t2, h2, w2, wl.c, c2) + conv_flops(wl.n, wl.t, wl.h, wl.w, wl.c, wl.c, taps=16)
-        return step, conv_only, (u, stats, ws, gamma, beta), flops, {"conv": "phases + 512->512 3x3x3 causal"}
+        conv = conv_flops(*ushape[:4], wl.c, wl.c)
+        flops = conv + conv_flops(wl.n, wl.t, wl.h, wl.w, wl.c, wl.c, taps=16)
+        return (step, lambda: gc.conv_only(u, y), (u, gc), flops, conv,
+                {"conv": "phases + %d->%d 3x3x3 causal" % (wl.c, wl.c)}, conv_name)
     if wl.kind == "resblock":
         x = wl.x(dev)
         params = [(wl.gamma(i, dev), wl.beta(i, dev), wl.conv_weight(i, dev)) for i in (1, 2)]
+        gcs = [GnConv(wl.shape, wl.c, g, eps, gm, bt, w, dev, fused) for gm, bt, w in params]
         caches = [torch.empty((wl.n, 2, wl.h, wl.w, wl.c), dtype=torch.bfloat16, device=dev) for _ in range(4)]
-        xp = wl.x_prev(dev)
-        h = xp
-        for i, (gm, bt, w) in enumerate(params):        # previous pass, untimed
-            st = sga.gn_silu_stats(h, g)
-            h = sga.causal_conv3d(h, w, None, residual=xp if i == 1 else None, fuse=(st, gm, bt, eps, g),
-                                  cache_out=caches[i])
-        del h, xp
         hbuf = torch.empty_like(x)
         y = torch.empty_like(x)
-        stats = torch.empty((wl.n, g, 2), dtype=torch.float64, device=dev)
-        ws = torch.empty(sga.gn_silu_stats_workspace(wl.shape, g), dtype=torch.uint8, device=dev)
+        xp = wl.x_prev(dev)                                 # previous pass, untimed
+        gcs[0](xp, hbuf, None, caches[0])
+        gcs[1](hbuf, y, None, caches[1], residual=xp)
+        del xp
 
         def step(timer=None):
-            (g1, b1, w1), (g2, b2, w2) = params
-            sga.gn_silu_stats(x, g, stats, ws)
-            mark(timer, "gn_silu_stats")
-            sga.causal_conv3d(x, w1, caches[0], fuse=(stats, g1, b1, eps, g), y=hbuf, cache_out=caches[2])
-            mark(timer, "causal_conv3d (fused)")
-            sga.gn_silu_stats(hbuf, g, stats, ws)
-            mark(timer, "gn_silu_stats")
-            sga.causal_conv3d(hbuf, w2, caches[1], residual=x, fuse=(stats, g2, b2, eps, g), y=y,
-                              cache_out=caches[3])
-            mark(timer, "causal_conv3d (fused)")
+            gcs[0](x, hbuf, caches[0], caches[2], timer=timer)
+            gcs[1](hbuf, y, caches[1], caches[3], residual=x, timer=timer)
 
-        def conv_only():
-            (g1, b1, w1), _ = params
-            sga.causal_conv3d(x, w1, caches[0], fuse=(stats, g1, b1, eps, g), y=hbuf)
-
-        flops = 2 * conv_flops(wl.n, wl.t, wl.h, wl.w, wl.c, wl.c)
-        return step, conv_only, (x, stats, ws, params[0][0], params[0][1]), flops, {"conv": "2 x 256->256 3x3x3 causal"}
+        conv = conv_flops(wl.n, wl.t, wl.h, wl.w, wl.c, wl.c)
+        return (step, lambda: gcs[0].conv_only(x, hbuf, caches[0]), (x, gcs[0]), 2 * conv, conv,
+                {"conv": "2 x %d->%d 3x3x3 causal" % (wl.c, wl.c)}, conv_name)
     # head
     x = wl.x(dev)
     w = wl.conv_weight(1, dev)
+    gc = GnConv(wl.shape, 12, g, eps, gamma, beta, w, dev, fused, head=True)
     video = torch.empty((wl.n, 3, wl.t, 2 * wl.h, 2 * wl.w), dtype=torch.bfloat16, device=dev)
-    stats = torch.empty((wl.n, g, 2), dtype=torch.float64, device=dev)
-    ws = torch.empty(sga.gn_silu_stats_workspace(wl.shape, g), dtype=torch.uint8, device=dev)
 
     def step(timer=None):
-        sga.gn_silu_stats(x, g, stats, ws)
-        mark(timer, "gn_silu_stats")
-        sga.head_conv_d2s(x, w, None, None, fuse=(stats, gamma, beta, eps, g), video=video)
-        mark(timer, "head_conv_d2s (fused)")
-
-    def conv_only():
-        sga.head_conv_d2s(x, w, None, None, fuse=(stats, gamma, beta, eps, g), video=video)
+        gc(x, video, timer=timer)
 
     flops = conv_flops(wl.n, wl.t, wl.h, wl.w, 12, wl.c)
-    return step, conv_only, (x, stats, ws, gamma, beta), flops, {"conv": "256->12 3x3x3 causal + d2s"}
+    return (step, lambda: gc.conv_only(x, video), (x, gc), flops, flops,
+            {"conv": "%d->12 3x3x3 causal + d2s" % wl.c},
+            "head_conv_d2s" + (" (fused GroupNorm+SiLU)" if fused else ""))
 
 
 def mark(timer, name):
@@ -249,6 +258,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2, choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--fused", action="store_true",
+                    help="apply GroupNorm+SiLU inside the conv's operand load instead of gn_silu_apply")
     ap.add_argument("--profile-pass", action="store_true",
                     help="for hardware-counter runs: one warm-up step, then 5 launches of the dominant "
                          "kernel and 3 plain copies of 1 GiB (the counters' scale), nothing else")
@@ -263,7 +274,7 @@ def main():
     sga.load_library()
     dev = "cuda:0"
     wl = WORKLOADS[args.config]
-    step, conv_only, gn_in, flops, info = build_step(wl, dev)
+    step, conv_only, gn_in, flops, conv_launch_flops, info, conv_name = build_step(wl, dev, args.fused)
 
     if args.profile_pass:
         step()
@@ -303,15 +314,12 @@ def main():
     # the conv kernel alone (no cache write), and GroupNorm+SiLU unfused on the same tensor
     iters = max(args.steps, 10)
     conv_ms = time_loop(conv_only, iters)
-    x, stats, ws, gamma, beta = gn_in
+    x, gc = gn_in
     g = wl.groups
     yb = torch.empty_like(x)
-    stats_ms = time_loop(lambda: sga.gn_silu_stats(x, g, stats, ws), iters)
-    apply_ms = time_loop(lambda: sga.gn_silu_apply(x, g, stats, gamma, beta, wl.eps, y=yb), iters)
+    stats_ms = time_loop(lambda: sga.gn_silu_stats(x, g, gc.stats, gc.ws), iters)
+    apply_ms = time_loop(lambda: sga.gn_silu_apply(x, g, gc.stats, gc.gamma, gc.beta, wl.eps, y=yb), iters)
     gn_bytes = 6.0 * x.numel()
-    conv_launch_flops = flops if wl.kind != "resblock" else flops / 2
-    if wl.kind == "upsample":
-        conv_launch_flops = conv_flops(*x.shape[:4], wl.c, wl.c)
     achieved = conv_launch_flops / (conv_ms * 1e-3) / 1e12
     gn_gbps = gn_bytes / ((stats_ms + apply_ms) * 1e-3) / 1e9
 
@@ -329,12 +337,13 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": wl.name, "shape_ndhwc": list(wl.shape), "k": wl.k, "groups": g,
+                   "gn_silu": "fused into the conv operand load" if args.fused else "gn_silu_apply, then the conv",
                    "parallelism": "none (1 GPU)", **info},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": read_traffic("conv_kernel_%s" % wl.name),
-                     "kernel": "conv_kernel (causal_conv3d fused)" if wl.kind != "head" else "conv_kernel (head)",
-                     "kernel_ms": round(conv_ms, 4)},
+                     "traffic": read_traffic("conv_kernel_%s%s" % (wl.name, "_fused" if args.fused else "")),
+                     "kernel": "conv_kernel (%s)" % conv_name, "kernel_ms": round(conv_ms, 4),
+                     "flop_per_launch": conv_launch_flops},
         "gn_silu": {"GB/s": round(gn_gbps, 1), "peak": PEAK_HBM_GBPS, "frac": round(gn_gbps / PEAK_HBM_GBPS, 4),
                     "stats_ms": round(stats_ms, 4), "apply_ms": round(apply_ms, 4),
                     "stats_GB/s": round(2.0 * x.numel() / (stats_ms * 1e-3) / 1e9, 1),

@@ -10,7 +10,9 @@
 // (128 bytes each) from global memory straight into LDS (global_load_lds_dwordx4: no
 // VGPR round trip), double buffered, and every wave runs v_mfma_f32_32x32x16_bf16 on
 // its sub-tile. The 16-byte chunks of each 128-byte LDS row are XOR-swizzled by the
-// row index so that the MFMA operand reads (ds_read_b128) are bank-conflict free.
+// row index (physical chunk = logical ^ f(row), f(row) = (row & 7) ^ ((row >> 3) & 1)) so
+// that the MFMA operand reads (ds_read_b128, 32 consecutive rows, one logical chunk) hit
+// distinct banks both per 8 lanes (128 B) and per 16 lanes (256 B, two rows apart).
 // With GroupNorm fused, position rows of the current frames go through VGPRs instead:
 // loaded, activated by the same activate_packet() as gn_silu_apply (so the result is
 // bitwise that of apply-then-convolve), and written to the same swizzled slots.
@@ -101,7 +103,9 @@ __global__ __launch_bounds__(kConvThreads, 1) void conv_kernel(ConvParams p) {
   const int C = p.C, K = p.K, H = p.H, W = p.W, T = p.T;
   const int kpt = C / kBK;
   const int KS = TAPS * kpt;
-  const int lc = (lane & 7) ^ (lane >> 3);           // logical 16-byte chunk this lane moves
+  // Logical 16-byte chunk this lane moves: its row is qi*8 + (lane >> 3) with qi = wave + 4j,
+  // so (row & 7) = lane >> 3 and (row >> 3) & 1 = wave & 1 for every j.
+  const int lc = (lane & 7) ^ (lane >> 3) ^ (wave & 1);
 
   // Weight rows: consecutive k-steps are consecutive 64-channel slices of a row.
   const uint16_t* wbase = p.w + (MODE == kPhase ? (int64_t)phase * K * 4 * C : 0);
@@ -246,7 +250,8 @@ __global__ __launch_bounds__(kConvThreads, 1) void conv_kernel(ConvParams p) {
     const char* lb = la + BN * 128;
 #pragma unroll
     for (int kk = 0; kk < kBK / 16; ++kk) {
-      const int chunk = ((kk * 2 + (lane >> 5)) ^ (lane & 7)) * 16;
+      // operand rows are (multiple of 32) + (lane & 31): f(row) from lane bits 0-3
+      const int chunk = ((kk * 2 + (lane >> 5)) ^ (lane & 7) ^ ((lane >> 3) & 1)) * 16;
       bf16x8 af[TN], bfr[TM];
 #pragma unroll
       for (int i = 0; i < TN; ++i)
