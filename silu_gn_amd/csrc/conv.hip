@@ -67,6 +67,76 @@ __device__ __forceinline__ void lds_dma16(const void* g, void* lds) {
   __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
 }
 
+// Epilogue shared by the convolution kernels. Lane l of a 32x32 accumulator tile holds
+// column m = l % 32 and rows k = 8 * (r / 4) + 4 * (l / 32) + r % 4 of element r; the
+// tile's k rows start at kbase + 32 * i, its m columns at mtile * BM + wm * WTM + 32 * j.
+// bias (+ residual) in fp32, one round to bf16, stored NDHWC (causal), interleaved at
+// (2h + a, 2w + b) (phases), or unfolded 2x2 into the channels-first video (head).
+template <int MODE, int TN, int TM, int WTM, int WTN>
+__device__ __forceinline__ void store_tile(const f32x16 (&acc)[TN][TM], const ConvParams& p, int n,
+                                           int64_t m0, int kbase, int wm, int lane, int phase) {
+  const int K = p.K, H = p.H, W = p.W, T = p.T;
+  const int pa = phase >> 1, pb = phase & 1;
+#pragma unroll
+  for (int j = 0; j < TM; ++j) {
+    const int64_t m = m0 + wm * WTM + j * 32 + (lane & 31);
+    if (m >= p.mper) continue;
+    const int w_ = (int)(m % W);
+    const int64_t th = m / W;
+    const int h_ = (int)(th % H);
+    const int t_ = (int)(th / H);
+#pragma unroll
+    for (int i = 0; i < TN; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int k0 = kbase + i * 32 + 8 * q + 4 * (lane >> 5);
+        if (k0 >= K) continue;
+        float v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = acc[i][j][4 * q + r];
+        if (p.bias) {
+          const float4 b = *reinterpret_cast<const float4*>(p.bias + k0);
+          v[0] += b.x;
+          v[1] += b.y;
+          v[2] += b.z;
+          v[3] += b.w;
+        }
+        if (MODE == kCausal) {
+          const int64_t off = ((int64_t)n * p.mper + m) * K + k0;
+          if (p.res) {
+            const uint2 rr = *reinterpret_cast<const uint2*>(p.res + off);
+            v[0] += bf16_lo(rr.x);
+            v[1] += bf16_hi(rr.x);
+            v[2] += bf16_lo(rr.y);
+            v[3] += bf16_hi(rr.y);
+          }
+          uint2 o;
+          o.x = pack_bf16x2(v[0], v[1]);
+          o.y = pack_bf16x2(v[2], v[3]);
+          *reinterpret_cast<uint2*>(p.y + off) = o;
+        } else if (MODE == kPhase) {
+          const int64_t yy = 2 * h_ + pa, xx = 2 * w_ + pb;
+          const int64_t off = ((((int64_t)n * T + t_) * (2 * H) + yy) * (2 * W) + xx) * K + k0;
+          uint2 o;
+          o.x = pack_bf16x2(v[0], v[1]);
+          o.y = pack_bf16x2(v[2], v[3]);
+          *reinterpret_cast<uint2*>(p.y + off) = o;
+        } else {
+          // K = 12: k0 = 4c, the four values are (dy, dx) = (0,0), (0,1), (1,0), (1,1).
+          if (p.clamp) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) v[r] = fminf(fmaxf(v[r], -1.0f), 1.0f);
+          }
+          const int c = k0 >> 2;
+          const int64_t W2 = 2 * (int64_t)W;
+          const int64_t base = (((int64_t)n * 3 + c) * T + t_) * (2 * (int64_t)H) * W2;
+          *reinterpret_cast<uint32_t*>(p.y + base + (2 * h_) * W2 + 2 * w_) = pack_bf16x2(v[0], v[1]);
+          *reinterpret_cast<uint32_t*>(p.y + base + (2 * h_ + 1) * W2 + 2 * w_) = pack_bf16x2(v[2], v[3]);
+        }
+      }
+  }
+}
+
 template <int BM, int BN, int WGM, int WGN, int MODE, bool FUSE>
 __global__ __launch_bounds__(kConvThreads, 1) void conv_kernel(ConvParams p) {
   constexpr int TAPS = MODE == kPhase ? 4 : 27;
@@ -271,66 +341,7 @@ __global__ __launch_bounds__(kConvThreads, 1) void conv_kernel(ConvParams p) {
     }
   }
 
-  // Epilogue. Lane l of a 32x32 tile holds column m = l % 32 and rows
-  // k = 8 * (r / 4) + 4 * (l / 32) + r % 4 of accumulator element r.
-#pragma unroll
-  for (int j = 0; j < TM; ++j) {
-    const int64_t m = (int64_t)mtile * BM + wm * WTM + j * 32 + (lane & 31);
-    if (m >= p.mper) continue;
-    const int w_ = (int)(m % W);
-    const int64_t th = m / W;
-    const int h_ = (int)(th % H);
-    const int t_ = (int)(th / H);
-#pragma unroll
-    for (int i = 0; i < TN; ++i)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int k0 = ntile * BN + wn * WTN + i * 32 + 8 * q + 4 * (lane >> 5);
-        if (k0 >= K) continue;
-        float v[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = acc[i][j][4 * q + r];
-        if (p.bias) {
-          const float4 b = *reinterpret_cast<const float4*>(p.bias + k0);
-          v[0] += b.x;
-          v[1] += b.y;
-          v[2] += b.z;
-          v[3] += b.w;
-        }
-        if (MODE == kCausal) {
-          const int64_t off = ((int64_t)n * p.mper + m) * K + k0;
-          if (p.res) {
-            const uint2 rr = *reinterpret_cast<const uint2*>(p.res + off);
-            v[0] += bf16_lo(rr.x);
-            v[1] += bf16_hi(rr.x);
-            v[2] += bf16_lo(rr.y);
-            v[3] += bf16_hi(rr.y);
-          }
-          uint2 o;
-          o.x = pack_bf16x2(v[0], v[1]);
-          o.y = pack_bf16x2(v[2], v[3]);
-          *reinterpret_cast<uint2*>(p.y + off) = o;
-        } else if (MODE == kPhase) {
-          const int64_t yy = 2 * h_ + pa, xx = 2 * w_ + pb;
-          const int64_t off = ((((int64_t)n * T + t_) * (2 * H) + yy) * (2 * W) + xx) * K + k0;
-          uint2 o;
-          o.x = pack_bf16x2(v[0], v[1]);
-          o.y = pack_bf16x2(v[2], v[3]);
-          *reinterpret_cast<uint2*>(p.y + off) = o;
-        } else {
-          // K = 12: k0 = 4c, the four values are (dy, dx) = (0,0), (0,1), (1,0), (1,1).
-          if (p.clamp) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) v[r] = fminf(fmaxf(v[r], -1.0f), 1.0f);
-          }
-          const int c = k0 >> 2;
-          const int64_t W2 = 2 * (int64_t)W;
-          const int64_t base = (((int64_t)n * 3 + c) * T + t_) * (2 * (int64_t)H) * W2;
-          *reinterpret_cast<uint32_t*>(p.y + base + (2 * h_) * W2 + 2 * w_) = pack_bf16x2(v[0], v[1]);
-          *reinterpret_cast<uint32_t*>(p.y + base + (2 * h_ + 1) * W2 + 2 * w_) = pack_bf16x2(v[2], v[3]);
-        }
-      }
-  }
+  store_tile<MODE, TN, TM, WTM, WTN>(acc, p, n, (int64_t)mtile * BM, ntile * BN + wn * WTN, wm, lane, phase);
 }
 
 // cache_out = the last 2 frames of P = cat(cache_in, a); frames of x are activated when
@@ -369,6 +380,243 @@ __global__ __launch_bounds__(256) void cache_out_kernel(
   }
 }
 
+// ---------------------------------------------------------------- pipelined kernel
+//
+// The unfused convolutions run on a software-pipelined form of the same implicit GEMM:
+// - a k-step ("stage") is one tap x 32 channels; its BN weight rows and BM position rows
+//   (64 bytes each) go global -> LDS with global_load_lds_dwordx4 into a ring of NS stage
+//   buffers, issued NS-1 stages ahead and waited for with counted vmcnt;
+// - each stage runs two MFMA phases (16 channels each); the operand fragments of the next
+//   phase are read from LDS while the current phase's MFMAs issue, one ds_read_b128 between
+//   every few MFMAs, so LDS latency never stalls the matrix pipe;
+// - one barrier per stage, between its two phases: it publishes stage s+1 (every wave has
+//   waited for its own moves of it) and retires stage s-1's buffer, which the stage
+//   s+NS-1 moves then overwrite.
+// The 16-byte chunks of each 64-byte row sit at physical chunk = logical ^ g(row), g(row) =
+// ((row >> 1) & 3) ^ ((row >> 3) & 1): fragment reads (32 consecutive rows, one logical
+// chunk) are conflict free for 8 and for 16 lanes per LDS cycle.
+// Per output the accumulation order is that of conv_kernel (taps outer, channels inner,
+// 16 at a time), so both kernels give the same bits.
+constexpr int kPK = 32;          // channels per pipeline stage
+
+#ifndef SGN_PIPE_STAGES
+#define SGN_PIPE_STAGES 4
+#endif
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Workgroup barrier without the memory fence of __syncthreads (which would also wait for
+// every outstanding LDS move); LDS-move completion is handled by the counted waits.
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int BM, int BN, int WGM, int WGN, int NS, int MODE>
+__global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_pipe_kernel(ConvParams p) {
+  constexpr int NW = WGM * WGN;
+  constexpr int TAPS = MODE == kPhase ? 4 : 27;
+  constexpr int WTM = BM / WGM, WTN = BN / WGN;
+  constexpr int TM = WTM / 32, TN = WTN / 32;
+  static_assert(TM * 32 * WGM == BM && TN * 32 * WGN == BN, "tile shape");
+  static_assert(BM % 16 == 0 && BN % 16 == 0 && NS >= 3, "pipeline shape");
+  constexpr int ROWB = kPK * 2;                      // bytes per LDS row
+  constexpr int STAGE = (BN + BM) * ROWB;
+  constexpr int IA = BN / 16, IB = BM / 16;          // 1 KB moves (16 rows) per stage
+  constexpr int IAW = (IA + NW - 1) / NW, IBW = (IB + NW - 1) / NW;
+
+  extern __shared__ __align__(16) char smem[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar branches
+
+  int tile;
+  {
+    const int bid = blockIdx.x, nb = p.nblocks;
+    const int xcd = bid & 7, idx = bid >> 3, q = nb >> 3, r = nb & 7;
+    tile = xcd < r ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
+  }
+  const int ntile = tile % p.tiles_n;
+  tile /= p.tiles_n;
+  int phase = 0;
+  if (MODE == kPhase) {
+    phase = tile & 3;
+    tile >>= 2;
+  }
+  const int mtile = tile % p.tiles_m;
+  const int n = tile / p.tiles_m;
+  const int pa = phase >> 1, pb = phase & 1;
+
+  const int C = p.C, K = p.K, H = p.H, W = p.W, T = p.T;
+  const int kpt = C / kPK;                           // stages per tap
+  const int KS = TAPS * kpt;
+  // This lane moves logical chunk lc of row (16 qi + (lane >> 2)); (row & 15) = lane >> 2.
+  const int lc = (lane & 3) ^ ((lane >> 3) & 3) ^ ((lane >> 5) & 1);
+
+  const uint16_t* wbase = p.w + (MODE == kPhase ? (int64_t)phase * K * 4 * C : 0);
+  const uint16_t* wptr[IAW];
+#pragma unroll
+  for (int j = 0; j < IAW; ++j) {
+    const int row = (wave + NW * j) * 16 + (lane >> 2);
+    int k = ntile * BN + row;
+    if (k > K - 1) k = K - 1;                        // columns past K: computed, never stored
+    wptr[j] = wbase + (int64_t)k * TAPS * C + lc * 8;
+  }
+  int rt[IBW], rhw[IBW];
+#pragma unroll
+  for (int j = 0; j < IBW; ++j) {
+    int64_t m = (int64_t)mtile * BM + (wave + NW * j) * 16 + (lane >> 2);
+    if (m > p.mper - 1) m = p.mper - 1;              // rows past the end: computed, never stored
+    const int w_ = (int)(m % W);
+    const int64_t th = m / W;
+    rt[j] = (int)(th / H);
+    rhw[j] = ((int)(th % H) << 16) | w_;
+  }
+
+  const uint16_t* rptr[IBW];
+  auto set_tap = [&](int tap) {
+    int dt, dh, dw;
+    if (MODE == kPhase) {
+      dt = 2;
+      dh = (tap >> 1) + pa;
+      dw = (tap & 1) + pb;
+    } else {
+      dt = tap / 9;
+      dh = (tap / 3) % 3;
+      dw = tap % 3;
+    }
+#pragma unroll
+    for (int j = 0; j < IBW; ++j) {
+      const int tt = rt[j] + dt - 2;
+      const int hh = (rhw[j] >> 16) + dh - 1;
+      const int ww = (rhw[j] & 0xffff) + dw - 1;
+      const bool inside = (unsigned)hh < (unsigned)H && (unsigned)ww < (unsigned)W;
+      const uint16_t* ptr = g_zero_row + lc * 8;
+      if (inside && tt >= 0)
+        ptr = p.x + ((((int64_t)n * T + tt) * H + hh) * W + ww) * C + lc * 8;
+      else if (inside && p.cache)
+        ptr = p.cache + ((((int64_t)n * 2 + tt + 2) * H + hh) * W + ww) * C + lc * 8;
+      rptr[j] = ptr;
+    }
+  };
+
+  // Issue side: the next stage to move and its (tap, chunk).
+  int is = 0, itap = 0, ichunk = 0, ibuf = 0;
+  set_tap(0);
+  auto issue_next = [&]() {
+    if (is >= KS) return;
+    char* lw = smem + ibuf * STAGE;
+    char* lp = lw + BN * ROWB;
+    const int64_t kofs = (int64_t)itap * C + ichunk * kPK;
+    const int cofs = ichunk * kPK;
+#pragma unroll
+    for (int j = 0; j < IAW; ++j) {
+      const int qi = wave + NW * j;
+      if (IA % NW == 0 || qi < IA) lds_dma16(wptr[j] + kofs, lw + qi * 1024);
+    }
+#pragma unroll
+    for (int j = 0; j < IBW; ++j) {
+      const int qi = wave + NW * j;
+      if (IB % NW == 0 || qi < IB) lds_dma16(rptr[j] + cofs, lp + qi * 1024);
+    }
+    ++is;
+    ibuf = ibuf == NS - 1 ? 0 : ibuf + 1;
+    if (++ichunk == kpt) {
+      ichunk = 0;
+      if (++itap < TAPS) set_tap(itap);
+    }
+  };
+
+  // Fragment reads: operand rows are (multiple of 32) + (lane & 31), so g(row) comes from
+  // lane bits 0-3; lanes 32-63 take the second logical chunk of a 16-channel phase.
+  const int wm = wave % WGM, wn = wave / WGM;
+  const int gl = ((lane >> 1) & 3) ^ ((lane >> 3) & 1);
+  const int rd = (lane & 31) * ROWB;
+  const int ck0 = ((lane >> 5) ^ gl) << 4;
+  const int ck1 = ((2 + (lane >> 5)) ^ gl) << 4;
+  auto load_frags = [&](bf16x8 (&a)[TN], bf16x8 (&b)[TM], int buf, int kk) {
+    const char* base = smem + buf * STAGE + rd + (kk ? ck1 : ck0);
+#pragma unroll
+    for (int i = 0; i < TN; ++i)
+      a[i] = *reinterpret_cast<const bf16x8*>(base + (wn * WTN + i * 32) * ROWB);
+#pragma unroll
+    for (int j = 0; j < TM; ++j)
+      b[j] = *reinterpret_cast<const bf16x8*>(base + (BN + wm * WTM + j * 32) * ROWB);
+  };
+
+  f32x16 acc[TN][TM];
+#pragma unroll
+  for (int i = 0; i < TN; ++i)
+#pragma unroll
+    for (int j = 0; j < TM; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+  auto mfmas = [&](const bf16x8 (&a)[TN], const bf16x8 (&b)[TM]) {
+#pragma unroll
+    for (int i = 0; i < TN; ++i)
+#pragma unroll
+      for (int j = 0; j < TM; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+  };
+  // One phase: its MFMAs with the next phase's fragment reads between the first few, so
+  // the reads complete long before the next phase needs them (and the wait the compiler
+  // places at the next phase's first MFMA never stalls).
+  constexpr int NRD = TN + TM, NMF = TN * TM;
+  constexpr int PAIRS = NRD < NMF ? NRD : NMF;
+  auto interleave = [&]() {
+#pragma unroll
+    for (int r = 0; r < PAIRS; ++r) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);     // one DS read
+    }
+    if (NRD > PAIRS) __builtin_amdgcn_sched_group_barrier(0x100, NRD - PAIRS, 0);
+    if (NMF > PAIRS) __builtin_amdgcn_sched_group_barrier(0x008, NMF - PAIRS, 0);
+  };
+  // Fewest LDS moves any wave issues per stage: a wave waiting until at most DMIN * j of its
+  // moves are in flight has completed all but (at most) its last j stages.
+  constexpr int DMIN = IA / NW + IB / NW;
+
+  // Prologue: NS-1 stages in flight; stage 0 published.
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s) issue_next();
+  if (KS >= NS - 1)
+    wait_vm<DMIN * (NS - 2)>();
+  else
+    wait_vm<0>();
+  stage_barrier();
+  bf16x8 a0[TN], b0[TM], a1[TN], b1[TM];
+  load_frags(a0, b0, 0, 0);
+  int buf = 0;
+  for (int s = 0; s < KS - 1; ++s) {
+    load_frags(a1, b1, buf, 1);
+    mfmas(a0, b0);
+    interleave();
+    __builtin_amdgcn_sched_barrier(0);
+    // Own moves of stage s+1 complete (those of the stages after it may stay in flight),
+    // then every wave's: stage s+1 is published and stage s-1's buffer is free.
+    if (s + NS - 1 <= KS)
+      wait_vm<DMIN * (NS - 3)>();
+    else
+      wait_vm<0>();                                  // the last few stages: wait for all
+    stage_barrier();
+    issue_next();
+    __builtin_amdgcn_sched_barrier(0);
+    buf = buf == NS - 1 ? 0 : buf + 1;
+    load_frags(a0, b0, buf, 0);
+    mfmas(a1, b1);
+    interleave();
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  load_frags(a1, b1, buf, 1);
+  mfmas(a0, b0);
+  mfmas(a1, b1);
+
+  store_tile<MODE, TN, TM, WTM, WTN>(acc, p, n, (int64_t)mtile * BM, ntile * BN + wn * WTN, wm, lane, phase);
+}
+
 // ---------------------------------------------------------------- host side
 
 typedef void (*ConvFn)(ConvParams);
@@ -377,6 +625,7 @@ struct TileCfg {
   int bm, bn;
   ConvFn fn;
   int lds;
+  int threads;
 };
 
 template <int BM, int BN, int WGM, int WGN, int MODE, bool FUSE>
@@ -386,7 +635,47 @@ static TileCfg make_cfg(int c) {
   t.bn = BN;
   t.fn = conv_kernel<BM, BN, WGM, WGN, MODE, FUSE>;
   t.lds = 2 * (BM + BN) * 128 + (FUSE ? c * 16 : 0);
+  t.threads = kConvThreads;
   return t;
+}
+
+template <int BM, int BN, int WGM, int WGN, int MODE>
+static TileCfg make_pipe_cfg() {
+  TileCfg t;
+  t.bm = BM;
+  t.bn = BN;
+  t.fn = conv_pipe_kernel<BM, BN, WGM, WGN, SGN_PIPE_STAGES, MODE>;
+  t.lds = SGN_PIPE_STAGES * (BM + BN) * kPK * 2;
+  t.threads = 64 * WGM * WGN;
+  return t;
+}
+
+// Candidate tiles of the pipelined kernel for N-tile width bn (largest M tile first).
+template <int MODE>
+static int pipe_candidates(int bn, TileCfg* out) {
+  int n = 0;
+  switch (bn) {
+    case 256:
+#ifdef SGN_PIPE_WAVES8
+      out[n++] = make_pipe_cfg<256, 256, 2, 4, MODE>();
+#else
+      out[n++] = make_pipe_cfg<256, 256, 2, 2, MODE>();
+#endif
+      out[n++] = make_pipe_cfg<224, 256, 1, 4, MODE>();
+      out[n++] = make_pipe_cfg<192, 256, 2, 2, MODE>();
+      out[n++] = make_pipe_cfg<128, 256, 2, 2, MODE>();
+      break;
+    case 128:
+      out[n++] = make_pipe_cfg<256, 128, 2, 2, MODE>();
+      break;
+    case 64:
+      out[n++] = make_pipe_cfg<256, 64, 4, 1, MODE>();
+      break;
+    default:
+      out[n++] = make_pipe_cfg<256, 32, 4, 1, MODE>();
+      break;
+  }
+  return n;
 }
 
 // Candidate tiles for N-tile width bn (largest M tile first).
@@ -414,11 +703,11 @@ static int candidates(int bn, int c, TileCfg* out) {
 }
 
 // Pick the M tile that minimises (waves of workgroups over 256 CUs) x (work per tile).
-template <int MODE, bool FUSE>
+template <int MODE, bool FUSE, bool PIPE>
 static TileCfg choose_tile(int64_t mper, int k, int c, int64_t groups_of_tiles) {
   const int bn = k > 128 ? 256 : k > 64 ? 128 : k > 32 ? 64 : 32;
   TileCfg cand[4];
-  const int nc = candidates<MODE, FUSE>(bn, c, cand);
+  const int nc = PIPE ? pipe_candidates<MODE>(bn, cand) : candidates<MODE, FUSE>(bn, c, cand);
   TileCfg best = cand[0];
   double best_cost = 1e300;
   for (int i = 0; i < nc; ++i) {
@@ -450,7 +739,7 @@ static bool launch_conv(const TileCfg& cfg, ConvParams& p, int64_t n_samples, in
     return false;
   }
   void* args[] = {&p};
-  e = hipLaunchKernel((const void*)cfg.fn, dim3((unsigned)nb), dim3(kConvThreads), args, cfg.lds, stream);
+  e = hipLaunchKernel((const void*)cfg.fn, dim3((unsigned)nb), dim3(cfg.threads), args, cfg.lds, stream);
   if (e != hipSuccess) {
     set_error("%s: launch failed: %s", fn, hipGetErrorString(e));
     return false;
@@ -577,8 +866,9 @@ extern "C" int causal_conv3d(const uint16_t* x, sgn_dims d, const uint16_t* cach
   p.C = (int)d.c;
   p.K = k;
   p.mper = d.t * d.h * d.w;
-  const TileCfg cfg = fuse ? choose_tile<kCausal, true>(p.mper, k, p.C, d.n)
-                           : choose_tile<kCausal, false>(p.mper, k, p.C, d.n);
+  // Unfused: the pipelined kernel; fused: the plain kernel's operand-load activation.
+  const TileCfg cfg = fuse ? choose_tile<kCausal, true, false>(p.mper, k, p.C, d.n)
+                           : choose_tile<kCausal, false, true>(p.mper, k, p.C, d.n);
   if (!launch_conv(cfg, p, d.n, 1, stream, fn)) return SGN_ELAUNCH;
   if (cache_out && !launch_cache_out(x, d, cache_in, fuse, cache_out, stream)) return SGN_ELAUNCH;
   return SGN_OK;
@@ -611,7 +901,7 @@ extern "C" int upsample2x_conv_phases(const uint16_t* x, sgn_dims d, const uint1
   p.C = (int)d.c;
   p.K = k;
   p.mper = d.t * d.h * d.w;
-  const TileCfg cfg = choose_tile<kPhase, false>(p.mper, k, p.C, d.n * 4);
+  const TileCfg cfg = choose_tile<kPhase, false, true>(p.mper, k, p.C, d.n * 4);
   if (!launch_conv(cfg, p, d.n, 4, stream, fn)) return SGN_ELAUNCH;
   return SGN_OK;
 }
