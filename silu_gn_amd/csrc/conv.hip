@@ -5,17 +5,12 @@
 // GEMM view (per sample, per upsample phase):
 //   D[k][m] = sum_{tap, c} W[k][tap][c] * P[src(m, tap)][c]
 // with m an output position, k an output channel and src(m, tap) the input position a
-// tap reads (or a zero row for padding). A workgroup of 4 waves computes a BN x BM
-// tile of D; each k-step moves BN weight rows and BM position rows of 64 channels
-// (128 bytes each) from global memory straight into LDS (global_load_lds_dwordx4: no
-// VGPR round trip), double buffered, and every wave runs v_mfma_f32_32x32x16_bf16 on
-// its sub-tile. The 16-byte chunks of each 128-byte LDS row are XOR-swizzled by the
-// row index (physical chunk = logical ^ f(row), f(row) = (row & 7) ^ ((row >> 3) & 1)) so
-// that the MFMA operand reads (ds_read_b128, 32 consecutive rows, one logical chunk) hit
-// distinct banks both per 8 lanes (128 B) and per 16 lanes (256 B, two rows apart).
-// With GroupNorm fused, position rows of the current frames go through VGPRs instead:
-// loaded, activated by the same activate_packet() as gn_silu_apply (so the result is
-// bitwise that of apply-then-convolve), and written to the same swizzled slots.
+// tap reads (or a zero row for padding). A workgroup of 4 waves computes a BN x BM tile
+// of D with v_mfma_f32_32x32x16_bf16, its operands staged through a ring of LDS buffers
+// (conv_kernel below describes the pipeline). With GroupNorm fused, position rows go
+// through VGPRs instead of straight to LDS: loaded, activated by the same
+// activate_packet() as gn_silu_apply (so the result is bitwise that of
+// apply-then-convolve), and written to the same swizzled slots.
 //
 // Pages: FastVideo wan22_vae_decode binding.cpp -- Decoder::conv (causal front padding
 // of kt-1 frames from the cache, 1-pixel spatial zero padding, the cache keeps the last
@@ -35,12 +30,7 @@ namespace sgn {
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 
-constexpr int kBK = 64;          // channels per k-step
-constexpr int kCMax = 4096;      // largest C: the zero row below covers one position
-constexpr int kConvThreads = 256;
-
-// One position's worth of zeros: padding rows are loaded from here.
-__device__ __align__(256) uint16_t g_zero_row[kCMax];
+constexpr int kCMax = 4096;      // largest C
 
 enum Mode { kCausal = 0, kPhase = 1, kHead = 2 };
 
@@ -57,30 +47,29 @@ struct ConvParams {
   double eps;
   int groups;
   int T, H, W, C, K;
-  int tiles_m, tiles_n;
+  int tiles_f, tiles_n;      // tiles per frame (M), tiles along K (N)
   int64_t mper;              // output positions per sample (and per phase)
   int nblocks;
   int clamp;
 };
 
-__device__ __forceinline__ void lds_dma16(const void* g, void* lds) {
-  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
-}
 
 // Epilogue shared by the convolution kernels. Lane l of a 32x32 accumulator tile holds
 // column m = l % 32 and rows k = 8 * (r / 4) + 4 * (l / 32) + r % 4 of element r; the
-// tile's k rows start at kbase + 32 * i, its m columns at mtile * BM + wm * WTM + 32 * j.
+// tile's k rows start at kbase + 32 * i, its m columns at m0 + wm * WTM + 32 * j; columns
+// at or past mlimit (the end of the tile's frame) are not stored.
 // bias (+ residual) in fp32, one round to bf16, stored NDHWC (causal), interleaved at
 // (2h + a, 2w + b) (phases), or unfolded 2x2 into the channels-first video (head).
 template <int MODE, int TN, int TM, int WTM, int WTN>
 __device__ __forceinline__ void store_tile(const f32x16 (&acc)[TN][TM], const ConvParams& p, int n,
-                                           int64_t m0, int kbase, int wm, int lane, int phase) {
+                                           int64_t m0, int64_t mlimit, int kbase, int wm, int lane,
+                                           int phase) {
   const int K = p.K, H = p.H, W = p.W, T = p.T;
   const int pa = phase >> 1, pb = phase & 1;
 #pragma unroll
   for (int j = 0; j < TM; ++j) {
     const int64_t m = m0 + wm * WTM + j * 32 + (lane & 31);
-    if (m >= p.mper) continue;
+    if (m >= mlimit) continue;
     const int w_ = (int)(m % W);
     const int64_t th = m / W;
     const int h_ = (int)(th % H);
@@ -137,213 +126,6 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[TN][TM], const Co
   }
 }
 
-template <int BM, int BN, int WGM, int WGN, int MODE, bool FUSE>
-__global__ __launch_bounds__(kConvThreads, 1) void conv_kernel(ConvParams p) {
-  constexpr int TAPS = MODE == kPhase ? 4 : 27;
-  constexpr int WTM = BM / WGM, WTN = BN / WGN;
-  constexpr int TM = WTM / 32, TN = WTN / 32;
-  static_assert(TM * 32 * WGM == BM && TN * 32 * WGN == BN && WGM * WGN == 4, "tile shape");
-  constexpr int STAGE = (BN + BM) * 128;
-  constexpr int IA = BN / 8, IB = BM / 8;            // 64-lane DMA instructions per k-step
-  constexpr int IAW = (IA + 3) / 4, IBW = (IB + 3) / 4;
-
-  extern __shared__ __align__(16) char smem[];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-
-  // Workgroup -> tile. Workgroups are dealt to the 8 XCDs round-robin; renumber so that
-  // each XCD works through a contiguous run of tiles (neighbouring tiles share input
-  // rows and weights in that XCD's L2). Order inside a run: N tile, phase, M tile, sample.
-  int tile;
-  {
-    const int bid = blockIdx.x, nb = p.nblocks;
-    const int xcd = bid & 7, idx = bid >> 3, q = nb >> 3, r = nb & 7;
-    tile = xcd < r ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
-  }
-  const int ntile = tile % p.tiles_n;
-  tile /= p.tiles_n;
-  int phase = 0;
-  if (MODE == kPhase) {
-    phase = tile & 3;
-    tile >>= 2;
-  }
-  const int mtile = tile % p.tiles_m;
-  const int n = tile / p.tiles_m;
-  const int pa = phase >> 1, pb = phase & 1;
-
-  const int C = p.C, K = p.K, H = p.H, W = p.W, T = p.T;
-  const int kpt = C / kBK;
-  const int KS = TAPS * kpt;
-  // Logical 16-byte chunk this lane moves: its row is qi*8 + (lane >> 3) with qi = wave + 4j,
-  // so (row & 7) = lane >> 3 and (row >> 3) & 1 = wave & 1 for every j.
-  const int lc = (lane & 7) ^ (lane >> 3) ^ (wave & 1);
-
-  // Weight rows: consecutive k-steps are consecutive 64-channel slices of a row.
-  const uint16_t* wbase = p.w + (MODE == kPhase ? (int64_t)phase * K * 4 * C : 0);
-  int woff[IAW];
-#pragma unroll
-  for (int j = 0; j < IAW; ++j) {
-    const int qi = wave + 4 * j;
-    int row = qi * 8 + (lane >> 3);
-    int k = ntile * BN + row;
-    if (k > K - 1) k = K - 1;                        // columns past K are computed, never stored
-    woff[j] = k * TAPS * C + lc * 8;
-  }
-
-  // Position rows of this lane: (t, h, w) of output position m.
-  int rt[IBW], rhw[IBW];
-#pragma unroll
-  for (int j = 0; j < IBW; ++j) {
-    const int qi = wave + 4 * j;
-    int64_t m = (int64_t)mtile * BM + qi * 8 + (lane >> 3);
-    if (m > p.mper - 1) m = p.mper - 1;              // rows past the end: computed, never stored
-    const int w_ = (int)(m % W);
-    const int64_t th = m / W;
-    const int h_ = (int)(th % H);
-    rt[j] = (int)(th / H);
-    rhw[j] = (h_ << 16) | w_;
-  }
-
-  const uint16_t* rptr[IBW];
-  int rkind[IBW];                                    // 0 activate, 1 copy, 2 zero (fused path)
-  auto set_tap = [&](int tap) {
-    int dt, dh, dw;
-    if (MODE == kPhase) {
-      dt = 2;
-      dh = (tap >> 1) + pa;                          // row offset u + a - 1, stored +1
-      dw = (tap & 1) + pb;
-    } else {
-      dt = tap / 9;
-      dh = (tap / 3) % 3;
-      dw = tap % 3;
-    }
-#pragma unroll
-    for (int j = 0; j < IBW; ++j) {
-      const int tt = rt[j] + dt - 2;
-      const int hh = (rhw[j] >> 16) + dh - 1;
-      const int ww = (rhw[j] & 0xffff) + dw - 1;
-      const bool inside = (unsigned)hh < (unsigned)H && (unsigned)ww < (unsigned)W;
-      const uint16_t* ptr = g_zero_row + lc * 8;
-      int kind = 2;
-      if (inside && tt >= 0) {
-        ptr = p.x + ((((int64_t)n * T + tt) * H + hh) * W + ww) * C + lc * 8;
-        kind = 0;
-      } else if (inside && p.cache) {
-        ptr = p.cache + ((((int64_t)n * 2 + tt + 2) * H + hh) * W + ww) * C + lc * 8;
-        kind = 1;
-      }
-      rptr[j] = ptr;
-      rkind[j] = kind;
-    }
-  };
-
-  // Fused GroupNorm: per-channel fp64 affines of this sample, kept in LDS.
-  double* tab = reinterpret_cast<double*>(smem + 2 * STAGE);
-  if (FUSE) {
-    const int cg = C / p.groups;
-    for (int c = tid; c < C; c += kConvThreads) {
-      const Affine a = channel_affine(p.stats, p.gamma, p.beta, p.eps, p.groups, cg, n, c);
-      tab[2 * c] = a.s;
-      tab[2 * c + 1] = a.b;
-    }
-  }
-
-  uint4 held[FUSE ? IBW : 1];
-  auto issue = [&](int ks, int stage) {
-    char* lw = smem + stage * STAGE;
-    char* lp = lw + BN * 128;
-    const int c0 = (ks % kpt) * kBK;
-#pragma unroll
-    for (int j = 0; j < IAW; ++j) {
-      const int qi = wave + 4 * j;
-      if (qi < IA) lds_dma16(wbase + woff[j] + ks * kBK, lw + qi * 1024);
-    }
-#pragma unroll
-    for (int j = 0; j < IBW; ++j) {
-      const int qi = wave + 4 * j;
-      if (qi < IB) {
-        if (FUSE)
-          held[j] = *reinterpret_cast<const uint4*>(rptr[j] + c0);
-        else
-          lds_dma16(rptr[j] + c0, lp + qi * 1024);
-      }
-    }
-  };
-  // Fused path: activate the held position packets and store them into the stage.
-  auto commit = [&](int ks, int stage) {
-    if (!FUSE) return;
-    char* lp = smem + stage * STAGE + BN * 128;
-    const int c0 = (ks % kpt) * kBK + lc * 8;
-    Affine a[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      a[i].s = tab[2 * (c0 + i)];
-      a[i].b = tab[2 * (c0 + i) + 1];
-    }
-#pragma unroll
-    for (int j = 0; j < IBW; ++j) {
-      const int qi = wave + 4 * j;
-      if (qi < IB) {
-        uint4 v = held[j];
-        if (rkind[j] == 0) v = activate_packet(v, a);
-        *reinterpret_cast<uint4*>(lp + qi * 1024 + lane * 16) = v;
-      }
-    }
-  };
-
-  f32x16 acc[TN][TM];
-#pragma unroll
-  for (int i = 0; i < TN; ++i)
-#pragma unroll
-    for (int j = 0; j < TM; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-  const int wm = wave % WGM, wn = wave / WGM;
-  if (FUSE) __syncthreads();                         // affine table visible
-  set_tap(0);
-  issue(0, 0);
-  if (FUSE) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    commit(0, 0);
-  }
-
-  for (int ks = 0; ks < KS; ++ks) {
-    const int stage = ks & 1;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    const bool more = ks + 1 < KS;
-    if (more) {
-      if ((ks + 1) % kpt == 0) set_tap((ks + 1) / kpt);
-      issue(ks + 1, stage ^ 1);
-    }
-    const char* la = smem + stage * STAGE;
-    const char* lb = la + BN * 128;
-#pragma unroll
-    for (int kk = 0; kk < kBK / 16; ++kk) {
-      // operand rows are (multiple of 32) + (lane & 31): f(row) from lane bits 0-3
-      const int chunk = ((kk * 2 + (lane >> 5)) ^ (lane & 7) ^ ((lane >> 3) & 1)) * 16;
-      bf16x8 af[TN], bfr[TM];
-#pragma unroll
-      for (int i = 0; i < TN; ++i)
-        af[i] = *reinterpret_cast<const bf16x8*>(la + (wn * WTN + i * 32 + (lane & 31)) * 128 + chunk);
-#pragma unroll
-      for (int j = 0; j < TM; ++j)
-        bfr[j] = *reinterpret_cast<const bf16x8*>(lb + (wm * WTM + j * 32 + (lane & 31)) * 128 + chunk);
-#pragma unroll
-      for (int i = 0; i < TN; ++i)
-#pragma unroll
-        for (int j = 0; j < TM; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    }
-    if (FUSE && more) {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      commit(ks + 1, stage ^ 1);
-    }
-  }
-
-  store_tile<MODE, TN, TM, WTM, WTN>(acc, p, n, (int64_t)mtile * BM, ntile * BN + wn * WTN, wm, lane, phase);
-}
-
 // cache_out = the last 2 frames of P = cat(cache_in, a); frames of x are activated when
 // fused (same per-thread column layout and activate_packet as gn_silu_apply).
 __global__ __launch_bounds__(256) void cache_out_kernel(
@@ -380,33 +162,63 @@ __global__ __launch_bounds__(256) void cache_out_kernel(
   }
 }
 
-// ---------------------------------------------------------------- pipelined kernel
+// ---------------------------------------------------------------- the convolution kernel
 //
-// The unfused convolutions run on a software-pipelined form of the same implicit GEMM:
-// - a k-step ("stage") is one tap x 32 channels; its BN weight rows and BM position rows
-//   (64 bytes each) go global -> LDS with global_load_lds_dwordx4 into a ring of NS stage
-//   buffers, issued NS-1 stages ahead and waited for with counted vmcnt;
-// - each stage runs two MFMA phases (16 channels each); the operand fragments of the next
-//   phase are read from LDS while the current phase's MFMAs issue, one ds_read_b128 between
-//   every few MFMAs, so LDS latency never stalls the matrix pipe;
-// - one barrier per stage, between its two phases: it publishes stage s+1 (every wave has
-//   waited for its own moves of it) and retires stage s-1's buffer, which the stage
-//   s+NS-1 moves then overwrite.
+// Tiles never straddle a frame: a tile is BM consecutive positions of one frame t (the last
+// tile of a frame is ragged), so every tap reads one source frame -- frame t + dt - 2 of x,
+// a cache frame, or none -- chosen once per tap in scalar registers.
+// Operands move with raw buffer instructions over 128-bit descriptors. A descriptor spans
+// exactly the source frame, so a row above or below the frame falls outside it and reads
+// zeros; a row left or right of the frame gets an offset past every descriptor and reads
+// zeros too. Padding costs two VALU instructions per row and tap and no branch.
+// A stage is one tap x 32 channels, taps outer, channels inner: its BN weight rows and BM
+// position rows (64 bytes each) go to one of NS LDS stage buffers. (Channel-chunk outer
+// order halves the HBM traffic at the full-resolution shape but runs slower: the per-stage
+// tap switch costs more than the L2 misses it saves.)
+// - Weights (and, unfused, position rows) move global -> LDS with buffer_load_dwordx4 ...
+//   lds, NS-1 stages ahead, waited for with counted vmcnt.
+// - Fused GroupNorm: the position rows are loaded into VGPRs one stage ahead, activated by
+//   activate_packet() (the code gn_silu_apply runs, so the result is bitwise that of
+//   apply-then-convolve) and stored to the same swizzled LDS slots.
+// - Each stage runs two MFMA phases of 16 channels; the next phase's fragments are read
+//   from LDS between the current phase's MFMAs, so LDS latency never stalls the matrix pipe.
+// - One barrier per stage, between its two phases: it publishes stage s+1 (each wave has
+//   waited for its own moves of it) and retires stage s-1's buffer, which the moves of stage
+//   s+NS-1 then overwrite.
 // The 16-byte chunks of each 64-byte row sit at physical chunk = logical ^ g(row), g(row) =
 // ((row >> 1) & 3) ^ ((row >> 3) & 1): fragment reads (32 consecutive rows, one logical
 // chunk) are conflict free for 8 and for 16 lanes per LDS cycle.
-// Per output the accumulation order is that of conv_kernel (taps outer, channels inner,
-// 16 at a time), so both kernels give the same bits.
-constexpr int kPK = 32;          // channels per pipeline stage
+// Per output the accumulation order is fixed -- tap, then 16 channels at a time -- and
+// independent of T, the tile and the launch: results are deterministic, and a pass split
+// along T gives the same bits.
+constexpr int kPK = 32;                  // channels per stage
+constexpr int kStages = 4;               // LDS stage buffers (a fifth measured no faster)
+constexpr int kRsrcFlags = 0x00020000;   // descriptor dword 3 (gfx9 raw buffer, 32-bit data)
+constexpr uint32_t kOOB = 0x80000000u;   // an offset past every descriptor built here
 
-#ifndef SGN_PIPE_STAGES
-#define SGN_PIPE_STAGES 4
-#endif
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+
+__device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcFlags);
+}
+
+// 16 bytes per lane from r at voff + soff into LDS at lds + 16 * lane (lds wave-uniform).
+__device__ __forceinline__ void dma16(Rsrc r, uint32_t voff, uint32_t soff, void* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
+}
+
+__device__ __forceinline__ uint4 load16(Rsrc r, uint32_t voff, uint32_t soff) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
 
 template <int N>
 __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
+
+__device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 // Workgroup barrier without the memory fence of __syncthreads (which would also wait for
 // every outstanding LDS move); LDS-move completion is handled by the counted waits.
@@ -416,14 +228,14 @@ __device__ __forceinline__ void stage_barrier() {
   asm volatile("" ::: "memory");
 }
 
-template <int BM, int BN, int WGM, int WGN, int NS, int MODE>
-__global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_pipe_kernel(ConvParams p) {
+template <int BM, int BN, int WGM, int WGN, int NS, int MODE, bool FUSE>
+__global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_kernel(ConvParams p) {
   constexpr int NW = WGM * WGN;
   constexpr int TAPS = MODE == kPhase ? 4 : 27;
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
   constexpr int TM = WTM / 32, TN = WTN / 32;
   static_assert(TM * 32 * WGM == BM && TN * 32 * WGN == BN, "tile shape");
-  static_assert(BM % 16 == 0 && BN % 16 == 0 && NS >= 3, "pipeline shape");
+  static_assert(BM % 16 == 0 && BN % 16 == 0 && NS >= 4, "pipeline shape");
   constexpr int ROWB = kPK * 2;                      // bytes per LDS row
   constexpr int STAGE = (BN + BM) * ROWB;
   constexpr int IA = BN / 16, IB = BM / 16;          // 1 KB moves (16 rows) per stage
@@ -433,6 +245,10 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_pipe_kernel(ConvParams
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar branches
 
+  // Workgroup -> tile. Workgroups are dealt to the 8 XCDs round-robin; renumber so that
+  // each XCD works through a contiguous run of tiles (neighbouring tiles share input rows
+  // and weights in that XCD's L2). Order inside a run: N tile, phase, tile of the frame,
+  // frame, sample.
   int tile;
   {
     const int bid = blockIdx.x, nb = p.nblocks;
@@ -446,87 +262,137 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_pipe_kernel(ConvParams
     phase = tile & 3;
     tile >>= 2;
   }
-  const int mtile = tile % p.tiles_m;
-  const int n = tile / p.tiles_m;
+  const int mt = tile % p.tiles_f;
+  tile /= p.tiles_f;
+  const int t = tile % p.T;
+  const int n = tile / p.T;
   const int pa = phase >> 1, pb = phase & 1;
 
   const int C = p.C, K = p.K, H = p.H, W = p.W, T = p.T;
+  const int HW = H * W;
+  const uint32_t frame_bytes = (uint32_t)HW * C * 2;
   const int kpt = C / kPK;                           // stages per tap
   const int KS = TAPS * kpt;
   // This lane moves logical chunk lc of row (16 qi + (lane >> 2)); (row & 15) = lane >> 2.
   const int lc = (lane & 3) ^ ((lane >> 3) & 3) ^ ((lane >> 5) & 1);
 
-  const uint16_t* wbase = p.w + (MODE == kPhase ? (int64_t)phase * K * 4 * C : 0);
-  const uint16_t* wptr[IAW];
+  const Rsrc wr = make_rsrc(p.w + (MODE == kPhase ? (int64_t)phase * K * 4 * C : 0),
+                            (uint32_t)K * TAPS * C * 2);
+  uint32_t wvo[IAW];
 #pragma unroll
   for (int j = 0; j < IAW; ++j) {
-    const int row = (wave + NW * j) * 16 + (lane >> 2);
-    int k = ntile * BN + row;
+    int k = ntile * BN + (wave + NW * j) * 16 + (lane >> 2);
     if (k > K - 1) k = K - 1;                        // columns past K: computed, never stored
-    wptr[j] = wbase + (int64_t)k * TAPS * C + lc * 8;
+    wvo[j] = ((uint32_t)k * TAPS * C + lc * 8) * 2;
   }
-  int rt[IBW], rhw[IBW];
+  // Position rows this lane moves: byte offset in the frame, and which row / column
+  // neighbours exist.
+  uint32_t pvo[IBW];
+  bool wl[IBW], wrt[IBW], hu[IBW], hd[IBW];
 #pragma unroll
   for (int j = 0; j < IBW; ++j) {
-    int64_t m = (int64_t)mtile * BM + (wave + NW * j) * 16 + (lane >> 2);
-    if (m > p.mper - 1) m = p.mper - 1;              // rows past the end: computed, never stored
-    const int w_ = (int)(m % W);
-    const int64_t th = m / W;
-    rt[j] = (int)(th / H);
-    rhw[j] = ((int)(th % H) << 16) | w_;
+    int pos = mt * BM + (wave + NW * j) * 16 + (lane >> 2);
+    if (pos > HW - 1) pos = HW - 1;                  // rows past the frame: computed, never stored
+    const int h_ = pos / W, w_ = pos - h_ * W;
+    pvo[j] = ((uint32_t)pos * C + lc * 8) * 2;
+    wl[j] = w_ > 0;
+    wrt[j] = w_ < W - 1;
+    hu[j] = h_ > 0;
+    hd[j] = h_ < H - 1;
   }
 
-  const uint16_t* rptr[IBW];
+  // Per-tap state of the position cursor (uniform): the source frame's descriptor, whether
+  // it is a frame of x (fused: activate), the tap's byte offset within the frame and its
+  // row and column offsets dh, dw (0 = one before).
+  Rsrc prs = make_rsrc(p.x, 0);
+  bool from_x = false;
+  int pdelta = 0, tdh = 1, tdw = 1;
   auto set_tap = [&](int tap) {
     int dt, dh, dw;
     if (MODE == kPhase) {
       dt = 2;
-      dh = (tap >> 1) + pa;
+      dh = (tap >> 1) + pa;                          // row offset u + a - 1, stored +1
       dw = (tap & 1) + pb;
     } else {
       dt = tap / 9;
       dh = (tap / 3) % 3;
       dw = tap % 3;
     }
-#pragma unroll
-    for (int j = 0; j < IBW; ++j) {
-      const int tt = rt[j] + dt - 2;
-      const int hh = (rhw[j] >> 16) + dh - 1;
-      const int ww = (rhw[j] & 0xffff) + dw - 1;
-      const bool inside = (unsigned)hh < (unsigned)H && (unsigned)ww < (unsigned)W;
-      const uint16_t* ptr = g_zero_row + lc * 8;
-      if (inside && tt >= 0)
-        ptr = p.x + ((((int64_t)n * T + tt) * H + hh) * W + ww) * C + lc * 8;
-      else if (inside && p.cache)
-        ptr = p.cache + ((((int64_t)n * 2 + tt + 2) * H + hh) * W + ww) * C + lc * 8;
-      rptr[j] = ptr;
-    }
+    const int tf = t + dt - 2;
+    from_x = tf >= 0;
+    if (tf >= 0)
+      prs = make_rsrc(p.x + ((int64_t)n * T + tf) * HW * C, frame_bytes);
+    else if (p.cache)
+      prs = make_rsrc(p.cache + ((int64_t)n * 2 + tf + 2) * HW * C, frame_bytes);
+    else
+      prs = make_rsrc(p.x, 0);                       // no cache: zero frames
+    pdelta = ((dh - 1) * W + (dw - 1)) * C * 2;
+    tdh = dh;
+    tdw = dw;
   };
 
-  // Issue side: the next stage to move and its (tap, chunk).
-  int is = 0, itap = 0, ichunk = 0, ibuf = 0;
-  set_tap(0);
-  auto issue_next = [&]() {
-    if (is >= KS) return;
-    char* lw = smem + ibuf * STAGE;
-    char* lp = lw + BN * ROWB;
-    const int64_t kofs = (int64_t)itap * C + ichunk * kPK;
-    const int cofs = ichunk * kPK;
+  uint4 held[FUSE ? IBW : 1];
+  bool hact[FUSE ? IBW : 1];                         // fused: activate (a row of x in the frame)
+
+  // Weight rows of stage s -> LDS. Stage s = tap * kpt + chunk reads channels
+  // tap * C + chunk * 32 of every row: byte offset 64 s.
+  auto issue_w = [&](int s) {
+    char* lw = smem + (s % NS) * STAGE;
+    const uint32_t soff = (uint32_t)s * (kPK * 2);
 #pragma unroll
     for (int j = 0; j < IAW; ++j) {
       const int qi = wave + NW * j;
-      if (IA % NW == 0 || qi < IA) lds_dma16(wptr[j] + kofs, lw + qi * 1024);
+      if (IA % NW == 0 || qi < IA) dma16(wr, wvo[j], soff, lw + qi * 1024);
+    }
+  };
+  // Position rows of the cursor's stage -> LDS (unfused) or VGPRs (fused); then the cursor
+  // moves to the next stage.
+  int pstage = 0, itap = 0, ichunk = 0;
+  set_tap(0);
+  auto issue_p = [&]() {
+    char* lp = smem + (pstage % NS) * STAGE + BN * ROWB;
+    const int d = pdelta + ichunk * kPK * 2;
+#pragma unroll
+    for (int j = 0; j < IBW; ++j) {
+      const int qi = wave + NW * j;
+      if (IB % NW == 0 || qi < IB) {
+        const bool okw = tdw == 0 ? wl[j] : tdw == 2 ? wrt[j] : true;
+        const uint32_t voff = okw ? pvo[j] + (uint32_t)d : kOOB;
+        if (FUSE) {
+          held[j] = load16(prs, voff, 0);
+          hact[j] = from_x && okw && (tdh == 0 ? hu[j] : tdh == 2 ? hd[j] : true);
+        } else {
+          dma16(prs, voff, 0, lp + qi * 1024);
+        }
+      }
+    }
+    ++pstage;
+    if (++ichunk == kpt) {
+      ichunk = 0;
+      if (++itap < TAPS) set_tap(itap);
+    }
+  };
+  // Fused: per-channel fp64 affines of this sample, in LDS after the stage buffers; the held
+  // rows of stage s (channel chunk cchunk) are activated into its buffer.
+  double* tab = reinterpret_cast<double*>(smem + NS * STAGE);
+  auto commit_p = [&](int s) {
+    if (!FUSE) return;
+    const int c0 = (s % kpt) * kPK + lc * 8;
+    char* lp = smem + (s % NS) * STAGE + BN * ROWB;
+    Affine a[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      a[i].s = tab[2 * (c0 + i)];
+      a[i].b = tab[2 * (c0 + i) + 1];
     }
 #pragma unroll
     for (int j = 0; j < IBW; ++j) {
       const int qi = wave + NW * j;
-      if (IB % NW == 0 || qi < IB) lds_dma16(rptr[j] + cofs, lp + qi * 1024);
-    }
-    ++is;
-    ibuf = ibuf == NS - 1 ? 0 : ibuf + 1;
-    if (++ichunk == kpt) {
-      ichunk = 0;
-      if (++itap < TAPS) set_tap(itap);
+      if (IB % NW == 0 || qi < IB) {
+        uint4 v = held[j];
+        if (hact[j]) v = activate_packet(v, a);
+        *reinterpret_cast<uint4*>(lp + qi * 1024 + lane * 16) = v;
+      }
     }
   };
 
@@ -562,8 +428,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_pipe_kernel(ConvParams
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
   };
   // One phase: its MFMAs with the next phase's fragment reads between the first few, so
-  // the reads complete long before the next phase needs them (and the wait the compiler
-  // places at the next phase's first MFMA never stalls).
+  // the reads complete long before the next phase needs them.
   constexpr int NRD = TN + TM, NMF = TN * TM;
   constexpr int PAIRS = NRD < NMF ? NRD : NMF;
   auto interleave = [&]() {
@@ -575,17 +440,39 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_pipe_kernel(ConvParams
     if (NRD > PAIRS) __builtin_amdgcn_sched_group_barrier(0x100, NRD - PAIRS, 0);
     if (NMF > PAIRS) __builtin_amdgcn_sched_group_barrier(0x008, NMF - PAIRS, 0);
   };
-  // Fewest LDS moves any wave issues per stage: a wave waiting until at most DMIN * j of its
-  // moves are in flight has completed all but (at most) its last j stages.
-  constexpr int DMIN = IA / NW + IB / NW;
+  // Fewest moves any wave issues per stage: weights only (DW), and with unfused position
+  // rows (DMIN). A wave waiting until at most DMIN * j of its moves are in flight has
+  // completed all but (at most) its last j stages.
+  constexpr int DW = IA / NW;
+  constexpr int DMIN = DW + IB / NW;
 
-  // Prologue: NS-1 stages in flight; stage 0 published.
+  // Prologue: stage 0 published; the weights (unfused: and positions) of the next NS-2
+  // stages in flight; fused, the position rows of stage 1 in flight to VGPRs. KS >= NS
+  // always (C >= 64).
+  if (FUSE) {
+    const int cg = C / p.groups;
+    for (int c = tid; c < C; c += 64 * NW) {
+      const Affine a = channel_affine(p.stats, p.gamma, p.beta, p.eps, p.groups, cg, n, c);
+      tab[2 * c] = a.s;
+      tab[2 * c + 1] = a.b;
+    }
 #pragma unroll
-  for (int s = 0; s < NS - 1; ++s) issue_next();
-  if (KS >= NS - 1)
-    wait_vm<DMIN * (NS - 2)>();
-  else
+    for (int s = 0; s < NS - 2; ++s) issue_w(s);
+    issue_p();                                       // stage 0
     wait_vm<0>();
+    __syncthreads();                                 // affine table visible
+    commit_p(0);
+    issue_p();                                       // stage 1
+    issue_w(NS - 2);
+    wait_lgkm0();
+  } else {
+#pragma unroll
+    for (int s = 0; s < NS - 1; ++s) {
+      issue_w(s);
+      issue_p();
+    }
+    wait_vm<DMIN * (NS - 2)>();
+  }
   stage_barrier();
   bf16x8 a0[TN], b0[TM], a1[TN], b1[TM];
   load_frags(a0, b0, 0, 0);
@@ -595,14 +482,30 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_pipe_kernel(ConvParams
     mfmas(a0, b0);
     interleave();
     __builtin_amdgcn_sched_barrier(0);
-    // Own moves of stage s+1 complete (those of the stages after it may stay in flight),
-    // then every wave's: stage s+1 is published and stage s-1's buffer is free.
-    if (s + NS - 1 <= KS)
-      wait_vm<DMIN * (NS - 3)>();
-    else
-      wait_vm<0>();                                  // the last few stages: wait for all
-    stage_barrier();
-    issue_next();
+    if (FUSE) {
+      // Everything before the last weight moves (of stage s+NS-2) has completed: the held
+      // rows of stage s+1, and the weights of stage s+1.
+      if (s + NS - 2 < KS)
+        wait_vm<DW>();
+      else
+        wait_vm<0>();
+      commit_p(s + 1);
+      wait_lgkm0();
+    } else {
+      // Own moves of stage s+1 complete (those of the stages after it may stay in flight).
+      if (s + NS - 1 <= KS)
+        wait_vm<DMIN * (NS - 3)>();
+      else
+        wait_vm<0>();                                // the last few stages: wait for all
+    }
+    stage_barrier();                                 // stage s+1 published, s-1 retired
+    if (FUSE) {
+      if (s + 2 < KS) issue_p();                     // stage s+2
+      if (s + NS - 1 < KS) issue_w(s + NS - 1);
+    } else if (s + NS - 1 < KS) {
+      issue_w(s + NS - 1);
+      issue_p();                                     // stage s+NS-1
+    }
     __builtin_amdgcn_sched_barrier(0);
     buf = buf == NS - 1 ? 0 : buf + 1;
     load_frags(a0, b0, buf, 0);
@@ -614,7 +517,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_pipe_kernel(ConvParams
   mfmas(a0, b0);
   mfmas(a1, b1);
 
-  store_tile<MODE, TN, TM, WTM, WTN>(acc, p, n, (int64_t)mtile * BM, ntile * BN + wn * WTN, wm, lane, phase);
+  store_tile<MODE, TN, TM, WTM, WTN>(acc, p, n, (int64_t)t * HW + mt * BM, (int64_t)(t + 1) * HW,
+                                     ntile * BN + wn * WTN, wm, lane, phase);
 }
 
 // ---------------------------------------------------------------- host side
@@ -628,54 +532,15 @@ struct TileCfg {
   int threads;
 };
 
-template <int BM, int BN, int WGM, int WGN, int MODE, bool FUSE>
+template <int BM, int BN, int WGM, int WGN, int NS, int MODE, bool FUSE>
 static TileCfg make_cfg(int c) {
   TileCfg t;
   t.bm = BM;
   t.bn = BN;
-  t.fn = conv_kernel<BM, BN, WGM, WGN, MODE, FUSE>;
-  t.lds = 2 * (BM + BN) * 128 + (FUSE ? c * 16 : 0);
-  t.threads = kConvThreads;
-  return t;
-}
-
-template <int BM, int BN, int WGM, int WGN, int MODE>
-static TileCfg make_pipe_cfg() {
-  TileCfg t;
-  t.bm = BM;
-  t.bn = BN;
-  t.fn = conv_pipe_kernel<BM, BN, WGM, WGN, SGN_PIPE_STAGES, MODE>;
-  t.lds = SGN_PIPE_STAGES * (BM + BN) * kPK * 2;
+  t.fn = conv_kernel<BM, BN, WGM, WGN, NS, MODE, FUSE>;
+  t.lds = NS * (BM + BN) * kPK * 2 + (FUSE ? c * 16 : 0);
   t.threads = 64 * WGM * WGN;
   return t;
-}
-
-// Candidate tiles of the pipelined kernel for N-tile width bn (largest M tile first).
-template <int MODE>
-static int pipe_candidates(int bn, TileCfg* out) {
-  int n = 0;
-  switch (bn) {
-    case 256:
-#ifdef SGN_PIPE_WAVES8
-      out[n++] = make_pipe_cfg<256, 256, 2, 4, MODE>();
-#else
-      out[n++] = make_pipe_cfg<256, 256, 2, 2, MODE>();
-#endif
-      out[n++] = make_pipe_cfg<224, 256, 1, 4, MODE>();
-      out[n++] = make_pipe_cfg<192, 256, 2, 2, MODE>();
-      out[n++] = make_pipe_cfg<128, 256, 2, 2, MODE>();
-      break;
-    case 128:
-      out[n++] = make_pipe_cfg<256, 128, 2, 2, MODE>();
-      break;
-    case 64:
-      out[n++] = make_pipe_cfg<256, 64, 4, 1, MODE>();
-      break;
-    default:
-      out[n++] = make_pipe_cfg<256, 32, 4, 1, MODE>();
-      break;
-  }
-  return n;
 }
 
 // Candidate tiles for N-tile width bn (largest M tile first).
@@ -684,34 +549,35 @@ static int candidates(int bn, int c, TileCfg* out) {
   int n = 0;
   switch (bn) {
     case 256:
-      out[n++] = make_cfg<256, 256, 2, 2, MODE, FUSE>(c);
-      out[n++] = make_cfg<224, 256, 1, 4, MODE, FUSE>(c);
-      out[n++] = make_cfg<192, 256, 2, 2, MODE, FUSE>(c);
-      out[n++] = make_cfg<128, 256, 2, 2, MODE, FUSE>(c);
+      // 8 waves, two per SIMD: one wave's barrier and LDS waits hide under the other's
+      // MFMAs. Measured faster than 4-wave 224/192-row tiles even where those fill the
+      // last round of workgroups better (latent block: 0.74 vs 0.81 ms).
+      out[n++] = make_cfg<256, 256, 2, 4, kStages, MODE, FUSE>(c);
       break;
     case 128:
-      out[n++] = make_cfg<256, 128, 2, 2, MODE, FUSE>(c);
+      out[n++] = make_cfg<256, 128, 2, 2, kStages, MODE, FUSE>(c);
       break;
     case 64:
-      out[n++] = make_cfg<256, 64, 4, 1, MODE, FUSE>(c);
+      out[n++] = make_cfg<256, 64, 4, 1, kStages, MODE, FUSE>(c);
       break;
     default:
-      out[n++] = make_cfg<256, 32, 4, 1, MODE, FUSE>(c);
+      out[n++] = make_cfg<256, 32, 4, 1, kStages, MODE, FUSE>(c);
       break;
   }
   return n;
 }
 
 // Pick the M tile that minimises (waves of workgroups over 256 CUs) x (work per tile).
-template <int MODE, bool FUSE, bool PIPE>
-static TileCfg choose_tile(int64_t mper, int k, int c, int64_t groups_of_tiles) {
+// Tiles do not straddle frames: hw positions per frame, frames frames in all.
+template <int MODE, bool FUSE>
+static TileCfg choose_tile(int64_t hw, int64_t frames, int k, int c, int64_t groups_of_tiles) {
   const int bn = k > 128 ? 256 : k > 64 ? 128 : k > 32 ? 64 : 32;
   TileCfg cand[4];
-  const int nc = PIPE ? pipe_candidates<MODE>(bn, cand) : candidates<MODE, FUSE>(bn, c, cand);
+  const int nc = candidates<MODE, FUSE>(bn, c, cand);
   TileCfg best = cand[0];
   double best_cost = 1e300;
   for (int i = 0; i < nc; ++i) {
-    const int64_t tiles_m = (mper + cand[i].bm - 1) / cand[i].bm;
+    const int64_t tiles_m = (hw + cand[i].bm - 1) / cand[i].bm * frames;
     const int64_t tiles = tiles_m * ((k + bn - 1) / bn) * groups_of_tiles;
     const double cost = (double)((tiles + 255) / 256) * cand[i].bm;
     if (cost < best_cost * 0.999) {
@@ -725,13 +591,13 @@ static TileCfg choose_tile(int64_t mper, int k, int c, int64_t groups_of_tiles) 
 static bool launch_conv(const TileCfg& cfg, ConvParams& p, int64_t n_samples, int phases,
                         hipStream_t stream, const char* fn) {
   p.tiles_n = (p.K + cfg.bn - 1) / cfg.bn;
-  const int64_t tiles_m = (p.mper + cfg.bm - 1) / cfg.bm;
-  const int64_t nb = tiles_m * p.tiles_n * phases * n_samples;
-  if (tiles_m > (1 << 30) || nb > (int64_t)1 << 31) {
+  const int64_t tiles_f = ((int64_t)p.H * p.W + cfg.bm - 1) / cfg.bm;
+  const int64_t nb = tiles_f * p.T * p.tiles_n * phases * n_samples;
+  if (tiles_f > (1 << 30) || nb >= (int64_t)1 << 31) {
     set_error("%s: problem too large for one launch", fn);
     return false;
   }
-  p.tiles_m = (int)tiles_m;
+  p.tiles_f = (int)tiles_f;
   p.nblocks = (int)nb;
   hipError_t e = hipFuncSetAttribute((const void*)cfg.fn, hipFuncAttributeMaxDynamicSharedMemorySize, cfg.lds);
   if (e != hipSuccess) {
@@ -784,6 +650,13 @@ static bool conv_common_checks(const uint16_t* x, sgn_dims d, const uint16_t* w,
   }
   if (d.t * d.h * d.w >= ((int64_t)1 << 40)) {
     set_error("%s: too many positions per sample", fn);
+    return false;
+  }
+  // Operands are read through 32-bit buffer offsets within one frame (plus a row above and
+  // below it): a frame of C channels must stay well under 2 GiB.
+  if ((d.h + 2) * d.w * d.c * 2 >= ((int64_t)1 << 31)) {
+    set_error("%s: a frame of H=%lld x W=%lld x C=%lld exceeds the 2 GiB frame limit", fn,
+              (long long)d.h, (long long)d.w, (long long)d.c);
     return false;
   }
   return true;
@@ -866,9 +739,8 @@ extern "C" int causal_conv3d(const uint16_t* x, sgn_dims d, const uint16_t* cach
   p.C = (int)d.c;
   p.K = k;
   p.mper = d.t * d.h * d.w;
-  // Unfused: the pipelined kernel; fused: the plain kernel's operand-load activation.
-  const TileCfg cfg = fuse ? choose_tile<kCausal, true, false>(p.mper, k, p.C, d.n)
-                           : choose_tile<kCausal, false, true>(p.mper, k, p.C, d.n);
+  const TileCfg cfg = fuse ? choose_tile<kCausal, true>(d.h * d.w, d.t, k, p.C, d.n)
+                           : choose_tile<kCausal, false>(d.h * d.w, d.t, k, p.C, d.n);
   if (!launch_conv(cfg, p, d.n, 1, stream, fn)) return SGN_ELAUNCH;
   if (cache_out && !launch_cache_out(x, d, cache_in, fuse, cache_out, stream)) return SGN_ELAUNCH;
   return SGN_OK;
@@ -901,7 +773,7 @@ extern "C" int upsample2x_conv_phases(const uint16_t* x, sgn_dims d, const uint1
   p.C = (int)d.c;
   p.K = k;
   p.mper = d.t * d.h * d.w;
-  const TileCfg cfg = choose_tile<kPhase, false, true>(p.mper, k, p.C, d.n * 4);
+  const TileCfg cfg = choose_tile<kPhase, false>(d.h * d.w, d.t, k, p.C, d.n * 4);
   if (!launch_conv(cfg, p, d.n, 4, stream, fn)) return SGN_ELAUNCH;
   return SGN_OK;
 }
@@ -950,7 +822,7 @@ extern "C" int head_conv_d2s(const uint16_t* x, sgn_dims d, const uint16_t* cach
   p.K = k;
   p.mper = d.t * d.h * d.w;
   p.clamp = clamp ? 1 : 0;
-  const TileCfg cfg = fuse ? make_cfg<256, 32, 4, 1, kHead, true>(p.C) : make_cfg<256, 32, 4, 1, kHead, false>(p.C);
+  const TileCfg cfg = fuse ? make_cfg<256, 32, 4, 1, kStages, kHead, true>(p.C) : make_cfg<256, 32, 4, 1, kStages, kHead, false>(p.C);
   if (!launch_conv(cfg, p, d.n, 1, stream, fn)) return SGN_ELAUNCH;
   if (cache_out && !launch_cache_out(x, d, cache_in, fuse, cache_out, stream)) return SGN_ELAUNCH;
   return SGN_OK;
