@@ -521,6 +521,215 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_kernel(ConvParams p) {
                                      ntile * BN + wn * WTN, wm, lane, phase);
 }
 
+// ---------------------------------------------------------------- the output head
+//
+// The head convolution has K = 12 output channels: as an implicit GEMM every input row it
+// stages feeds only 12 (padded 16) MACs per channel, so the generic tile above spends its
+// time moving operands. This kernel keeps the operands where the reuse is instead:
+// - Weights live in registers for the whole kernel. Wave w owns channel chunks
+//   [w CPW, (w + 1) CPW) of 32 channels and holds its 27 x CPW weight fragments (the A
+//   operand of v_mfma_f32_16x16x32_bf16: 16 output channels x 32 input channels, rows
+//   12-15 zero). The 4 waves' partial sums are added through LDS when an output frame is
+//   complete.
+// - A workgroup owns one output row h and 64 columns (4 segments of 16) for every frame,
+//   and streams the input frames of P = cat(cache, x) once: frame p feeds output frames
+//   p - dt, dt = 0..2, held in a ring of 3 accumulators per segment. Output frame t is
+//   complete after input frame t + 2.
+// - Each input fragment (16 columns x 32 channels of one input row, the B operand: lane l
+//   holds column l % 16, channels 8 (l / 16) .. + 8) is loaded once and serves all 3 column
+//   taps: the dw = 0 / 2 fragments are DPP row shifts of it by one lane, with the neighbour
+//   column outside the segment supplied as the shift's "old" value. Each fragment then
+//   feeds 3 x 3 MFMAs (dw x dt).
+// - Loads are raw-buffer loads over the input frame: rows above or below the frame and
+//   columns outside [0, W) read zeros.
+// The epilogue adds the bias, clamps if asked, and writes the 2x2 depth-to-space video
+// (channel k = 4c + 2dy + dx) as 4-byte pairs, 64 contiguous bytes per 16 columns.
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+constexpr int kHeadSeg = 4;              // 16-column segments per workgroup
+
+template <int V>
+struct IC {
+  static constexpr int value = V;
+};
+
+template <int CPW>
+__global__ __launch_bounds__(256, 1) void head_kernel(ConvParams p, int wblocks) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int j = lane & 15, g = lane >> 4;            // column in the segment, channel group
+  const int C = p.C, H = p.H, W = p.W, T = p.T;
+  const int HW = H * W;
+  const uint32_t frame_bytes = (uint32_t)HW * C * 2;
+
+  // Workgroup -> (n, h, column block), XCD-aware: each XCD takes a contiguous run, so the
+  // workgroups of neighbouring rows -- which read the same input rows -- share its L2.
+  int blk;
+  {
+    const int bid = blockIdx.x, nb = p.nblocks;
+    const int xcd = bid & 7, idx = bid >> 3, q = nb >> 3, r = nb & 7;
+    blk = xcd < r ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
+  }
+  const int wb = blk % wblocks;
+  const int h = (blk / wblocks) % H;
+  const int n = blk / (wblocks * H);
+  const int w0 = wb * (16 * kHeadSeg);
+
+  // Weight fragments: a[c][tap] for this wave's chunks.
+  bf16x8 a[CPW][27];
+  {
+    const int k = j;                                 // output channel (A row) of this lane
+#pragma unroll
+    for (int c = 0; c < CPW; ++c)
+#pragma unroll
+      for (int tap = 0; tap < 27; ++tap) {
+        const int ch = (wave * CPW + c) * 32 + 8 * g;
+        if (k < 12)
+          a[c][tap] = *reinterpret_cast<const bf16x8*>(p.w + ((int64_t)k * 27 + tap) * C + ch);
+        else
+          a[c][tap] = bf16x8{};
+      }
+  }
+
+  // Byte offsets of this lane's main column and of its edge column (lane 0 of a row: the
+  // column before the segment; lane 15: the column after it) within a frame row, per
+  // segment; out-of-range columns read zeros.
+  uint32_t mo[kHeadSeg], eo[kHeadSeg];
+#pragma unroll
+  for (int s = 0; s < kHeadSeg; ++s) {
+    const int wm = w0 + 16 * s + j;
+    const int we = j == 0 ? w0 + 16 * s - 1 : j == 15 ? w0 + 16 * s + 16 : wm;
+    mo[s] = wm < W ? ((uint32_t)wm * C + wave * CPW * 32 + 8 * g) * 2 : kOOB;
+    eo[s] = (we >= 0 && we < W) ? ((uint32_t)we * C + wave * CPW * 32 + 8 * g) * 2 : kOOB;
+  }
+
+  f32x4 acc[3][kHeadSeg];
+#pragma unroll
+  for (int r = 0; r < 3; ++r)
+#pragma unroll
+    for (int s = 0; s < kHeadSeg; ++s) acc[r][s] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // Source frame p of P = cat(cache, x): a descriptor over it (no records: zeros).
+  auto frame_rsrc = [&](int pf) {
+    if (pf >= 2 && pf < T + 2) return make_rsrc(p.x + ((int64_t)n * T + pf - 2) * HW * C, frame_bytes);
+    if (pf < 2 && p.cache) return make_rsrc(p.cache + ((int64_t)n * 2 + pf) * HW * C, frame_bytes);
+    return make_rsrc(p.x, 0);
+  };
+  // One unit of work: input frame pf, input row h + dh - 1, channel chunk c, all segments.
+  struct Unit {
+    uint4 m[kHeadSeg], e[kHeadSeg];
+  };
+  auto load_unit = [&](int pf, int dh, int c) {
+    Unit u;
+    const Rsrc r = frame_rsrc(pf);
+    const int row = (h + dh - 1) * W * C * 2 + c * 64;   // may be negative: out of range
+#pragma unroll
+    for (int s = 0; s < kHeadSeg; ++s) {
+      u.m[s] = load16(r, mo[s] == kOOB ? kOOB : mo[s] + (uint32_t)row, 0);
+      u.e[s] = load16(r, eo[s] == kOOB ? kOOB : eo[s] + (uint32_t)row, 0);
+    }
+    return u;
+  };
+  auto dpp_shift = [&](uint4 old, uint4 src, bool right) {
+    uint4 o;
+    if (right) {                                     // lane j takes lane j - 1 (column - 1)
+      o.x = __builtin_amdgcn_update_dpp(old.x, src.x, 0x111, 0xf, 0xf, false);
+      o.y = __builtin_amdgcn_update_dpp(old.y, src.y, 0x111, 0xf, 0xf, false);
+      o.z = __builtin_amdgcn_update_dpp(old.z, src.z, 0x111, 0xf, 0xf, false);
+      o.w = __builtin_amdgcn_update_dpp(old.w, src.w, 0x111, 0xf, 0xf, false);
+    } else {                                         // lane j takes lane j + 1 (column + 1)
+      o.x = __builtin_amdgcn_update_dpp(old.x, src.x, 0x101, 0xf, 0xf, false);
+      o.y = __builtin_amdgcn_update_dpp(old.y, src.y, 0x101, 0xf, 0xf, false);
+      o.z = __builtin_amdgcn_update_dpp(old.z, src.z, 0x101, 0xf, 0xf, false);
+      o.w = __builtin_amdgcn_update_dpp(old.w, src.w, 0x101, 0xf, 0xf, false);
+    }
+    return o;
+  };
+  // Input frame pf = 3 q + U, row dh, chunk c: 3 column taps x 3 frame taps per segment into
+  // the ring slots of output frames pf - dt (slot (U - dt) mod 3).
+  auto compute_unit = [&](const Unit& u, auto U_, int dh, int c) {
+    constexpr int U = decltype(U_)::value;
+#pragma unroll
+    for (int s = 0; s < kHeadSeg; ++s) {
+      const uint4 b1 = u.m[s];
+      const uint4 b0 = dpp_shift(u.e[s], b1, true);
+      const uint4 b2 = dpp_shift(u.e[s], b1, false);
+      const bf16x8 bb[3] = {__builtin_bit_cast(bf16x8, b0), __builtin_bit_cast(bf16x8, b1),
+                            __builtin_bit_cast(bf16x8, b2)};
+#pragma unroll
+      for (int dw = 0; dw < 3; ++dw)
+#pragma unroll
+        for (int dt = 0; dt < 3; ++dt) {
+          const int slot = ((U - dt) % 3 + 3) % 3;
+          acc[slot][s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[c][dt * 9 + dh * 3 + dw], bb[dw],
+                                                                 acc[slot][s], 0, 0, 0);
+        }
+    }
+  };
+
+  // Output frame t (ring slot S) is complete: add the waves' partial sums through LDS (two
+  // buffers, one barrier per frame), then wave w writes segment w; the slot is cleared for
+  // output frame t + 3. Slots of frames before 0 only collect the taps that reach before
+  // the first frame: they are cleared without a store.
+  __shared__ f32x4 red[2][4][kHeadSeg][64];
+  const float* bias = p.bias;
+  int rb = 0;
+  auto retire = [&](int t, auto S_) {
+    constexpr int S = decltype(S_)::value;
+    if (t < 0) {
+#pragma unroll
+      for (int s = 0; s < kHeadSeg; ++s) acc[S][s] = f32x4{0.f, 0.f, 0.f, 0.f};
+      return;
+    }
+#pragma unroll
+    for (int s = 0; s < kHeadSeg; ++s) {
+      red[rb][wave][s][lane] = acc[S][s];
+      acc[S][s] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    __syncthreads();
+    if (t < T && g < 3) {
+      const int s = wave;
+      const int col = w0 + 16 * s + j;
+      if (col < W) {
+        f32x4 v = red[rb][0][s][lane];
+#pragma unroll
+        for (int q = 1; q < 4; ++q) v += red[rb][q][s][lane];
+        float o[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          o[r] = v[r] + (bias ? bias[4 * g + r] : 0.0f);
+          if (p.clamp) o[r] = fminf(fmaxf(o[r], -1.0f), 1.0f);
+        }
+        const int64_t W2 = 2 * (int64_t)W;
+        const int64_t base = (((int64_t)n * 3 + g) * T + t) * (2 * (int64_t)H) * W2 + 2 * (int64_t)col;
+        *reinterpret_cast<uint32_t*>(p.y + base + (2 * h) * W2) = pack_bf16x2(o[0], o[1]);
+        *reinterpret_cast<uint32_t*>(p.y + base + (2 * h + 1) * W2) = pack_bf16x2(o[2], o[3]);
+      }
+    }
+    rb ^= 1;
+  };
+
+  // Frames of P in groups of three (frames past T + 1 read zeros and store nothing).
+  const int groups3 = (T + 2 + 2) / 3;
+  for (int q = 0; q < groups3; ++q) {
+    const int pf0 = 3 * q;
+#pragma unroll
+    for (int dh = 0; dh < 3; ++dh)
+#pragma unroll
+      for (int c = 0; c < CPW; ++c) compute_unit(load_unit(pf0, dh, c), IC<0>{}, dh, c);
+    retire(pf0 - 2, IC<1>{});
+#pragma unroll
+    for (int dh = 0; dh < 3; ++dh)
+#pragma unroll
+      for (int c = 0; c < CPW; ++c) compute_unit(load_unit(pf0 + 1, dh, c), IC<1>{}, dh, c);
+    retire(pf0 - 1, IC<2>{});
+#pragma unroll
+    for (int dh = 0; dh < 3; ++dh)
+#pragma unroll
+      for (int c = 0; c < CPW; ++c) compute_unit(load_unit(pf0 + 2, dh, c), IC<2>{}, dh, c);
+    retire(pf0, IC<0>{});
+  }
+}
+
 // ---------------------------------------------------------------- host side
 
 typedef void (*ConvFn)(ConvParams);
@@ -822,8 +1031,25 @@ extern "C" int head_conv_d2s(const uint16_t* x, sgn_dims d, const uint16_t* cach
   p.K = k;
   p.mper = d.t * d.h * d.w;
   p.clamp = clamp ? 1 : 0;
-  const TileCfg cfg = fuse ? make_cfg<256, 32, 4, 1, kStages, kHead, true>(p.C) : make_cfg<256, 32, 4, 1, kStages, kHead, false>(p.C);
-  if (!launch_conv(cfg, p, d.n, 1, stream, fn)) return SGN_ELAUNCH;
+  if (!fuse && (p.C == 128 || p.C == 256)) {
+    // The dedicated head kernel: one workgroup per (sample, row, 64 columns).
+    const int wblocks = (p.W + 16 * kHeadSeg - 1) / (16 * kHeadSeg);
+    const int64_t nb = (int64_t)d.n * p.H * wblocks;
+    if (nb >= ((int64_t)1 << 31)) {
+      set_error("%s: problem too large for one launch", fn);
+      return SGN_ELAUNCH;
+    }
+    p.nblocks = (int)nb;
+    if (p.C == 128)
+      head_kernel<1><<<dim3((unsigned)nb), 256, 0, stream>>>(p, wblocks);
+    else
+      head_kernel<2><<<dim3((unsigned)nb), 256, 0, stream>>>(p, wblocks);
+    if (!launch_ok(fn)) return SGN_ELAUNCH;
+  } else {
+    const TileCfg cfg = fuse ? make_cfg<256, 32, 4, 1, kStages, kHead, true>(p.C)
+                             : make_cfg<256, 32, 4, 1, kStages, kHead, false>(p.C);
+    if (!launch_conv(cfg, p, d.n, 1, stream, fn)) return SGN_ELAUNCH;
+  }
   if (cache_out && !launch_cache_out(x, d, cache_in, fuse, cache_out, stream)) return SGN_ELAUNCH;
   return SGN_OK;
 }

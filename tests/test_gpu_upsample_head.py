@@ -65,6 +65,11 @@ def test_upsample_workload_sampled():
     (1, 2, 9, 31, 256, True, True, False, True),
     (2, 1, 5, 6, 128, True, True, True, False),
     (1, 4, 7, 9, 256, False, True, True, True),
+    # unfused, C = 128 / 256: the dedicated head kernel (ragged column blocks, long T, 1x1)
+    (1, 3, 9, 70, 256, True, True, False, False),
+    (1, 16, 6, 33, 256, False, False, False, False),
+    (2, 2, 3, 17, 128, True, False, True, False),
+    (1, 1, 1, 1, 256, True, True, False, False),
 ])
 def test_head_small(n, t, h, w, c, cache, bias, clamp, fused):
     print("case head", (n, t, h, w, c, cache, bias, clamp, fused), flush=True)
@@ -100,15 +105,21 @@ def test_head_small(n, t, h, w, c, cache, bias, clamp, fused):
 
 
 @pytest.mark.slow
-def test_head_workload_sampled():
-    """[1,16,352,624,256] -> video [1,3,16,704,1248], fused GroupNorm, sampled."""
+@pytest.mark.parametrize("fused", [True, False])
+def test_head_workload_sampled(fused):
+    """[1,16,352,624,256] -> video [1,3,16,704,1248]: GroupNorm fused into the head's operand
+    load, or gn_silu_apply then the head kernel; sampled positions, all 12 channels."""
     wl = WORKLOADS[5]
     x = wl.x(device=DEV)
     gamma, beta, wt = wl.gamma(), wl.beta(), wl.conv_weight()
-    print("case head workload", flush=True)
+    print("case head workload fused=%s" % fused, flush=True)
     st = sga.gn_silu_stats(x, wl.groups)
-    video = sga.head_conv_d2s(x, wt.to(DEV), None, None,
-                              fuse=(st, gamma.to(DEV), beta.to(DEV), wl.eps, wl.groups))
+    gn = (st, gamma.to(DEV), beta.to(DEV), wl.eps, wl.groups)
+    if fused:
+        video = sga.head_conv_d2s(x, wt.to(DEV), None, None, fuse=gn)
+    else:
+        a = sga.gn_silu_apply(x, wl.groups, st, gn[1], gn[2], wl.eps)
+        video = sga.head_conv_d2s(a, wt.to(DEV), None, None)
     torch.cuda.synchronize()
     xv = vals32(x)
     mean, var = ogn.group_stats(xv, wl.groups)
