@@ -526,34 +526,34 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_kernel(ConvParams p) {
 // The head convolution has K = 12 output channels: as an implicit GEMM every input row it
 // stages feeds only 12 (padded 16) MACs per channel, so the generic tile above spends its
 // time moving operands. This kernel keeps the operands where the reuse is instead:
-// - Weights live in registers for the whole kernel. Wave w owns channel chunks
+// - Weights live in registers for the whole kernel. Wave w of NW owns channel chunks
 //   [w CPW, (w + 1) CPW) of 32 channels and holds its 27 x CPW weight fragments (the A
 //   operand of v_mfma_f32_16x16x32_bf16: 16 output channels x 32 input channels, rows
-//   12-15 zero). The 4 waves' partial sums are added through LDS when an output frame is
-//   complete.
-// - A workgroup owns one output row h and 64 columns (4 segments of 16) for every frame,
+//   12-15 zero). The waves' partial sums are added through LDS when an output frame is
+//   complete. Eight waves (two per SIMD) with one chunk each cover C = 256.
+// - A workgroup owns one output row h and 48 columns (3 segments of 16) for every frame,
 //   and streams the input frames of P = cat(cache, x) once: frame p feeds output frames
 //   p - dt, dt = 0..2, held in a ring of 3 accumulators per segment. Output frame t is
 //   complete after input frame t + 2.
 // - Each input fragment (16 columns x 32 channels of one input row, the B operand: lane l
 //   holds column l % 16, channels 8 (l / 16) .. + 8) is loaded once and serves all 3 column
-//   taps: the dw = 0 / 2 fragments are DPP row shifts of it by one lane, with the neighbour
-//   column outside the segment supplied as the shift's "old" value. Each fragment then
-//   feeds 3 x 3 MFMAs (dw x dt).
+//   taps: the dw = 0 / 2 fragments are DPP row shifts of it by one lane, done in place over
+//   a register that already holds the neighbour columns outside the segment (loaded by
+//   the row's first and last lanes only). Each fragment then feeds 3 x 3 MFMAs (dw x dt).
 // - Loads are raw-buffer loads over the input frame: rows above or below the frame and
 //   columns outside [0, W) read zeros.
 // The epilogue adds the bias, clamps if asked, and writes the 2x2 depth-to-space video
 // (channel k = 4c + 2dy + dx) as 4-byte pairs, 64 contiguous bytes per 16 columns.
 typedef __attribute__((ext_vector_type(4))) float f32x4;
-constexpr int kHeadSeg = 4;              // 16-column segments per workgroup
+constexpr int kHeadSeg = 3;              // 16-column segments per workgroup (W = 624: 13 blocks)
 
 template <int V>
 struct IC {
   static constexpr int value = V;
 };
 
-template <int CPW>
-__global__ __launch_bounds__(256, 1) void head_kernel(ConvParams p, int wblocks) {
+template <int CPW, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void head_kernel(ConvParams p, int wblocks) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int j = lane & 15, g = lane >> 4;            // column in the segment, channel group
@@ -590,16 +590,17 @@ __global__ __launch_bounds__(256, 1) void head_kernel(ConvParams p, int wblocks)
       }
   }
 
-  // Byte offsets of this lane's main column and of its edge column (lane 0 of a row: the
-  // column before the segment; lane 15: the column after it) within a frame row, per
-  // segment; out-of-range columns read zeros.
+  // Byte offsets within a frame row of this lane's main column and of the edge columns
+  // (the column before the segment, read by lane 0 of a row; the one after it, by lane 15).
+  // Out-of-range columns get kOOB: adding a row offset (|offset| < 2^31 - frame) keeps them
+  // out of range, so no select is needed per load.
   uint32_t mo[kHeadSeg], eo[kHeadSeg];
 #pragma unroll
   for (int s = 0; s < kHeadSeg; ++s) {
-    const int wm = w0 + 16 * s + j;
-    const int we = j == 0 ? w0 + 16 * s - 1 : j == 15 ? w0 + 16 * s + 16 : wm;
-    mo[s] = wm < W ? ((uint32_t)wm * C + wave * CPW * 32 + 8 * g) * 2 : kOOB;
-    eo[s] = (we >= 0 && we < W) ? ((uint32_t)we * C + wave * CPW * 32 + 8 * g) * 2 : kOOB;
+    const int wm = w0 + 16 * s + j, we = j == 0 ? w0 + 16 * s - 1 : w0 + 16 * s + 16;
+    const uint32_t ch = (uint32_t)(wave * CPW * 32 + 8 * g);
+    mo[s] = wm < W ? ((uint32_t)wm * C + ch) * 2 : kOOB;
+    eo[s] = we >= 0 && we < W ? ((uint32_t)we * C + ch) * 2 : kOOB;
   }
 
   f32x4 acc[3][kHeadSeg];
@@ -616,16 +617,16 @@ __global__ __launch_bounds__(256, 1) void head_kernel(ConvParams p, int wblocks)
   };
   // One unit of work: input frame pf, input row h + dh - 1, channel chunk c, all segments.
   struct Unit {
-    uint4 m[kHeadSeg], e[kHeadSeg];
+    uint4 m[kHeadSeg], e[kHeadSeg];                // main; edges (lane 0: left, lane 15: right)
   };
   auto load_unit = [&](int pf, int dh, int c) {
     Unit u;
-    const Rsrc r = frame_rsrc(pf);
-    const int row = (h + dh - 1) * W * C * 2 + c * 64;   // may be negative: out of range
+    const Rsrc rs = frame_rsrc(pf);
+    const uint32_t row = (uint32_t)((h + dh - 1) * W * C * 2 + c * 64);   // may wrap: out of range
 #pragma unroll
     for (int s = 0; s < kHeadSeg; ++s) {
-      u.m[s] = load16(r, mo[s] == kOOB ? kOOB : mo[s] + (uint32_t)row, 0);
-      u.e[s] = load16(r, eo[s] == kOOB ? kOOB : eo[s] + (uint32_t)row, 0);
+      u.m[s] = load16(rs, mo[s] + row, 0);
+      u.e[s] = (j == 0 || j == 15) ? load16(rs, eo[s] + row, 0) : make_uint4(0, 0, 0, 0);
     }
     return u;
   };
@@ -670,8 +671,11 @@ __global__ __launch_bounds__(256, 1) void head_kernel(ConvParams p, int wblocks)
   // buffers, one barrier per frame), then wave w writes segment w; the slot is cleared for
   // output frame t + 3. Slots of frames before 0 only collect the taps that reach before
   // the first frame: they are cleared without a store.
-  __shared__ f32x4 red[2][4][kHeadSeg][64];
-  const float* bias = p.bias;
+  __shared__ f32x4 red[2][NW][kHeadSeg][64];
+  // The bias, staged in LDS up front: a global load in the epilogue would make its wait
+  // also wait for every prefetched input fragment.
+  __shared__ float sbias[16];
+  if (tid < 16) sbias[tid] = (p.bias && tid < 12) ? p.bias[tid] : 0.0f;
   int rb = 0;
   auto retire = [&](int t, auto S_) {
     constexpr int S = decltype(S_)::value;
@@ -685,18 +689,21 @@ __global__ __launch_bounds__(256, 1) void head_kernel(ConvParams p, int wblocks)
       red[rb][wave][s][lane] = acc[S][s];
       acc[S][s] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    __syncthreads();
-    if (t < T && g < 3) {
+    // LDS writes complete, then the barrier: not __syncthreads, whose fence would also
+    // wait for the prefetched input loads.
+    wait_lgkm0();
+    stage_barrier();
+    if (t < T && g < 3 && wave < kHeadSeg) {
       const int s = wave;
       const int col = w0 + 16 * s + j;
       if (col < W) {
         f32x4 v = red[rb][0][s][lane];
 #pragma unroll
-        for (int q = 1; q < 4; ++q) v += red[rb][q][s][lane];
+        for (int q = 1; q < NW; ++q) v += red[rb][q][s][lane];
         float o[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          o[r] = v[r] + (bias ? bias[4 * g + r] : 0.0f);
+          o[r] = v[r] + sbias[4 * g + r];
           if (p.clamp) o[r] = fminf(fmaxf(o[r], -1.0f), 1.0f);
         }
         const int64_t W2 = 2 * (int64_t)W;
@@ -708,26 +715,40 @@ __global__ __launch_bounds__(256, 1) void head_kernel(ConvParams p, int wblocks)
     rb ^= 1;
   };
 
-  // Frames of P in groups of three (frames past T + 1 read zeros and store nothing).
+  // Units in order u = (pf * 3 + dh) * CPW + c, frames of P in groups of three. The loads of
+  // unit u + 1 are in flight while unit u computes.
+  constexpr int UPF = 3 * CPW;                       // units per frame
+  // Without a cache the first two frames of P are zeros: the first group of three skips
+  // their MFMAs (a separate copy of the group, so both copies keep static registers).
+  // Frames past T + 1 read zeros and store nothing.
+  auto unit_load = [&](int u) { return load_unit(u / UPF, (u % UPF) / CPW, u % CPW); };
   const int groups3 = (T + 2 + 2) / 3;
-  for (int q = 0; q < groups3; ++q) {
-    const int pf0 = 3 * q;
+  Unit u0 = unit_load(0);
+  auto group = [&](int q, auto SKIP_) {
+    constexpr bool SKIP = decltype(SKIP_)::value != 0;
+    const int pf0 = 3 * q, ub = pf0 * UPF;
 #pragma unroll
-    for (int dh = 0; dh < 3; ++dh)
-#pragma unroll
-      for (int c = 0; c < CPW; ++c) compute_unit(load_unit(pf0, dh, c), IC<0>{}, dh, c);
-    retire(pf0 - 2, IC<1>{});
-#pragma unroll
-    for (int dh = 0; dh < 3; ++dh)
-#pragma unroll
-      for (int c = 0; c < CPW; ++c) compute_unit(load_unit(pf0 + 1, dh, c), IC<1>{}, dh, c);
-    retire(pf0 - 1, IC<2>{});
-#pragma unroll
-    for (int dh = 0; dh < 3; ++dh)
-#pragma unroll
-      for (int c = 0; c < CPW; ++c) compute_unit(load_unit(pf0 + 2, dh, c), IC<2>{}, dh, c);
-    retire(pf0, IC<0>{});
-  }
+    for (int k = 0; k < 3 * UPF; ++k) {
+      Unit u1 = unit_load(ub + k + 1);
+      const int dh = (k % UPF) / CPW, c = k % CPW;
+      if (k < UPF) {
+        if (!SKIP) compute_unit(u0, IC<0>{}, dh, c);
+      } else if (k < 2 * UPF) {
+        if (!SKIP) compute_unit(u0, IC<1>{}, dh, c);
+      } else {
+        compute_unit(u0, IC<2>{}, dh, c);
+      }
+      u0 = u1;
+      if (k == UPF - 1) retire(pf0 - 2, IC<1>{});
+      if (k == 2 * UPF - 1) retire(pf0 - 1, IC<2>{});
+      if (k == 3 * UPF - 1) retire(pf0, IC<0>{});
+    }
+  };
+  if (p.cache)
+    group(0, IC<0>{});
+  else
+    group(0, IC<1>{});
+  for (int q = 1; q < groups3; ++q) group(q, IC<0>{});
 }
 
 // ---------------------------------------------------------------- host side
@@ -1032,7 +1053,7 @@ extern "C" int head_conv_d2s(const uint16_t* x, sgn_dims d, const uint16_t* cach
   p.mper = d.t * d.h * d.w;
   p.clamp = clamp ? 1 : 0;
   if (!fuse && (p.C == 128 || p.C == 256)) {
-    // The dedicated head kernel: one workgroup per (sample, row, 64 columns).
+    // The dedicated head kernel: one workgroup per (sample, row, 48 columns).
     const int wblocks = (p.W + 16 * kHeadSeg - 1) / (16 * kHeadSeg);
     const int64_t nb = (int64_t)d.n * p.H * wblocks;
     if (nb >= ((int64_t)1 << 31)) {
@@ -1041,9 +1062,9 @@ extern "C" int head_conv_d2s(const uint16_t* x, sgn_dims d, const uint16_t* cach
     }
     p.nblocks = (int)nb;
     if (p.C == 128)
-      head_kernel<1><<<dim3((unsigned)nb), 256, 0, stream>>>(p, wblocks);
+      head_kernel<1, 4><<<dim3((unsigned)nb), 256, 0, stream>>>(p, wblocks);
     else
-      head_kernel<2><<<dim3((unsigned)nb), 256, 0, stream>>>(p, wblocks);
+      head_kernel<1, 8><<<dim3((unsigned)nb), 512, 0, stream>>>(p, wblocks);
     if (!launch_ok(fn)) return SGN_ELAUNCH;
   } else {
     const TileCfg cfg = fuse ? make_cfg<256, 32, 4, 1, kStages, kHead, true>(p.C)
