@@ -10,8 +10,11 @@ Other workloads: --config 1..5 (see synthgen/workloads.py).
 Prints ONE JSON line. ``value`` = algorithmic conv FLOPs of a step / step time
 (TFLOP/s). ``roofline`` is the conv kernel alone (HIP events on the stream it runs
 on) against the bf16 dense MFMA peak; ``gn_silu`` is gn_silu_stats + gn_silu_apply on
-the same tensor at 6 bytes/element against HBM peak; ``cpu_baseline`` is the fp64
-oracle on the host over a bounded sample (rank 0, N=1 only).
+the same tensor at 6 bytes/element against HBM peak; ``box_ceilings`` is what this GPU
+sustains for those two resources (libsgnprobe.so: bf16 MFMA with random and with
+constant operand bits, HBM streaming read and copy), with each fraction repeated
+against it; ``cpu_baseline`` is the fp64 oracle on the host over a bounded sample
+(rank 0, N=1 only).
 """
 from __future__ import annotations
 
@@ -217,6 +220,42 @@ def cpu_baseline(wl, budget_s=12.0, max_reps=8):
                       (wl.name, wl.t, reps, dt, step_s)}
 
 
+def box_ceilings(dev):
+    """Sustained bf16 MFMA (random / constant operands) and HBM read / copy rates of this GPU,
+    from the probe kernels in libsgnprobe.so (about a second in all)."""
+    import ctypes
+    path = os.path.join(ROOT, "silu_gn_amd", "libsgnprobe.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    lib.sgn_probe_mfma.argtypes = [vp, i32, i32, i32, vp]
+    lib.sgn_probe_read.argtypes = [vp, sz, vp, vp]
+    lib.sgn_probe_copy.argtypes = [vp, vp, sz, vp]
+    stream = torch.cuda.current_stream().cuda_stream
+    out = {}
+    blocks, iters = 512, 8000
+    buf = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    flops = 2.0 * 32 * 32 * 16 * 32 * 4 * blocks * iters
+    for name, rnd in (("mfma_bf16_random_TFLOP/s", 1), ("mfma_bf16_constant_TFLOP/s", 0)):
+        lib.sgn_probe_mfma(buf.data_ptr(), blocks, iters, rnd, stream)
+        ms = time_loop(lambda: lib.sgn_probe_mfma(buf.data_ptr(), blocks, iters, rnd, stream), 3)
+        out[name] = round(flops / (ms * 1e-3) / 1e12, 1)
+    nbytes = 1 << 30
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    red = torch.empty(2048 * 256 * 16, dtype=torch.uint8, device=dev)
+    lib.sgn_probe_read(src.data_ptr(), nbytes, red.data_ptr(), stream)
+    ms = time_loop(lambda: lib.sgn_probe_read(src.data_ptr(), nbytes, red.data_ptr(), stream), 10)
+    out["hbm_read_GB/s"] = round(nbytes / (ms * 1e-3) / 1e9, 1)
+    lib.sgn_probe_copy(src.data_ptr(), dst.data_ptr(), nbytes, stream)
+    ms = time_loop(lambda: lib.sgn_probe_copy(src.data_ptr(), dst.data_ptr(), nbytes, stream), 10)
+    out["hbm_copy_GB/s"] = round(2 * nbytes / (ms * 1e-3) / 1e9, 1)
+    del src, dst, red, buf
+    torch.cuda.empty_cache()
+    return out
+
+
 def read_traffic(kernel_tag):
     """HBM bytes per launch of the dominant kernel from the committed counter summary, if the
     kernel's sources are unchanged since the counters were taken (else None)."""
@@ -258,6 +297,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2, choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceilings", action="store_true", help="skip the box-ceiling probes")
     ap.add_argument("--fused", action="store_true",
                     help="apply GroupNorm+SiLU inside the conv's operand load instead of gn_silu_apply")
     ap.add_argument("--profile-pass", action="store_true",
@@ -322,6 +362,33 @@ def main():
     gn_bytes = 6.0 * x.numel()
     achieved = conv_launch_flops / (conv_ms * 1e-3) / 1e12
     gn_gbps = gn_bytes / ((stats_ms + apply_ms) * 1e-3) / 1e9
+    flushed = None
+    if x.numel() * 2 < (512 << 20):
+        # The tensor fits the 256 MB last-level cache: also time each launch after writing
+        # 512 MB elsewhere, so that it starts from HBM.
+        scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+
+        def cold(fn):
+            tot = 0.0
+            for _ in range(iters):
+                scratch.fill_(0)
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                fn()
+                b.record()
+                torch.cuda.synchronize()
+                tot += a.elapsed_time(b)
+            return tot / iters
+
+        fs = cold(lambda: sga.gn_silu_stats(x, g, gc.stats, gc.ws))
+        fa = cold(lambda: sga.gn_silu_apply(x, g, gc.stats, gc.gamma, gc.beta, wl.eps, y=yb))
+        flushed = {"stats_ms": round(fs, 4), "apply_ms": round(fa, 4),
+                   "GB/s": round(gn_bytes / ((fs + fa) * 1e-3) / 1e9, 1)}
+        del scratch
+    ceilings = None if args.no_ceilings else box_ceilings(dev)
+    head_kernel = wl.kind == "head" and not args.fused and wl.c in (128, 256)
+    kernel_tag = "%s_%s%s" % ("head_kernel" if head_kernel else "conv_kernel", wl.name,
+                              "_fused" if args.fused else "")
 
     out = {
         "metric": METRIC,
@@ -341,9 +408,9 @@ def main():
                    "parallelism": "none (1 GPU)", **info},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": read_traffic("conv_kernel_%s%s" % (wl.name, "_fused" if args.fused else "")),
-                     "kernel": "conv_kernel (%s)" % conv_name, "kernel_ms": round(conv_ms, 4),
-                     "flop_per_launch": conv_launch_flops},
+                     "traffic": read_traffic(kernel_tag),
+                     "kernel": "%s (%s)" % (kernel_tag.split("_" + wl.name)[0], conv_name),
+                     "kernel_ms": round(conv_ms, 4), "flop_per_launch": conv_launch_flops},
         "gn_silu": {"GB/s": round(gn_gbps, 1), "peak": PEAK_HBM_GBPS, "frac": round(gn_gbps / PEAK_HBM_GBPS, 4),
                     "stats_ms": round(stats_ms, 4), "apply_ms": round(apply_ms, 4),
                     "stats_GB/s": round(2.0 * x.numel() / (stats_ms * 1e-3) / 1e9, 1),
@@ -351,6 +418,17 @@ def main():
                     "bytes_per_element": 6},
         "stages_ms": {k: round(v, 4) for k, v in stages.items()},
     }
+    if flushed:
+        out["gn_silu"]["cold_cache"] = flushed
+    if ceilings:
+        out["box_ceilings"] = ceilings
+        out["roofline"]["frac_of_box_mfma_random"] = round(achieved / ceilings["mfma_bf16_random_TFLOP/s"], 4)
+        # the box's rate for this access pattern: the stats' 2 B/element at the read
+        # ceiling, the apply's 4 B/element at the copy ceiling
+        box_s = (2.0 * x.numel() / (ceilings["hbm_read_GB/s"] * 1e9) +
+                 4.0 * x.numel() / (ceilings["hbm_copy_GB/s"] * 1e9))
+        out["gn_silu"]["box_GB/s"] = round(gn_bytes / box_s / 1e9, 1)
+        out["gn_silu"]["frac_of_box"] = round(gn_gbps / (gn_bytes / box_s / 1e9), 4)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(out), flush=True)
