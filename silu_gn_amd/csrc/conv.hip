@@ -526,40 +526,50 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_kernel(ConvParams p) {
 // The head convolution has K = 12 output channels: as an implicit GEMM every input row it
 // stages feeds only 12 (padded 16) MACs per channel, so the generic tile above spends its
 // time moving operands. This kernel keeps the operands where the reuse is instead:
-// - Weights live in registers for the whole kernel. Wave w of NW owns channel chunks
-//   [w CPW, (w + 1) CPW) of 32 channels and holds its 27 x CPW weight fragments (the A
-//   operand of v_mfma_f32_16x16x32_bf16: 16 output channels x 32 input channels, rows
-//   12-15 zero). The waves' partial sums are added through LDS when an output frame is
-//   complete. Eight waves (two per SIMD) with one chunk each cover C = 256.
+// - Weights live in registers for the whole kernel. Wave w of NW owns the 32-channel chunk
+//   w and holds its 27 weight fragments (the A operand of v_mfma_f32_16x16x32_bf16: 16
+//   output channels x 32 input channels, rows 12-15 zero). The waves' partial sums are
+//   added through LDS when an output frame is complete. Eight waves (two per SIMD) cover
+//   C = 256, four cover C = 128.
 // - A workgroup owns one output row h and 48 columns (3 segments of 16) for every frame,
 //   and streams the input frames of P = cat(cache, x) once: frame p feeds output frames
 //   p - dt, dt = 0..2, held in a ring of 3 accumulators per segment. Output frame t is
 //   complete after input frame t + 2.
-// - Each input fragment (16 columns x 32 channels of one input row, the B operand: lane l
-//   holds column l % 16, channels 8 (l / 16) .. + 8) is loaded once and serves all 3 column
-//   taps: the dw = 0 / 2 fragments are DPP row shifts of it by one lane, done in place over
-//   a register that already holds the neighbour columns outside the segment (loaded by
-//   the row's first and last lanes only). Each fragment then feeds 3 x 3 MFMAs (dw x dt).
-// - Loads are raw-buffer loads over the input frame: rows above or below the frame and
-//   columns outside [0, W) read zeros.
+// - A unit of work is (input frame, input row h + dh - 1, the wave's chunk). Its 50 input
+//   columns w0 - 1 .. w0 + 48 (64-byte rows) move global -> LDS with buffer_load ... lds
+//   into the wave's own ring of kHeadRing units, two units ahead; each wave waits only for
+//   its own moves (counted vmcnt), so the ring needs no barrier.
+// - The B operand of a column tap dw is the 16-row LDS window starting at row 16 s + dw:
+//   one input row staged once serves all 3 column taps and, through the frame ring, all 3
+//   frame taps (9 MFMAs per window set). The 16-byte chunks of row r sit at chunk
+//   logical ^ ((r >> 2) & 3), which keeps any 16 consecutive rows conflict free.
+// - Raw-buffer loads over the input frame: rows above or below the frame and columns
+//   outside [0, W) read zeros; without a cache the two zero frames are skipped.
 // The epilogue adds the bias, clamps if asked, and writes the 2x2 depth-to-space video
 // (channel k = 4c + 2dy + dx) as 4-byte pairs, 64 contiguous bytes per 16 columns.
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 constexpr int kHeadSeg = 3;              // 16-column segments per workgroup (W = 624: 13 blocks)
+constexpr int kHeadRows = 64;            // LDS rows per unit (50 used: 48 columns + 2 edges)
+constexpr int kHeadRing = 3;             // units per wave in LDS
 
 template <int V>
 struct IC {
   static constexpr int value = V;
 };
 
-template <int CPW, int NW>
+template <int NW>
 __global__ __launch_bounds__(64 * NW, 1) void head_kernel(ConvParams p, int wblocks) {
+  extern __shared__ __align__(16) char smem[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int j = lane & 15, g = lane >> 4;            // column in the segment, channel group
+  const int j = lane & 15, g = lane >> 4;            // row in a 16-row window, channel group
   const int C = p.C, H = p.H, W = p.W, T = p.T;
   const int HW = H * W;
   const uint32_t frame_bytes = (uint32_t)HW * C * 2;
+  constexpr int UNIT = kHeadRows * 64;               // bytes per unit in LDS
+  char* ring = smem + wave * (kHeadRing * UNIT);
+  f32x4* red = reinterpret_cast<f32x4*>(smem + NW * kHeadRing * UNIT);   // [2][NW][seg][64]
+  float* sbias = reinterpret_cast<float*>(red + 2 * NW * kHeadSeg * 64);
 
   // Workgroup -> (n, h, column block), XCD-aware: each XCD takes a contiguous run, so the
   // workgroups of neighbouring rows -- which read the same input rows -- share its L2.
@@ -574,33 +584,31 @@ __global__ __launch_bounds__(64 * NW, 1) void head_kernel(ConvParams p, int wblo
   const int n = blk / (wblocks * H);
   const int w0 = wb * (16 * kHeadSeg);
 
-  // Weight fragments: a[c][tap] for this wave's chunks.
-  bf16x8 a[CPW][27];
-  {
-    const int k = j;                                 // output channel (A row) of this lane
+  // Weight fragments of this wave's chunk, one per tap.
+  bf16x8 a[27];
 #pragma unroll
-    for (int c = 0; c < CPW; ++c)
-#pragma unroll
-      for (int tap = 0; tap < 27; ++tap) {
-        const int ch = (wave * CPW + c) * 32 + 8 * g;
-        if (k < 12)
-          a[c][tap] = *reinterpret_cast<const bf16x8*>(p.w + ((int64_t)k * 27 + tap) * C + ch);
-        else
-          a[c][tap] = bf16x8{};
-      }
+  for (int tap = 0; tap < 27; ++tap) {
+    const int ch = wave * 32 + 8 * g;
+    if (j < 12)
+      a[tap] = *reinterpret_cast<const bf16x8*>(p.w + ((int64_t)j * 27 + tap) * C + ch);
+    else
+      a[tap] = bf16x8{};
   }
+  if (tid < 16) sbias[tid] = (p.bias && tid < 12) ? p.bias[tid] : 0.0f;
 
-  // Byte offsets within a frame row of this lane's main column and of the edge columns
-  // (the column before the segment, read by lane 0 of a row; the one after it, by lane 15).
-  // Out-of-range columns get kOOB: adding a row offset (|offset| < 2^31 - frame) keeps them
-  // out of range, so no select is needed per load.
-  uint32_t mo[kHeadSeg], eo[kHeadSeg];
+  // The 4 moves of a unit: move i writes LDS rows 16 i .. 16 i + 15; lane l fills row
+  // 16 i + l / 4 (column w0 - 1 + row) at physical chunk l & 3, i.e. it loads logical chunk
+  // (l & 3) ^ ((row >> 2) & 3) = (l & 3) ^ (l >> 4). Rows past 49 and columns outside the
+  // frame get kOOB (zeros, no memory access); adding a row offset keeps them out of range.
+  uint32_t pvo[4];
+  {
+    const int lc = (lane & 3) ^ (lane >> 4);
 #pragma unroll
-  for (int s = 0; s < kHeadSeg; ++s) {
-    const int wm = w0 + 16 * s + j, we = j == 0 ? w0 + 16 * s - 1 : w0 + 16 * s + 16;
-    const uint32_t ch = (uint32_t)(wave * CPW * 32 + 8 * g);
-    mo[s] = wm < W ? ((uint32_t)wm * C + ch) * 2 : kOOB;
-    eo[s] = we >= 0 && we < W ? ((uint32_t)we * C + ch) * 2 : kOOB;
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * i + (lane >> 2), col = w0 - 1 + r;
+      pvo[i] = (r < 16 * kHeadSeg + 2 && col >= 0 && col < W)
+                   ? ((uint32_t)col * C + wave * 32 + lc * 8) * 2 : kOOB;
+    }
   }
 
   f32x4 acc[3][kHeadSeg];
@@ -609,73 +617,49 @@ __global__ __launch_bounds__(64 * NW, 1) void head_kernel(ConvParams p, int wblo
 #pragma unroll
     for (int s = 0; s < kHeadSeg; ++s) acc[r][s] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Source frame p of P = cat(cache, x): a descriptor over it (no records: zeros).
+  // Source frame pf of P = cat(cache, x): a descriptor over it (no records: zeros).
   auto frame_rsrc = [&](int pf) {
     if (pf >= 2 && pf < T + 2) return make_rsrc(p.x + ((int64_t)n * T + pf - 2) * HW * C, frame_bytes);
     if (pf < 2 && p.cache) return make_rsrc(p.cache + ((int64_t)n * 2 + pf) * HW * C, frame_bytes);
     return make_rsrc(p.x, 0);
   };
-  // One unit of work: input frame pf, input row h + dh - 1, channel chunk c, all segments.
-  struct Unit {
-    uint4 m[kHeadSeg], e[kHeadSeg];                // main; edges (lane 0: left, lane 15: right)
-  };
-  auto load_unit = [&](int pf, int dh, int c) {
-    Unit u;
+  // Units in order u = pf * 3 + dh; unit u lives in ring slot u % kHeadRing.
+  auto issue = [&](int u) {
+    const int pf = u / 3, dh = u - 3 * (u / 3);
     const Rsrc rs = frame_rsrc(pf);
-    const uint32_t row = (uint32_t)((h + dh - 1) * W * C * 2 + c * 64);   // may wrap: out of range
+    const uint32_t row = (uint32_t)((h + dh - 1) * W * C * 2);   // may wrap: out of range
+    char* dst = ring + (u % kHeadRing) * UNIT;
 #pragma unroll
-    for (int s = 0; s < kHeadSeg; ++s) {
-      u.m[s] = load16(rs, mo[s] + row, 0);
-      u.e[s] = (j == 0 || j == 15) ? load16(rs, eo[s] + row, 0) : make_uint4(0, 0, 0, 0);
-    }
-    return u;
+    for (int i = 0; i < 4; ++i) dma16(rs, pvo[i] + row, 0, dst + i * 1024);
   };
-  auto dpp_shift = [&](uint4 old, uint4 src, bool right) {
-    uint4 o;
-    if (right) {                                     // lane j takes lane j - 1 (column - 1)
-      o.x = __builtin_amdgcn_update_dpp(old.x, src.x, 0x111, 0xf, 0xf, false);
-      o.y = __builtin_amdgcn_update_dpp(old.y, src.y, 0x111, 0xf, 0xf, false);
-      o.z = __builtin_amdgcn_update_dpp(old.z, src.z, 0x111, 0xf, 0xf, false);
-      o.w = __builtin_amdgcn_update_dpp(old.w, src.w, 0x111, 0xf, 0xf, false);
-    } else {                                         // lane j takes lane j + 1 (column + 1)
-      o.x = __builtin_amdgcn_update_dpp(old.x, src.x, 0x101, 0xf, 0xf, false);
-      o.y = __builtin_amdgcn_update_dpp(old.y, src.y, 0x101, 0xf, 0xf, false);
-      o.z = __builtin_amdgcn_update_dpp(old.z, src.z, 0x101, 0xf, 0xf, false);
-      o.w = __builtin_amdgcn_update_dpp(old.w, src.w, 0x101, 0xf, 0xf, false);
-    }
-    return o;
+  const int rb0 = ((lane >> 4) ^ 0) << 4;
+  auto window = [&](const char* base, int r0) {     // rows r0 .. r0 + 15, chunk g
+    const int r = r0 + j;
+    return *reinterpret_cast<const bf16x8*>(base + r * 64 + ((g ^ ((r >> 2) & 3)) << 4));
   };
-  // Input frame pf = 3 q + U, row dh, chunk c: 3 column taps x 3 frame taps per segment into
-  // the ring slots of output frames pf - dt (slot (U - dt) mod 3).
-  auto compute_unit = [&](const Unit& u, auto U_, int dh, int c) {
+  (void)rb0;
+  // Unit of frame pf = 3 q + U, row dh: 3 column taps x 3 frame taps per segment into the
+  // ring slots of output frames pf - dt (slot (U - dt) mod 3).
+  auto compute_unit = [&](int u, auto U_, int dh) {
     constexpr int U = decltype(U_)::value;
+    const char* base = ring + (u % kHeadRing) * UNIT;
 #pragma unroll
-    for (int s = 0; s < kHeadSeg; ++s) {
-      const uint4 b1 = u.m[s];
-      const uint4 b0 = dpp_shift(u.e[s], b1, true);
-      const uint4 b2 = dpp_shift(u.e[s], b1, false);
-      const bf16x8 bb[3] = {__builtin_bit_cast(bf16x8, b0), __builtin_bit_cast(bf16x8, b1),
-                            __builtin_bit_cast(bf16x8, b2)};
+    for (int s = 0; s < kHeadSeg; ++s)
 #pragma unroll
-      for (int dw = 0; dw < 3; ++dw)
+      for (int dw = 0; dw < 3; ++dw) {
+        const bf16x8 bb = window(base, 16 * s + dw);
 #pragma unroll
         for (int dt = 0; dt < 3; ++dt) {
           const int slot = ((U - dt) % 3 + 3) % 3;
-          acc[slot][s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[c][dt * 9 + dh * 3 + dw], bb[dw],
-                                                                 acc[slot][s], 0, 0, 0);
+          acc[slot][s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[dt * 9 + dh * 3 + dw], bb, acc[slot][s], 0, 0, 0);
         }
-    }
+      }
   };
 
   // Output frame t (ring slot S) is complete: add the waves' partial sums through LDS (two
-  // buffers, one barrier per frame), then wave w writes segment w; the slot is cleared for
-  // output frame t + 3. Slots of frames before 0 only collect the taps that reach before
-  // the first frame: they are cleared without a store.
-  __shared__ f32x4 red[2][NW][kHeadSeg][64];
-  // The bias, staged in LDS up front: a global load in the epilogue would make its wait
-  // also wait for every prefetched input fragment.
-  __shared__ float sbias[16];
-  if (tid < 16) sbias[tid] = (p.bias && tid < 12) ? p.bias[tid] : 0.0f;
+  // buffers, one barrier per frame), then wave w < kHeadSeg writes segment w; the slot is
+  // cleared for output frame t + 3. Slots of frames before 0 only collect the taps that
+  // reach before the first frame: they are cleared without a store.
   int rb = 0;
   auto retire = [&](int t, auto S_) {
     constexpr int S = decltype(S_)::value;
@@ -684,22 +668,23 @@ __global__ __launch_bounds__(64 * NW, 1) void head_kernel(ConvParams p, int wblo
       for (int s = 0; s < kHeadSeg; ++s) acc[S][s] = f32x4{0.f, 0.f, 0.f, 0.f};
       return;
     }
+    f32x4* rr = red + rb * (NW * kHeadSeg * 64);
 #pragma unroll
     for (int s = 0; s < kHeadSeg; ++s) {
-      red[rb][wave][s][lane] = acc[S][s];
+      rr[(wave * kHeadSeg + s) * 64 + lane] = acc[S][s];
       acc[S][s] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     // LDS writes complete, then the barrier: not __syncthreads, whose fence would also
-    // wait for the prefetched input loads.
+    // wait for the moves in flight.
     wait_lgkm0();
     stage_barrier();
     if (t < T && g < 3 && wave < kHeadSeg) {
       const int s = wave;
       const int col = w0 + 16 * s + j;
       if (col < W) {
-        f32x4 v = red[rb][0][s][lane];
+        f32x4 v = rr[s * 64 + lane];
 #pragma unroll
-        for (int q = 1; q < NW; ++q) v += red[rb][q][s][lane];
+        for (int q = 1; q < NW; ++q) v += rr[(q * kHeadSeg + s) * 64 + lane];
         float o[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -715,33 +700,30 @@ __global__ __launch_bounds__(64 * NW, 1) void head_kernel(ConvParams p, int wblo
     rb ^= 1;
   };
 
-  // Units in order u = (pf * 3 + dh) * CPW + c, frames of P in groups of three. The loads of
-  // unit u + 1 are in flight while unit u computes.
-  constexpr int UPF = 3 * CPW;                       // units per frame
-  // Without a cache the first two frames of P are zeros: the first group of three skips
-  // their MFMAs (a separate copy of the group, so both copies keep static registers).
-  // Frames past T + 1 read zeros and store nothing.
-  auto unit_load = [&](int u) { return load_unit(u / UPF, (u % UPF) / CPW, u % CPW); };
+  // Frames in groups of three; without a cache the first group skips the two zero frames
+  // (a separate copy of the group, so both keep static registers). Frames past T + 1 read
+  // zeros and store nothing. Unit u + 2's moves are in flight while unit u computes.
   const int groups3 = (T + 2 + 2) / 3;
-  Unit u0 = unit_load(0);
+  issue(0);
+  issue(1);
   auto group = [&](int q, auto SKIP_) {
     constexpr bool SKIP = decltype(SKIP_)::value != 0;
-    const int pf0 = 3 * q, ub = pf0 * UPF;
+    const int ub = 9 * q;
 #pragma unroll
-    for (int k = 0; k < 3 * UPF; ++k) {
-      Unit u1 = unit_load(ub + k + 1);
-      const int dh = (k % UPF) / CPW, c = k % CPW;
-      if (k < UPF) {
-        if (!SKIP) compute_unit(u0, IC<0>{}, dh, c);
-      } else if (k < 2 * UPF) {
-        if (!SKIP) compute_unit(u0, IC<1>{}, dh, c);
+    for (int k = 0; k < 9; ++k) {
+      wait_vm<4>();                                  // this wave's moves of unit ub + k landed
+      const int dh = k % 3;
+      if (k < 3) {
+        if (!SKIP) compute_unit(ub + k, IC<0>{}, dh);
+      } else if (k < 6) {
+        if (!SKIP) compute_unit(ub + k, IC<1>{}, dh);
       } else {
-        compute_unit(u0, IC<2>{}, dh, c);
+        compute_unit(ub + k, IC<2>{}, dh);
       }
-      u0 = u1;
-      if (k == UPF - 1) retire(pf0 - 2, IC<1>{});
-      if (k == 2 * UPF - 1) retire(pf0 - 1, IC<2>{});
-      if (k == 3 * UPF - 1) retire(pf0, IC<0>{});
+      issue(ub + k + 2);                             // into the slot unit ub + k - 1 used
+      if (k == 2) retire(3 * q - 2, IC<1>{});
+      if (k == 5) retire(3 * q - 1, IC<2>{});
+      if (k == 8) retire(3 * q, IC<0>{});
     }
   };
   if (p.cache)
@@ -749,6 +731,7 @@ __global__ __launch_bounds__(64 * NW, 1) void head_kernel(ConvParams p, int wblo
   else
     group(0, IC<1>{});
   for (int q = 1; q < groups3; ++q) group(q, IC<0>{});
+  wait_vm<0>();
 }
 
 // ---------------------------------------------------------------- host side
@@ -1061,10 +1044,18 @@ extern "C" int head_conv_d2s(const uint16_t* x, sgn_dims d, const uint16_t* cach
       return SGN_ELAUNCH;
     }
     p.nblocks = (int)nb;
-    if (p.C == 128)
-      head_kernel<1, 4><<<dim3((unsigned)nb), 256, 0, stream>>>(p, wblocks);
+    const int nw = p.C / 32;
+    const int lds = nw * kHeadRing * kHeadRows * 64 + 2 * nw * kHeadSeg * 64 * 16 + 64;
+    const void* fn_ptr = nw == 4 ? (const void*)head_kernel<4> : (const void*)head_kernel<8>;
+    hipError_t e = hipFuncSetAttribute(fn_ptr, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e != hipSuccess) {
+      set_error("%s: cannot reserve %d bytes of LDS: %s", fn, lds, hipGetErrorString(e));
+      return SGN_ELAUNCH;
+    }
+    if (nw == 4)
+      head_kernel<4><<<dim3((unsigned)nb), 256, lds, stream>>>(p, wblocks);
     else
-      head_kernel<1, 8><<<dim3((unsigned)nb), 512, 0, stream>>>(p, wblocks);
+      head_kernel<8><<<dim3((unsigned)nb), 512, lds, stream>>>(p, wblocks);
     if (!launch_ok(fn)) return SGN_ELAUNCH;
   } else {
     const TileCfg cfg = fuse ? make_cfg<256, 32, 4, 1, kStages, kHead, true>(p.C)
