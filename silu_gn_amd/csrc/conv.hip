@@ -542,7 +542,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_kernel(ConvParams p) {
 // - The B operand of a column tap dw is the 16-row LDS window starting at row 16 s + dw:
 //   one input row staged once serves all 3 column taps and, through the frame ring, all 3
 //   frame taps (9 MFMAs per window set). The 16-byte chunks of row r sit at chunk
-//   logical ^ ((r >> 2) & 3), which keeps any 16 consecutive rows conflict free.
+//   logical ^ ((r >> 1) & 3): LDS serves a 16-byte read 8 lanes (128 bytes) at a time, and
+//   any 8 consecutive rows then hit 8 distinct bank groups, whatever the window offset.
 // - Raw-buffer loads over the input frame: rows above or below the frame and columns
 //   outside [0, W) read zeros; without a cache the two zero frames are skipped.
 // The epilogue adds the bias, clamps if asked, and writes the 2x2 depth-to-space video
@@ -598,11 +599,11 @@ __global__ __launch_bounds__(64 * NW, 1) void head_kernel(ConvParams p, int wblo
 
   // The 4 moves of a unit: move i writes LDS rows 16 i .. 16 i + 15; lane l fills row
   // 16 i + l / 4 (column w0 - 1 + row) at physical chunk l & 3, i.e. it loads logical chunk
-  // (l & 3) ^ ((row >> 2) & 3) = (l & 3) ^ (l >> 4). Rows past 49 and columns outside the
-  // frame get kOOB (zeros, no memory access); adding a row offset keeps them out of range.
+  // (l & 3) ^ ((row >> 1) & 3) = (l & 3) ^ ((l >> 3) & 3). Rows past 49 and columns outside
+  // the frame get kOOB (zeros, no memory access); adding a row offset keeps them out of range.
   uint32_t pvo[4];
   {
-    const int lc = (lane & 3) ^ (lane >> 4);
+    const int lc = (lane & 3) ^ ((lane >> 3) & 3);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 16 * i + (lane >> 2), col = w0 - 1 + r;
@@ -632,12 +633,10 @@ __global__ __launch_bounds__(64 * NW, 1) void head_kernel(ConvParams p, int wblo
 #pragma unroll
     for (int i = 0; i < 4; ++i) dma16(rs, pvo[i] + row, 0, dst + i * 1024);
   };
-  const int rb0 = ((lane >> 4) ^ 0) << 4;
   auto window = [&](const char* base, int r0) {     // rows r0 .. r0 + 15, chunk g
     const int r = r0 + j;
-    return *reinterpret_cast<const bf16x8*>(base + r * 64 + ((g ^ ((r >> 2) & 3)) << 4));
+    return *reinterpret_cast<const bf16x8*>(base + r * 64 + ((g ^ ((r >> 1) & 3)) << 4));
   };
-  (void)rb0;
   // Unit of frame pf = 3 q + U, row dh: 3 column taps x 3 frame taps per segment into the
   // ring slots of output frames pf - dt (slot (U - dt) mod 3).
   auto compute_unit = [&](int u, auto U_, int dh) {
