@@ -171,10 +171,10 @@ __global__ __launch_bounds__(256) void cache_out_kernel(
 // exactly the source frame, so a row above or below the frame falls outside it and reads
 // zeros; a row left or right of the frame gets an offset past every descriptor and reads
 // zeros too. Padding costs two VALU instructions per row and tap and no branch.
-// A stage is one tap x 32 channels, taps outer, channels inner: its BN weight rows and BM
-// position rows (64 bytes each) go to one of NS LDS stage buffers. (Channel-chunk outer
-// order halves the HBM traffic at the full-resolution shape but runs slower: the per-stage
-// tap switch costs more than the L2 misses it saves.)
+// A stage is one tap x 32 channels: its BN weight rows and BM position rows (64 bytes each)
+// go to one of NS LDS stage buffers. Stage order, causal: (frame tap dt, row tap dh), then
+// the 32-channel chunk, then the column tap dw -- the order of conv_slab_kernel, so that
+// both accumulate every output in the same sequence; phases: tap, then chunk.
 // - Weights (and, unfused, position rows) move global -> LDS with buffer_load_dwordx4 ...
 //   lds, NS-1 stages ahead, waited for with counted vmcnt.
 // - Fused GroupNorm: the position rows are loaded into VGPRs one stage ahead, activated by
@@ -188,9 +188,14 @@ __global__ __launch_bounds__(256) void cache_out_kernel(
 // The 16-byte chunks of each 64-byte row sit at physical chunk = logical ^ g(row), g(row) =
 // ((row >> 1) & 3) ^ ((row >> 3) & 1): fragment reads (32 consecutive rows, one logical
 // chunk) are conflict free for 8 and for 16 lanes per LDS cycle.
-// Per output the accumulation order is fixed -- tap, then 16 channels at a time -- and
-// independent of T, the tile and the launch: results are deterministic, and a pass split
-// along T gives the same bits.
+// Per output the accumulation order is fixed -- the stage order above, then 16 channels at
+// a time -- and independent of T, the tile and the launch: results are deterministic, and
+// a pass split along T gives the same bits.
+template <int V>
+struct IC {
+  static constexpr int value = V;
+};
+
 constexpr int kPK = 32;                  // channels per stage
 constexpr int kStages = 4;               // LDS stage buffers (a fifth measured no faster)
 constexpr int kRsrcFlags = 0x00020000;   // descriptor dword 3 (gfx9 raw buffer, 32-bit data)
@@ -232,6 +237,7 @@ template <int BM, int BN, int WGM, int WGN, int NS, int MODE, bool FUSE>
 __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_kernel(ConvParams p) {
   constexpr int NW = WGM * WGN;
   constexpr int TAPS = MODE == kPhase ? 4 : 27;
+  constexpr int INNER = MODE == kPhase ? 1 : 3;      // taps sharing a channel chunk in a row
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
   constexpr int TM = WTM / 32, TN = WTN / 32;
   static_assert(TM * 32 * WGM == BM && TN * 32 * WGN == BN, "tile shape");
@@ -334,50 +340,63 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_kernel(ConvParams p) {
   uint4 held[FUSE ? IBW : 1];
   bool hact[FUSE ? IBW : 1];                         // fused: activate (a row of x in the frame)
 
-  // Weight rows of stage s -> LDS. Stage s = tap * kpt + chunk reads channels
-  // tap * C + chunk * 32 of every row: byte offset 64 s.
+  // Stage cursors (uniform): inner tap i, channel chunk ch, tap group o; stage (o, ch, i)
+  // is tap o * INNER + i over channels ch * 32 .. ch * 32 + 31.
+  auto next_stage = [&](int& i, int& ch, int& o) {
+    if (++i == INNER) {
+      i = 0;
+      if (++ch == kpt) {
+        ch = 0;
+        ++o;
+      }
+    }
+  };
+  // Weight rows of stage s -> LDS (calls come in stage order): channels tap * C + ch * 32
+  // of every row.
+  int wi = 0, wch = 0, wo = 0;
   auto issue_w = [&](int s) {
     char* lw = smem + (s % NS) * STAGE;
-    const uint32_t soff = (uint32_t)s * (kPK * 2);
+    const uint32_t soff = ((uint32_t)(wo * INNER + wi) * C + wch * kPK) * 2;
 #pragma unroll
     for (int j = 0; j < IAW; ++j) {
       const int qi = wave + NW * j;
       if (IA % NW == 0 || qi < IA) dma16(wr, wvo[j], soff, lw + qi * 1024);
     }
+    next_stage(wi, wch, wo);
   };
   // Position rows of the cursor's stage -> LDS (unfused) or VGPRs (fused); then the cursor
   // moves to the next stage.
-  int pstage = 0, itap = 0, ichunk = 0;
+  int pstage = 0, pi = 0, pch = 0, po = 0;
   set_tap(0);
   auto issue_p = [&]() {
     char* lp = smem + (pstage % NS) * STAGE + BN * ROWB;
-    const int d = pdelta + ichunk * kPK * 2;
+    const int d = pdelta + pch * kPK * 2;
 #pragma unroll
     for (int j = 0; j < IBW; ++j) {
       const int qi = wave + NW * j;
       if (IB % NW == 0 || qi < IB) {
-        const bool okw = tdw == 0 ? wl[j] : tdw == 2 ? wrt[j] : true;
+        const bool okw = (tdw != 0 || wl[j]) && (tdw != 2 || wrt[j]);
         const uint32_t voff = okw ? pvo[j] + (uint32_t)d : kOOB;
         if (FUSE) {
           held[j] = load16(prs, voff, 0);
-          hact[j] = from_x && okw && (tdh == 0 ? hu[j] : tdh == 2 ? hd[j] : true);
+          hact[j] = from_x && okw && (tdh != 0 || hu[j]) && (tdh != 2 || hd[j]);
         } else {
           dma16(prs, voff, 0, lp + qi * 1024);
         }
       }
     }
     ++pstage;
-    if (++ichunk == kpt) {
-      ichunk = 0;
-      if (++itap < TAPS) set_tap(itap);
-    }
+    next_stage(pi, pch, po);
+    if ((INNER > 1 || pch == 0) && po < TAPS / INNER) set_tap(po * INNER + pi);
   };
   // Fused: per-channel fp64 affines of this sample, in LDS after the stage buffers; the held
-  // rows of stage s (channel chunk cchunk) are activated into its buffer.
+  // rows of stage s are activated into its buffer (calls come in stage order).
   double* tab = reinterpret_cast<double*>(smem + NS * STAGE);
+  int ci = 0, cch = 0, co = 0;
   auto commit_p = [&](int s) {
     if (!FUSE) return;
-    const int c0 = (s % kpt) * kPK + lc * 8;
+    const int c0 = cch * kPK + lc * 8;
+    next_stage(ci, cch, co);
     char* lp = smem + (s % NS) * STAGE + BN * ROWB;
     Affine a[8];
 #pragma unroll
@@ -521,6 +540,276 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_kernel(ConvParams p) {
                                      ntile * BN + wn * WTN, wm, lane, phase);
 }
 
+// ---------------------------------------------------------------- causal conv, slab form
+//
+// The unfused causal convolution for K > 128. Same tiles, stage order and accumulation
+// order as conv_kernel, but the three column taps of a (frame tap dt, row tap dh, channel
+// chunk) group share their position rows: the input rows of column tap dw for output
+// positions m0 .. m0 + BM - 1 are positions m0 + (dh - 1) W + dw - 1 + r of the source
+// frame, so one slab of BM + 2 rows starting at m0 + (dh - 1) W - 1 serves all three, tap
+// dw reading the BM-row window that starts at slab row dw. A third of conv_kernel's
+// position rows move.
+// - Padding: slab rows above or below the frame read zeros through the frame's descriptor
+//   (a negative offset wraps past it). The window row of an output in column 0 (dw = 0) or
+//   column W - 1 (dw = 2) holds the neighbour across the image-row edge; such lanes read a
+//   64-byte zero row of LDS instead (one address select per fragment, chosen per tile).
+// - Pipeline: weights as in conv_kernel (kStages stage buffers, moved 3 stages ahead).
+//   Three slab buffers: the slab of group G moves in three parts, alongside the weights of
+//   the three stages of group G - 1, i.e. while stages 3G - 6 .. 3G - 4 compute. Each
+//   iteration a wave moves its weight rows, then at most one slab row block; the counted
+//   wait before the barrier leaves exactly the previous iteration's moves in flight.
+// - Slab row r of the swizzled LDS layout keeps g(r) of conv_kernel; the window rows of a
+//   fragment are (multiple of 32) + (lane & 31) + dw, and g only reads row bits 1-3, so each
+//   (dw, 16-channel phase) has one per-lane chunk offset. Any 8 consecutive rows hit 8
+//   distinct 16-byte bank groups, whatever the window offset.
+constexpr int kSlabBufs = 3;
+
+template <int BM, int BN>
+constexpr int slab_lds_bytes() {
+  return kStages * BN * kPK * 2 + kSlabBufs * ((BM + 2 + 15) / 16) * 1024 + 64;
+}
+
+template <int BM, int BN, int WGM, int WGN>
+__global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_slab_kernel(ConvParams p) {
+  constexpr int NW = WGM * WGN, NS = kStages;
+  constexpr int WTM = BM / WGM, WTN = BN / WGN;
+  constexpr int TM = WTM / 32, TN = WTN / 32;
+  static_assert(TM * 32 * WGM == BM && TN * 32 * WGN == BN, "tile shape");
+  static_assert((NS & (NS - 1)) == 0, "stage ring");
+  constexpr int ROWB = kPK * 2;                      // bytes per LDS row
+  constexpr int WSTAGE = BN * ROWB;                  // weight rows of one stage
+  constexpr int SMOVES = (BM + 2 + 15) / 16;         // 16-row moves per slab
+  constexpr int SLAB = SMOVES * 1024;
+  constexpr int SLABS = NS * WSTAGE;                 // slab buffers follow the weight stages
+  constexpr int ZROW = SLABS + kSlabBufs * SLAB;     // 64 zero bytes
+  static_assert(ZROW + 64 == slab_lds_bytes<BM, BN>(), "LDS layout");
+  constexpr int IA = BN / 16, DW = IA / NW;          // weight moves per wave and stage
+  constexpr int SP = (SMOVES + 2) / 3;               // slab moves of parts 0 and 1
+  constexpr int SP2 = SMOVES - 2 * SP;               // ... and of part 2
+  static_assert(IA % NW == 0 && SP <= NW && SP2 >= 0, "moves per wave");
+
+  extern __shared__ __align__(16) char smem[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar branches
+
+  // Workgroup -> tile, XCD-aware as in conv_kernel. Order inside a run: N tile, tile of the
+  // frame, frame, sample.
+  int tile;
+  {
+    const int bid = blockIdx.x, nb = p.nblocks;
+    const int xcd = bid & 7, idx = bid >> 3, q = nb >> 3, r = nb & 7;
+    tile = xcd < r ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
+  }
+  const int ntile = tile % p.tiles_n;
+  tile /= p.tiles_n;
+  const int mt = tile % p.tiles_f;
+  tile /= p.tiles_f;
+  const int t = tile % p.T;
+  const int n = tile / p.T;
+
+  const int C = p.C, K = p.K, H = p.H, W = p.W, T = p.T;
+  const int HW = H * W;
+  const uint32_t frame_bytes = (uint32_t)HW * C * 2;
+  const int kpt = C / kPK;
+  const int NG = 9 * kpt;                            // groups, 3 stages each
+  const int KS = 3 * NG;
+  const int pos0 = mt * BM;
+  // This lane moves logical chunk lc of row (16 qi + (lane >> 2)); (row & 15) = lane >> 2.
+  const int lc = (lane & 3) ^ ((lane >> 3) & 3) ^ ((lane >> 5) & 1);
+
+  const Rsrc wr = make_rsrc(p.w, (uint32_t)K * 27 * C * 2);
+  uint32_t wvo[DW];
+#pragma unroll
+  for (int j = 0; j < DW; ++j) {
+    int k = ntile * BN + (wave + NW * j) * 16 + (lane >> 2);
+    if (k > K - 1) k = K - 1;                        // columns past K: computed, never stored
+    wvo[j] = ((uint32_t)k * 27 * C + lc * 8) * 2;
+  }
+  // Slab rows this lane moves in parts 0, 1, 2: slab row 16 q + lane / 4 with
+  // q = part * SP + wave, i.e. position pos0 - 1 + row (plus (dh - 1) W per group).
+  uint32_t svo[3];
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
+    const int64_t pos = (int64_t)pos0 - 1 + 16 * (k * SP + wave) + (lane >> 2);
+    svo[k] = (uint32_t)((pos * C + lc * 8) * 2);
+  }
+
+  // Weight cursor (stage order: group (dt, dh), chunk, dw) and slab cursor (group).
+  int wi = 0, wch = 0, wo = 0;
+  auto issue_w = [&](int u) {
+    char* lw = smem + (u & (NS - 1)) * WSTAGE;
+    const uint32_t soff = ((uint32_t)(wo * 3 + wi) * C + wch * kPK) * 2;
+#pragma unroll
+    for (int j = 0; j < DW; ++j) dma16(wr, wvo[j], soff, lw + (wave + NW * j) * 1024);
+    if (++wi == 3) {
+      wi = 0;
+      if (++wch == kpt) {
+        wch = 0;
+        ++wo;
+      }
+    }
+  };
+  Rsrc srs = make_rsrc(p.x, 0);
+  int sdelta = 0, gch = 0, go = 0, gbuf = 0;
+  auto issue_s = [&](auto part_c) {
+    constexpr int PART = decltype(part_c)::value;
+    if (PART == 0) {
+      const int dt = go / 3, dh = go - 3 * dt;
+      const int tf = t + dt - 2;
+      if (tf >= 0)
+        srs = make_rsrc(p.x + ((int64_t)n * T + tf) * HW * C, frame_bytes);
+      else if (p.cache)
+        srs = make_rsrc(p.cache + ((int64_t)n * 2 + tf + 2) * HW * C, frame_bytes);
+      else
+        srs = make_rsrc(p.x, 0);                     // no cache: zero frames
+      sdelta = ((dh - 1) * W * C + gch * kPK) * 2;
+    }
+    if (wave < (PART < 2 ? SP : SP2))
+      dma16(srs, svo[PART] + (uint32_t)sdelta, 0, smem + SLABS + gbuf * SLAB + (PART * SP + wave) * 1024);
+    if (PART == 2) {
+      gbuf = gbuf == kSlabBufs - 1 ? 0 : gbuf + 1;
+      if (++gch == kpt) {
+        gch = 0;
+        ++go;
+      }
+    }
+  };
+
+  // Fragment reads. A (weights): rows (multiple of 32) + (lane & 31) of the stage buffer, as
+  // in conv_kernel. B (positions): window rows (multiple of 32) + (lane & 31) + dw of the
+  // slab, or the zero row for an output at the image-row edge the tap crosses.
+  const int wm = wave % WGM, wn = wave / WGM;
+  const int gl = ((lane >> 1) & 3) ^ ((lane >> 3) & 1);
+  const int rd = (lane & 31) * ROWB;
+  const int ck0 = ((lane >> 5) ^ gl) << 4;
+  const int ck1 = ((2 + (lane >> 5)) ^ gl) << 4;
+  int bo[3][2];
+#pragma unroll
+  for (int dw = 0; dw < 3; ++dw) {
+    const int r = (lane & 31) + dw;
+    const int g = ((r >> 1) & 3) ^ ((r >> 3) & 1);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) bo[dw][kk] = r * ROWB + (((2 * kk + (lane >> 5)) ^ g) << 4);
+  }
+  bool edge_l[TM], edge_r[TM];
+#pragma unroll
+  for (int j = 0; j < TM; ++j) {
+    const int pos = pos0 + wm * WTM + 32 * j + (lane & 31);
+    const int w_ = pos % W;
+    edge_l[j] = w_ == 0;
+    edge_r[j] = w_ == W - 1;
+  }
+  auto load_frags = [&](auto dw_c, bf16x8 (&a)[TN], bf16x8 (&b)[TM], int wbuf, int sbuf, int kk) {
+    constexpr int DWV = decltype(dw_c)::value;
+    const char* abase = smem + wbuf * WSTAGE + rd + (kk ? ck1 : ck0);
+#pragma unroll
+    for (int i = 0; i < TN; ++i)
+      a[i] = *reinterpret_cast<const bf16x8*>(abase + (wn * WTN + i * 32) * ROWB);
+    const int boff = bo[DWV][kk];
+    const char* bbase = smem + SLABS + sbuf * SLAB + boff;
+#pragma unroll
+    for (int j = 0; j < TM; ++j) {
+      const char* ptr = bbase + (wm * WTM + j * 32) * ROWB;
+      if (DWV == 0 && edge_l[j]) ptr = smem + ZROW + (boff & 63);
+      if (DWV == 2 && edge_r[j]) ptr = smem + ZROW + (boff & 63);
+      b[j] = *reinterpret_cast<const bf16x8*>(ptr);
+    }
+  };
+
+  f32x16 acc[TN][TM];
+#pragma unroll
+  for (int i = 0; i < TN; ++i)
+#pragma unroll
+    for (int j = 0; j < TM; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+  auto mfmas = [&](const bf16x8 (&a)[TN], const bf16x8 (&b)[TM]) {
+#pragma unroll
+    for (int i = 0; i < TN; ++i)
+#pragma unroll
+      for (int j = 0; j < TM; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+  };
+  constexpr int NRD = TN + TM, NMF = TN * TM;
+  constexpr int PAIRS = NRD < NMF ? NRD : NMF;
+  auto interleave = [&]() {
+#pragma unroll
+    for (int r = 0; r < PAIRS; ++r) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);     // one DS read
+    }
+    if (NRD > PAIRS) __builtin_amdgcn_sched_group_barrier(0x100, NRD - PAIRS, 0);
+    if (NMF > PAIRS) __builtin_amdgcn_sched_group_barrier(0x008, NMF - PAIRS, 0);
+  };
+
+  // Prologue: slab 0, then the weights of stages 0..2 each followed by a part of slab 1.
+  // Waiting until at most 2 DW moves are in flight leaves only moves issued after the
+  // weights of stage 1 began (those of stages 1 and 2 and slab 1's parts 1 and 2): stage 0
+  // and slab 0 have landed. The zero row is written meanwhile.
+  if (tid < 4) *reinterpret_cast<uint4*>(smem + ZROW + 16 * tid) = make_uint4(0, 0, 0, 0);
+  issue_s(IC<0>{});
+  issue_s(IC<1>{});
+  issue_s(IC<2>{});
+  issue_w(0);
+  issue_s(IC<0>{});
+  issue_w(1);
+  issue_s(IC<1>{});
+  issue_w(2);
+  issue_s(IC<2>{});
+  wait_vm<2 * DW>();
+  wait_lgkm0();
+  stage_barrier();
+  bf16x8 a0[TN], b0[TM], a1[TN], b1[TM];
+  load_frags(IC<0>{}, a0, b0, 0, 0, 0);
+  int wbuf = 0, sbuf = 0;
+  // Iteration s: second phase's fragments of stage s, first-phase MFMAs; wait for the own
+  // moves of stage s + 1 (the moves of the iteration before -- weights of stage s + 2 and,
+  // if it moved one, a slab block -- may stay in flight); barrier: stage s + 1 published,
+  // stage s - 1 retired; moves of stage s + 3 (weights) and part s % 3 of slab s / 3 + 2;
+  // first phase's fragments of stage s + 1 during the second-phase MFMAs.
+  auto step = [&](auto dw_c, int s) {
+    constexpr int DWV = decltype(dw_c)::value;
+    constexpr int NXT = DWV == 2 ? 0 : DWV + 1;
+    constexpr int PREV = DWV == 0 ? 2 : DWV - 1;     // slab part moved the iteration before
+    load_frags(dw_c, a1, b1, wbuf, sbuf, 1);
+    mfmas(a0, b0);
+    interleave();
+    __builtin_amdgcn_sched_barrier(0);
+    if (s + 2 < KS) {
+      const bool moved = (s == 0 || (s - 1) / 3 + 2 < NG) && wave < (PREV < 2 ? SP : SP2);
+      if (moved)
+        wait_vm<DW + 1>();
+      else
+        wait_vm<DW>();
+    } else {
+      wait_vm<0>();
+    }
+    stage_barrier();
+    if (s + 3 < KS) issue_w(s + 3);
+    if (s / 3 + 2 < NG) issue_s(dw_c);
+    __builtin_amdgcn_sched_barrier(0);
+    wbuf = (wbuf + 1) & (NS - 1);
+    if (DWV == 2) sbuf = sbuf == kSlabBufs - 1 ? 0 : sbuf + 1;
+    load_frags(IC<NXT>{}, a0, b0, wbuf, sbuf, 0);
+    mfmas(a1, b1);
+    interleave();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  for (int g = 0; g < NG - 1; ++g) {
+    step(IC<0>{}, 3 * g);
+    step(IC<1>{}, 3 * g + 1);
+    step(IC<2>{}, 3 * g + 2);
+  }
+  step(IC<0>{}, KS - 3);
+  step(IC<1>{}, KS - 2);
+  load_frags(IC<2>{}, a1, b1, wbuf, sbuf, 1);
+  mfmas(a0, b0);
+  mfmas(a1, b1);
+
+  store_tile<kCausal, TN, TM, WTM, WTN>(acc, p, n, (int64_t)t * HW + pos0, (int64_t)(t + 1) * HW,
+                                        ntile * BN + wn * WTN, wm, lane, 0);
+}
+
 // ---------------------------------------------------------------- the output head
 //
 // The head convolution has K = 12 output channels: as an implicit GEMM every input row it
@@ -553,10 +842,6 @@ constexpr int kHeadSeg = 3;              // 16-column segments per workgroup (W 
 constexpr int kHeadRows = 64;            // LDS rows per unit (50 used: 48 columns + 2 edges)
 constexpr int kHeadRing = 3;             // units per wave in LDS
 
-template <int V>
-struct IC {
-  static constexpr int value = V;
-};
 
 template <int NW>
 __global__ __launch_bounds__(64 * NW, 1) void head_kernel(ConvParams p, int wblocks) {
@@ -755,6 +1040,17 @@ static TileCfg make_cfg(int c) {
   return t;
 }
 
+template <int BM, int BN, int WGM, int WGN>
+static TileCfg make_slab_cfg() {
+  TileCfg t;
+  t.bm = BM;
+  t.bn = BN;
+  t.fn = conv_slab_kernel<BM, BN, WGM, WGN>;
+  t.lds = slab_lds_bytes<BM, BN>();
+  t.threads = 64 * WGM * WGN;
+  return t;
+}
+
 // Candidate tiles for N-tile width bn (largest M tile first).
 template <int MODE, bool FUSE>
 static int candidates(int bn, int c, TileCfg* out) {
@@ -764,7 +1060,10 @@ static int candidates(int bn, int c, TileCfg* out) {
       // 8 waves, two per SIMD: one wave's barrier and LDS waits hide under the other's
       // MFMAs. Measured faster than 4-wave 224/192-row tiles even where those fill the
       // last round of workgroups better (latent block: 0.74 vs 0.81 ms).
-      out[n++] = make_cfg<256, 256, 2, 4, kStages, MODE, FUSE>(c);
+      if constexpr (MODE == kCausal && !FUSE)
+        out[n++] = make_slab_cfg<256, 256, 2, 4>();
+      else
+        out[n++] = make_cfg<256, 256, 2, 4, kStages, MODE, FUSE>(c);
       break;
     case 128:
       out[n++] = make_cfg<256, 128, 2, 2, kStages, MODE, FUSE>(c);
