@@ -386,9 +386,12 @@ def main():
                    "GB/s": round(gn_bytes / ((fs + fa) * 1e-3) / 1e9, 1)}
         del scratch
     ceilings = None if args.no_ceilings else box_ceilings(dev)
-    head_kernel = wl.kind == "head" and not args.fused and wl.c in (128, 256)
-    kernel_tag = "%s_%s%s" % ("head_kernel" if head_kernel else "conv_kernel", wl.name,
-                              "_fused" if args.fused else "")
+    # the kernel the dominant launch runs (the library's dispatch rules)
+    if wl.kind == "head":
+        kname = "head_kernel" if not args.fused and wl.c in (128, 256) else "conv_kernel"
+    else:
+        kname = "conv_slab_kernel" if not args.fused and wl.k > 128 else "conv_kernel"
+    kernel_tag = "%s_%s%s" % (kname, wl.name, "_fused" if args.fused else "")
 
     out = {
         "metric": METRIC,

@@ -553,40 +553,74 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_kernel(ConvParams p) {
 //   (a negative offset wraps past it). The window row of an output in column 0 (dw = 0) or
 //   column W - 1 (dw = 2) holds the neighbour across the image-row edge; such lanes read a
 //   64-byte zero row of LDS instead (one address select per fragment, chosen per tile).
-// - Pipeline: weights as in conv_kernel (kStages stage buffers, moved 3 stages ahead).
-//   Three slab buffers: the slab of group G moves in three parts, alongside the weights of
-//   the three stages of group G - 1, i.e. while stages 3G - 6 .. 3G - 4 compute. Each
-//   iteration a wave moves its weight rows, then at most one slab row block; the counted
-//   wait before the barrier leaves exactly the previous iteration's moves in flight.
+// - Pipeline: NS weight stage buffers, weights moved L = NS - 1 stages ahead. The slab of
+//   group G moves in three parts, each right after the weights of one stage of group G - 1,
+//   into one of NSL slab buffers (enough that a buffer is retired before it is refilled).
+//   "Iteration" i issues the weights of stage i + L and then one slab block per wave (a
+//   wave without a block of that part moves an out-of-range row: zeros into a dummy LDS
+//   block, no memory access), so every wave has the same moves in flight. Iterations
+//   -L .. -1 form the prologue. The wait before the barrier of iteration s lets exactly the
+//   moves issued after the weights of stage s + 1 stay in flight (vmcnt counts in issue
+//   order): a constant while every iteration has moved its slab block, counted per
+//   iteration in the last two groups.
 // - Slab row r of the swizzled LDS layout keeps g(r) of conv_kernel; the window rows of a
 //   fragment are (multiple of 32) + (lane & 31) + dw, and g only reads row bits 1-3, so each
 //   (dw, 16-channel phase) has one per-lane chunk offset. Any 8 consecutive rows hit 8
 //   distinct 16-byte bank groups, whatever the window offset.
-constexpr int kSlabBufs = 3;
+constexpr int kSlabStages = 4;           // weight stage buffers of the slab kernel
 
-template <int BM, int BN>
+__host__ __device__ constexpr int slab_bufs(int ns) { return (ns - 1 + 6 + 2) / 3; }
+
+template <int BM, int BN, int NS>
 constexpr int slab_lds_bytes() {
-  return kStages * BN * kPK * 2 + kSlabBufs * ((BM + 2 + 15) / 16) * 1024 + 64;
+  return NS * BN * kPK * 2 + slab_bufs(NS) * ((BM + 2 + 15) / 16) * 1024 + 1024 + 64;
 }
 
-template <int BM, int BN, int WGM, int WGN>
+// s_waitcnt vmcnt(n) for a wave-uniform n in [0, 15].
+__device__ __forceinline__ void wait_vm_n(int n) {
+  switch (n) {
+    case 0: wait_vm<0>(); break;
+    case 1: wait_vm<1>(); break;
+    case 2: wait_vm<2>(); break;
+    case 3: wait_vm<3>(); break;
+    case 4: wait_vm<4>(); break;
+    case 5: wait_vm<5>(); break;
+    case 6: wait_vm<6>(); break;
+    case 7: wait_vm<7>(); break;
+    case 8: wait_vm<8>(); break;
+    case 9: wait_vm<9>(); break;
+    case 10: wait_vm<10>(); break;
+    case 11: wait_vm<11>(); break;
+    case 12: wait_vm<12>(); break;
+    case 13: wait_vm<13>(); break;
+    case 14: wait_vm<14>(); break;
+    default: wait_vm<15>(); break;
+  }
+}
+
+template <int BM, int BN, int WGM, int WGN, int NS>
 __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_slab_kernel(ConvParams p) {
-  constexpr int NW = WGM * WGN, NS = kStages;
+  constexpr int NW = WGM * WGN, L = NS - 1, NSL = slab_bufs(NS);
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
   constexpr int TM = WTM / 32, TN = WTN / 32;
   static_assert(TM * 32 * WGM == BM && TN * 32 * WGN == BN, "tile shape");
-  static_assert((NS & (NS - 1)) == 0, "stage ring");
+  static_assert(NS >= 4 && 3 * NSL >= L + 6, "pipeline depth");
   constexpr int ROWB = kPK * 2;                      // bytes per LDS row
   constexpr int WSTAGE = BN * ROWB;                  // weight rows of one stage
   constexpr int SMOVES = (BM + 2 + 15) / 16;         // 16-row moves per slab
   constexpr int SLAB = SMOVES * 1024;
   constexpr int SLABS = NS * WSTAGE;                 // slab buffers follow the weight stages
-  constexpr int ZROW = SLABS + kSlabBufs * SLAB;     // 64 zero bytes
-  static_assert(ZROW + 64 == slab_lds_bytes<BM, BN>(), "LDS layout");
+  constexpr int DUMMY = SLABS + NSL * SLAB;          // 1 KB written by the dummy moves
+  constexpr int ZROW = DUMMY + 1024;                 // 64 zero bytes
+  static_assert(ZROW + 64 == slab_lds_bytes<BM, BN, NS>(), "LDS layout");
   constexpr int IA = BN / 16, DW = IA / NW;          // weight moves per wave and stage
   constexpr int SP = (SMOVES + 2) / 3;               // slab moves of parts 0 and 1
   constexpr int SP2 = SMOVES - 2 * SP;               // ... and of part 2
-  static_assert(IA % NW == 0 && SP <= NW && SP2 >= 0, "moves per wave");
+  constexpr int SPW = (SP + NW - 1) / NW;            // slab moves per wave and part
+  static_assert(IA % NW == 0 && SP2 >= 0, "moves per wave");
+  constexpr int STEADY = SPW + (L - 2) * (DW + SPW); // moves after those of stage s + 1
+  static_assert(STEADY + DW <= 15, "wait range");
+  constexpr int TAILG = (L + 5) / 3;                 // last groups, waited for exactly
 
   extern __shared__ __align__(16) char smem[];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -626,53 +660,82 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_slab_kernel(ConvParams
     wvo[j] = ((uint32_t)k * 27 * C + lc * 8) * 2;
   }
   // Slab rows this lane moves in parts 0, 1, 2: slab row 16 q + lane / 4 with
-  // q = part * SP + wave, i.e. position pos0 - 1 + row (plus (dh - 1) W per group).
-  uint32_t svo[3];
+  // q = part * SP + wave + NW * j, i.e. position pos0 - 1 + row (plus (dh - 1) W per group).
+  uint32_t svo[3][SPW];
 #pragma unroll
-  for (int k = 0; k < 3; ++k) {
-    const int64_t pos = (int64_t)pos0 - 1 + 16 * (k * SP + wave) + (lane >> 2);
-    svo[k] = (uint32_t)((pos * C + lc * 8) * 2);
-  }
+  for (int k = 0; k < 3; ++k)
+#pragma unroll
+    for (int j = 0; j < SPW; ++j) {
+      const int64_t pos = (int64_t)pos0 - 1 + 16 * (k * SP + wave + NW * j) + (lane >> 2);
+      svo[k][j] = (uint32_t)((pos * C + lc * 8) * 2);
+    }
+  // Slab moves of iteration i (i >= -L) per wave: SPW (real or dummy) while group
+  // (i + L) / 3 + 1 exists.
+  auto slab_moves = [&](int i) __attribute__((always_inline)) -> int { return (i + L) / 3 + 1 < NG ? SPW : 0; };
 
-  // Weight cursor (stage order: group (dt, dh), chunk, dw) and slab cursor (group).
-  int wi = 0, wch = 0, wo = 0;
-  auto issue_w = [&](int u) {
-    char* lw = smem + (u & (NS - 1)) * WSTAGE;
-    const uint32_t soff = ((uint32_t)(wo * 3 + wi) * C + wch * kPK) * 2;
+  // Weight cursor (stage order: group (dt, dh), chunk, dw) and slab cursor (group). Both
+  // advance by selects and the slab's frame by a select, so that the moves of a
+  // steady-state iteration are one basic block and can be scheduled between MFMAs.
+  int wi = 0, wch = 0, wo = 0, wbi = 0;
+  auto issue_w = [&]() __attribute__((always_inline)) {
+    char* lw = smem + wbi * WSTAGE;
+    const uint32_t soff = __builtin_amdgcn_readfirstlane(((wo * 3 + wi) * C + wch * kPK) * 2);
 #pragma unroll
     for (int j = 0; j < DW; ++j) dma16(wr, wvo[j], soff, lw + (wave + NW * j) * 1024);
-    if (++wi == 3) {
-      wi = 0;
-      if (++wch == kpt) {
-        wch = 0;
-        ++wo;
-      }
-    }
+    wbi = wbi == NS - 1 ? 0 : wbi + 1;
+    const bool wrap_i = wi == 2, wrap_c = wrap_i && wch == kpt - 1;
+    wi = wrap_i ? 0 : wi + 1;
+    wch = wrap_c ? 0 : (wrap_i ? wch + 1 : wch);
+    wo += wrap_c ? 1 : 0;
   };
-  Rsrc srs = make_rsrc(p.x, 0);
+  // Descriptors of the source frames of frame taps dt = 0, 1, 2: frame t + dt - 2 of x, a
+  // cache frame, or (no cache) zeros.
+  Rsrc frs0, frs1;
+  const Rsrc frs2 = make_rsrc(p.x + ((int64_t)n * T + t) * HW * C, frame_bytes);
+  if (t >= 2)
+    frs0 = make_rsrc(p.x + ((int64_t)n * T + t - 2) * HW * C, frame_bytes);
+  else if (p.cache)
+    frs0 = make_rsrc(p.cache + ((int64_t)n * 2 + t) * HW * C, frame_bytes);
+  else
+    frs0 = make_rsrc(p.x, 0);
+  if (t >= 1)
+    frs1 = make_rsrc(p.x + ((int64_t)n * T + t - 1) * HW * C, frame_bytes);
+  else if (p.cache)
+    frs1 = make_rsrc(p.cache + ((int64_t)n * 2 + t + 1) * HW * C, frame_bytes);
+  else
+    frs1 = make_rsrc(p.x, 0);
+  Rsrc srs = frs0;
   int sdelta = 0, gch = 0, go = 0, gbuf = 0;
-  auto issue_s = [&](auto part_c) {
+  auto issue_s = [&](auto part_c) __attribute__((always_inline)) {
     constexpr int PART = decltype(part_c)::value;
     if (PART == 0) {
       const int dt = go / 3, dh = go - 3 * dt;
-      const int tf = t + dt - 2;
-      if (tf >= 0)
-        srs = make_rsrc(p.x + ((int64_t)n * T + tf) * HW * C, frame_bytes);
-      else if (p.cache)
-        srs = make_rsrc(p.cache + ((int64_t)n * 2 + tf + 2) * HW * C, frame_bytes);
-      else
-        srs = make_rsrc(p.x, 0);                     // no cache: zero frames
+      const Rsrc r0 = frs0, r1 = frs1, r2 = frs2;     // values: a select of lvalues would
+      srs = dt == 0 ? r0 : dt == 1 ? r1 : r2;        // select their addresses
       sdelta = ((dh - 1) * W * C + gch * kPK) * 2;
     }
-    if (wave < (PART < 2 ? SP : SP2))
-      dma16(srs, svo[PART] + (uint32_t)sdelta, 0, smem + SLABS + gbuf * SLAB + (PART * SP + wave) * 1024);
-    if (PART == 2) {
-      gbuf = gbuf == kSlabBufs - 1 ? 0 : gbuf + 1;
-      if (++gch == kpt) {
-        gch = 0;
-        ++go;
-      }
+#pragma unroll
+    for (int j = 0; j < SPW; ++j) {
+      const int q = wave + NW * j;
+      const bool real = q < (PART < 2 ? SP : SP2);
+      dma16(srs, real ? svo[PART][j] + (uint32_t)sdelta : kOOB, 0,
+            real ? smem + SLABS + gbuf * SLAB + (PART * SP + q) * 1024 : smem + DUMMY);
     }
+    if (PART == 2) {
+      gbuf = gbuf == NSL - 1 ? 0 : gbuf + 1;
+      const bool wrap = gch == kpt - 1;
+      gch = wrap ? 0 : gch + 1;
+      go += wrap ? 1 : 0;
+    }
+  };
+  // Moves issued after the weights of stage s + 1 by the end of iteration last (>= s + 1 - L).
+  auto in_flight_after = [&](int s, int last) __attribute__((always_inline)) -> int {
+    int c = 0;
+    for (int i = s + 1 - L; i <= last; ++i) {
+      if (i > s + 1 - L && i + L < KS) c += DW;
+      c += slab_moves(i);
+    }
+    return c;
   };
 
   // Fragment reads. A (weights): rows (multiple of 32) + (lane & 31) of the stage buffer, as
@@ -699,7 +762,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_slab_kernel(ConvParams
     edge_l[j] = w_ == 0;
     edge_r[j] = w_ == W - 1;
   }
-  auto load_frags = [&](auto dw_c, bf16x8 (&a)[TN], bf16x8 (&b)[TM], int wbuf, int sbuf, int kk) {
+  auto load_frags = [&](auto dw_c, bf16x8 (&a)[TN], bf16x8 (&b)[TM], int wbuf, int sbuf,
+                        int kk) __attribute__((always_inline)) {
     constexpr int DWV = decltype(dw_c)::value;
     const char* abase = smem + wbuf * WSTAGE + rd + (kk ? ck1 : ck0);
 #pragma unroll
@@ -723,7 +787,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_slab_kernel(ConvParams
     for (int j = 0; j < TM; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-  auto mfmas = [&](const bf16x8 (&a)[TN], const bf16x8 (&b)[TM]) {
+  auto mfmas = [&](const bf16x8 (&a)[TN], const bf16x8 (&b)[TM]) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < TN; ++i)
 #pragma unroll
@@ -732,7 +796,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_slab_kernel(ConvParams
   };
   constexpr int NRD = TN + TM, NMF = TN * TM;
   constexpr int PAIRS = NRD < NMF ? NRD : NMF;
-  auto interleave = [&]() {
+  auto interleave = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int r = 0; r < PAIRS; ++r) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // one MFMA
@@ -741,67 +805,106 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_slab_kernel(ConvParams
     if (NRD > PAIRS) __builtin_amdgcn_sched_group_barrier(0x100, NRD - PAIRS, 0);
     if (NMF > PAIRS) __builtin_amdgcn_sched_group_barrier(0x008, NMF - PAIRS, 0);
   };
+  // Steady-state second phase: the iteration's moves, then the next fragments, each placed
+  // after one MFMA.
+  constexpr int NV = DW + SPW;
+  constexpr int PV = NV < NMF ? NV : NMF;
+  constexpr int RM = NMF - PV;
+  constexpr int PD = NRD < RM ? NRD : RM;
+  auto interleave_moves = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int r = 0; r < PV; ++r) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);     // one global -> LDS move
+    }
+    if (NV > PV) __builtin_amdgcn_sched_group_barrier(0x010, NV - PV, 0);
+#pragma unroll
+    for (int r = 0; r < PD; ++r) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);     // one DS read
+    }
+    if (NRD > PD) __builtin_amdgcn_sched_group_barrier(0x100, NRD - PD, 0);
+    if (RM > PD) __builtin_amdgcn_sched_group_barrier(0x008, RM - PD, 0);
+  };
 
-  // Prologue: slab 0, then the weights of stages 0..2 each followed by a part of slab 1.
-  // Waiting until at most 2 DW moves are in flight leaves only moves issued after the
-  // weights of stage 1 began (those of stages 1 and 2 and slab 1's parts 1 and 2): stage 0
-  // and slab 0 have landed. The zero row is written meanwhile.
+  // Prologue: slab 0, then iterations -L .. -1; once the weights of stage 0 (and so slab 0,
+  // moved before them) have landed, the zero row written meanwhile is published too.
   if (tid < 4) *reinterpret_cast<uint4*>(smem + ZROW + 16 * tid) = make_uint4(0, 0, 0, 0);
   issue_s(IC<0>{});
   issue_s(IC<1>{});
   issue_s(IC<2>{});
-  issue_w(0);
+  // Iteration i's moves: weights of stage i + L, then part (i + L) % 3 of its slab.
+  issue_w();
   issue_s(IC<0>{});
-  issue_w(1);
+  issue_w();
   issue_s(IC<1>{});
-  issue_w(2);
+  issue_w();
   issue_s(IC<2>{});
-  wait_vm<2 * DW>();
+  if constexpr (L > 3) {
+    issue_w();
+    issue_s(IC<0>{});
+  }
+  if constexpr (L > 4) {
+    issue_w();
+    issue_s(IC<1>{});
+  }
+  static_assert(L <= 5, "prologue");
+  wait_vm_n(in_flight_after(-1, -1));
   wait_lgkm0();
   stage_barrier();
   bf16x8 a0[TN], b0[TM], a1[TN], b1[TM];
   load_frags(IC<0>{}, a0, b0, 0, 0, 0);
   int wbuf = 0, sbuf = 0;
   // Iteration s: second phase's fragments of stage s, first-phase MFMAs; wait for the own
-  // moves of stage s + 1 (the moves of the iteration before -- weights of stage s + 2 and,
-  // if it moved one, a slab block -- may stay in flight); barrier: stage s + 1 published,
-  // stage s - 1 retired; moves of stage s + 3 (weights) and part s % 3 of slab s / 3 + 2;
-  // first phase's fragments of stage s + 1 during the second-phase MFMAs.
-  auto step = [&](auto dw_c, int s) {
+  // moves of stage s + 1; barrier: stage s + 1 published, stage s - 1 retired; the moves of
+  // iteration s; first phase's fragments of stage s + 1 during the second-phase MFMAs.
+  auto step = [&](auto dw_c, auto steady_c, int s) __attribute__((always_inline)) {
     constexpr int DWV = decltype(dw_c)::value;
     constexpr int NXT = DWV == 2 ? 0 : DWV + 1;
-    constexpr int PREV = DWV == 0 ? 2 : DWV - 1;     // slab part moved the iteration before
     load_frags(dw_c, a1, b1, wbuf, sbuf, 1);
     mfmas(a0, b0);
     interleave();
     __builtin_amdgcn_sched_barrier(0);
-    if (s + 2 < KS) {
-      const bool moved = (s == 0 || (s - 1) / 3 + 2 < NG) && wave < (PREV < 2 ? SP : SP2);
-      if (moved)
-        wait_vm<DW + 1>();
-      else
-        wait_vm<DW>();
-    } else {
-      wait_vm<0>();
-    }
+    if (decltype(steady_c)::value)
+      wait_vm<STEADY>();
+    else
+      wait_vm_n(in_flight_after(s, s - 1));
     stage_barrier();
-    if (s + 3 < KS) issue_w(s + 3);
-    if (s / 3 + 2 < NG) issue_s(dw_c);
-    __builtin_amdgcn_sched_barrier(0);
-    wbuf = (wbuf + 1) & (NS - 1);
-    if (DWV == 2) sbuf = sbuf == kSlabBufs - 1 ? 0 : sbuf + 1;
+    wbuf = wbuf == NS - 1 ? 0 : wbuf + 1;
+    if (DWV == 2) sbuf = sbuf == NSL - 1 ? 0 : sbuf + 1;
+    if constexpr (decltype(steady_c)::value) {
+      // the weights of stage s + L and a slab block both exist
+      issue_w();
+      issue_s(IC<(DWV + L) % 3>{});
+    } else {
+      if (s + L < KS) issue_w();
+      if ((s + L) / 3 + 1 < NG) issue_s(IC<(DWV + L) % 3>{});
+      __builtin_amdgcn_sched_barrier(0);
+    }
     load_frags(IC<NXT>{}, a0, b0, wbuf, sbuf, 0);
     mfmas(a1, b1);
-    interleave();
+    if constexpr (decltype(steady_c)::value)
+      interleave_moves();
+    else
+      interleave();
     __builtin_amdgcn_sched_barrier(0);
   };
-  for (int g = 0; g < NG - 1; ++g) {
-    step(IC<0>{}, 3 * g);
-    step(IC<1>{}, 3 * g + 1);
-    step(IC<2>{}, 3 * g + 2);
+  // Groups before the last TAILG (s <= KS - 3 TAILG - 1 < KS - 3 - L): iteration s and
+  // every iteration i in s + 1 - L .. s - 1 move a slab block (i + L < KS - 3) and the
+  // weights of stage i + L.
+  static_assert(3 * TAILG >= L + 3, "tail");
+  for (int g = 0; g < NG - TAILG; ++g) {
+    step(IC<0>{}, IC<1>{}, 3 * g);
+    step(IC<1>{}, IC<1>{}, 3 * g + 1);
+    step(IC<2>{}, IC<1>{}, 3 * g + 2);
   }
-  step(IC<0>{}, KS - 3);
-  step(IC<1>{}, KS - 2);
+  for (int g = NG - TAILG; g < NG - 1; ++g) {
+    step(IC<0>{}, IC<0>{}, 3 * g);
+    step(IC<1>{}, IC<0>{}, 3 * g + 1);
+    step(IC<2>{}, IC<0>{}, 3 * g + 2);
+  }
+  step(IC<0>{}, IC<0>{}, KS - 3);
+  step(IC<1>{}, IC<0>{}, KS - 2);
   load_frags(IC<2>{}, a1, b1, wbuf, sbuf, 1);
   mfmas(a0, b0);
   mfmas(a1, b1);
@@ -1045,8 +1148,8 @@ static TileCfg make_slab_cfg() {
   TileCfg t;
   t.bm = BM;
   t.bn = BN;
-  t.fn = conv_slab_kernel<BM, BN, WGM, WGN>;
-  t.lds = slab_lds_bytes<BM, BN>();
+  t.fn = conv_slab_kernel<BM, BN, WGM, WGN, kSlabStages>;
+  t.lds = slab_lds_bytes<BM, BN, kSlabStages>();
   t.threads = 64 * WGM * WGN;
   return t;
 }
@@ -1057,11 +1160,13 @@ static int candidates(int bn, int c, TileCfg* out) {
   int n = 0;
   switch (bn) {
     case 256:
-      // 8 waves, two per SIMD: one wave's barrier and LDS waits hide under the other's
-      // MFMAs. Measured faster than 4-wave 224/192-row tiles even where those fill the
-      // last round of workgroups better (latent block: 0.74 vs 0.81 ms).
+      // conv_kernel: 8 waves, two per SIMD: one wave's barrier and LDS waits hide under the
+      // other's MFMAs (measured faster than 4-wave 224/192-row tiles, latent block 0.74 vs
+      // 0.81 ms). The slab kernel: 4 waves of 128 x 128 (accumulators in AGPRs), a third
+      // fewer fragment reads per MFMA; its moves are scheduled between MFMAs, so one wave
+      // per SIMD keeps the matrix pipe fed (latent block 0.600 vs 0.632 ms with 8 waves).
       if constexpr (MODE == kCausal && !FUSE)
-        out[n++] = make_slab_cfg<256, 256, 2, 4>();
+        out[n++] = make_slab_cfg<256, 256, 2, 2>();
       else
         out[n++] = make_cfg<256, 256, 2, 4, kStages, MODE, FUSE>(c);
       break;
