@@ -1165,10 +1165,12 @@ static int candidates(int bn, int c, TileCfg* out) {
       // 0.81 ms). The slab kernel: 4 waves of 128 x 128 (accumulators in AGPRs), a third
       // fewer fragment reads per MFMA; its moves are scheduled between MFMAs, so one wave
       // per SIMD keeps the matrix pipe fed (latent block 0.600 vs 0.632 ms with 8 waves).
-      if constexpr (MODE == kCausal && !FUSE)
+      if constexpr (MODE == kCausal && !FUSE) {
         out[n++] = make_slab_cfg<256, 256, 2, 2>();
-      else
+        out[n++] = make_slab_cfg<224, 256, 1, 4>();
+      } else {
         out[n++] = make_cfg<256, 256, 2, 4, kStages, MODE, FUSE>(c);
+      }
       break;
     case 128:
       out[n++] = make_cfg<256, 128, 2, 2, kStages, MODE, FUSE>(c);
