@@ -32,6 +32,12 @@ typedef __attribute__((ext_vector_type(16))) float f32x16;
 
 constexpr int kCMax = 4096;      // largest C
 
+// An int as a type, for compile-time arguments of generic lambdas.
+template <int V>
+struct IC {
+  static constexpr int value = V;
+};
+
 enum Mode { kCausal = 0, kPhase = 1, kHead = 2 };
 
 struct ConvParams {
@@ -60,71 +66,114 @@ struct ConvParams {
 // at or past mlimit (the end of the tile's frame) are not stored.
 // bias (+ residual) in fp32, one round to bf16, stored NDHWC (causal), interleaved at
 // (2h + a, 2w + b) (phases), or unfolded 2x2 into the channels-first video (head).
+// The bias comes from LDS (lbias: the workgroup's BN entries, zeros without a bias), and
+// every residual load is issued before the first store: vmcnt counts stores as well as
+// loads, so a load issued after stores would make its use wait for those stores. A wave
+// whose whole tile lies inside the frame and K takes a path without per-lane conditions.
 template <int MODE, int TN, int TM, int WTM, int WTN>
 __device__ __forceinline__ void store_tile(const f32x16 (&acc)[TN][TM], const ConvParams& p, int n,
                                            int64_t m0, int64_t mlimit, int kbase, int wm, int lane,
-                                           int phase) {
+                                           int phase, const float* lbias) {
   const int K = p.K, H = p.H, W = p.W, T = p.T;
   const int pa = phase >> 1, pb = phase & 1;
+  auto body = [&](auto full_c) __attribute__((always_inline)) {
+    constexpr bool FULL = decltype(full_c)::value;
+    uint2 rv[MODE == kCausal ? TM : 1][TN][4];
+    if (MODE == kCausal && p.res) {
 #pragma unroll
-  for (int j = 0; j < TM; ++j) {
-    const int64_t m = m0 + wm * WTM + j * 32 + (lane & 31);
-    if (m >= mlimit) continue;
-    const int w_ = (int)(m % W);
-    const int64_t th = m / W;
-    const int h_ = (int)(th % H);
-    const int t_ = (int)(th / H);
+      for (int j = 0; j < TM; ++j) {
+        const int64_t m = m0 + wm * WTM + j * 32 + (lane & 31);
 #pragma unroll
-    for (int i = 0; i < TN; ++i)
+        for (int i = 0; i < TN; ++i)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int k0 = kbase + i * 32 + 8 * q + 4 * (lane >> 5);
-        if (k0 >= K) continue;
-        float v[4];
+          for (int q = 0; q < 4; ++q) {
+            const int k0 = kbase + i * 32 + 8 * q + 4 * (lane >> 5);
+            const uint2* src = reinterpret_cast<const uint2*>(p.res + ((int64_t)n * p.mper + m) * K + k0);
+            rv[MODE == kCausal ? j : 0][i][q] = FULL || (m < mlimit && k0 < K) ? *src : make_uint2(0, 0);
+          }
+      }
+    }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = acc[i][j][4 * q + r];
-        if (p.bias) {
-          const float4 b = *reinterpret_cast<const float4*>(p.bias + k0);
+    for (int j = 0; j < TM; ++j) {
+      const int64_t m = m0 + wm * WTM + j * 32 + (lane & 31);
+      if (!FULL && m >= mlimit) continue;
+      const int w_ = (int)(m % W);
+      const int64_t th = m / W;
+      const int h_ = (int)(th % H);
+      const int t_ = (int)(th / H);
+#pragma unroll
+      for (int i = 0; i < TN; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int kr = i * 32 + 8 * q + 4 * (lane >> 5);      // row within the wave's tile
+          const int k0 = kbase + kr;
+          if (!FULL && k0 >= K) continue;
+          const float4 b = *reinterpret_cast<const float4*>(lbias + kr);
+          float v[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v[r] = acc[i][j][4 * q + r];
           v[0] += b.x;
           v[1] += b.y;
           v[2] += b.z;
           v[3] += b.w;
-        }
-        if (MODE == kCausal) {
-          const int64_t off = ((int64_t)n * p.mper + m) * K + k0;
-          if (p.res) {
-            const uint2 rr = *reinterpret_cast<const uint2*>(p.res + off);
-            v[0] += bf16_lo(rr.x);
-            v[1] += bf16_hi(rr.x);
-            v[2] += bf16_lo(rr.y);
-            v[3] += bf16_hi(rr.y);
-          }
-          uint2 o;
-          o.x = pack_bf16x2(v[0], v[1]);
-          o.y = pack_bf16x2(v[2], v[3]);
-          *reinterpret_cast<uint2*>(p.y + off) = o;
-        } else if (MODE == kPhase) {
-          const int64_t yy = 2 * h_ + pa, xx = 2 * w_ + pb;
-          const int64_t off = ((((int64_t)n * T + t_) * (2 * H) + yy) * (2 * W) + xx) * K + k0;
-          uint2 o;
-          o.x = pack_bf16x2(v[0], v[1]);
-          o.y = pack_bf16x2(v[2], v[3]);
-          *reinterpret_cast<uint2*>(p.y + off) = o;
-        } else {
-          // K = 12: k0 = 4c, the four values are (dy, dx) = (0,0), (0,1), (1,0), (1,1).
-          if (p.clamp) {
+          if (MODE == kCausal) {
+            const int64_t off = ((int64_t)n * p.mper + m) * K + k0;
+            if (p.res) {
+              const uint2 rr = rv[MODE == kCausal ? j : 0][i][q];
+              v[0] += bf16_lo(rr.x);
+              v[1] += bf16_hi(rr.x);
+              v[2] += bf16_lo(rr.y);
+              v[3] += bf16_hi(rr.y);
+            }
+            uint2 o;
+            o.x = pack_bf16x2(v[0], v[1]);
+            o.y = pack_bf16x2(v[2], v[3]);
+            *reinterpret_cast<uint2*>(p.y + off) = o;
+          } else if (MODE == kPhase) {
+            const int64_t yy = 2 * h_ + pa, xx = 2 * w_ + pb;
+            const int64_t off = ((((int64_t)n * T + t_) * (2 * H) + yy) * (2 * W) + xx) * K + k0;
+            uint2 o;
+            o.x = pack_bf16x2(v[0], v[1]);
+            o.y = pack_bf16x2(v[2], v[3]);
+            *reinterpret_cast<uint2*>(p.y + off) = o;
+          } else {
+            // K = 12: k0 = 4c, the four values are (dy, dx) = (0,0), (0,1), (1,0), (1,1).
+            if (p.clamp) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) v[r] = fminf(fmaxf(v[r], -1.0f), 1.0f);
+              for (int r = 0; r < 4; ++r) v[r] = fminf(fmaxf(v[r], -1.0f), 1.0f);
+            }
+            const int c = k0 >> 2;
+            const int64_t W2 = 2 * (int64_t)W;
+            const int64_t base = (((int64_t)n * 3 + c) * T + t_) * (2 * (int64_t)H) * W2;
+            *reinterpret_cast<uint32_t*>(p.y + base + (2 * h_) * W2 + 2 * w_) = pack_bf16x2(v[0], v[1]);
+            *reinterpret_cast<uint32_t*>(p.y + base + (2 * h_ + 1) * W2 + 2 * w_) = pack_bf16x2(v[2], v[3]);
           }
-          const int c = k0 >> 2;
-          const int64_t W2 = 2 * (int64_t)W;
-          const int64_t base = (((int64_t)n * 3 + c) * T + t_) * (2 * (int64_t)H) * W2;
-          *reinterpret_cast<uint32_t*>(p.y + base + (2 * h_) * W2 + 2 * w_) = pack_bf16x2(v[0], v[1]);
-          *reinterpret_cast<uint32_t*>(p.y + base + (2 * h_ + 1) * W2 + 2 * w_) = pack_bf16x2(v[2], v[3]);
         }
-      }
-  }
+    }
+  };
+  const bool full = m0 + wm * WTM + TM * 32 <= mlimit && kbase + TN * 32 <= K;
+  if (full)
+    body(IC<1>{});
+  else
+    body(IC<0>{});
 }
+
+// The bias of the workgroup's BN output channels (zeros past K or without a bias) into
+// LDS: each of the first BN / 4 threads loads 16 bytes at issue_bias() and stores them at
+// commit_bias(), which must come after a wait that covers the load (the load is issued
+// before any other move, and counted waits complete moves in issue order).
+template <int BN>
+struct BiasStage {
+  float4 v;
+  __device__ __forceinline__ void issue(const ConvParams& p, int ntile, int tid) {
+    v = make_float4(0.f, 0.f, 0.f, 0.f);
+    const int k = ntile * BN + 4 * tid;
+    if (tid < BN / 4 && p.bias && k < p.K) v = *reinterpret_cast<const float4*>(p.bias + k);
+  }
+  __device__ __forceinline__ void commit(float* lbias, int tid) {
+    if (tid < BN / 4) *reinterpret_cast<float4*>(lbias + 4 * tid) = v;
+  }
+};
 
 // cache_out = the last 2 frames of P = cat(cache_in, a); frames of x are activated when
 // fused (same per-thread column layout and activate_packet as gn_silu_apply).
@@ -191,10 +240,6 @@ __global__ __launch_bounds__(256) void cache_out_kernel(
 // Per output the accumulation order is fixed -- the stage order above, then 16 channels at
 // a time -- and independent of T, the tile and the launch: results are deterministic, and
 // a pass split along T gives the same bits.
-template <int V>
-struct IC {
-  static constexpr int value = V;
-};
 
 constexpr int kPK = 32;                  // channels per stage
 constexpr int kStages = 4;               // LDS stage buffers (a fifth measured no faster)
@@ -390,8 +435,10 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_kernel(ConvParams p) {
     if ((INNER > 1 || pch == 0) && po < TAPS / INNER) set_tap(po * INNER + pi);
   };
   // Fused: per-channel fp64 affines of this sample, in LDS after the stage buffers; the held
-  // rows of stage s are activated into its buffer (calls come in stage order).
+  // rows of stage s are activated into its buffer (calls come in stage order). The bias of
+  // the tile's BN output channels follows.
   double* tab = reinterpret_cast<double*>(smem + NS * STAGE);
+  float* lbias = reinterpret_cast<float*>(smem + NS * STAGE + (FUSE ? C * 16 : 0));
   int ci = 0, cch = 0, co = 0;
   auto commit_p = [&](int s) {
     if (!FUSE) return;
@@ -468,6 +515,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_kernel(ConvParams p) {
   // Prologue: stage 0 published; the weights (unfused: and positions) of the next NS-2
   // stages in flight; fused, the position rows of stage 1 in flight to VGPRs. KS >= NS
   // always (C >= 64).
+  BiasStage<BN> bias;
+  bias.issue(p, ntile, tid);                         // before any move: the waits below cover it
   if (FUSE) {
     const int cg = C / p.groups;
     for (int c = tid; c < C; c += 64 * NW) {
@@ -479,7 +528,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_kernel(ConvParams p) {
     for (int s = 0; s < NS - 2; ++s) issue_w(s);
     issue_p();                                       // stage 0
     wait_vm<0>();
-    __syncthreads();                                 // affine table visible
+    bias.commit(lbias, tid);
+    __syncthreads();                                 // affine table and bias visible
     commit_p(0);
     issue_p();                                       // stage 1
     issue_w(NS - 2);
@@ -491,6 +541,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_kernel(ConvParams p) {
       issue_p();
     }
     wait_vm<DMIN * (NS - 2)>();
+    bias.commit(lbias, tid);
+    wait_lgkm0();
   }
   stage_barrier();
   bf16x8 a0[TN], b0[TM], a1[TN], b1[TM];
@@ -537,43 +589,59 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_kernel(ConvParams p) {
   mfmas(a1, b1);
 
   store_tile<MODE, TN, TM, WTM, WTN>(acc, p, n, (int64_t)t * HW + mt * BM, (int64_t)(t + 1) * HW,
-                                     ntile * BN + wn * WTN, wm, lane, phase);
+                                     ntile * BN + wn * WTN, wm, lane, phase, lbias + wn * WTN);
 }
 
-// ---------------------------------------------------------------- causal conv, slab form
+// ---------------------------------------------------------------- slab form
 //
-// The unfused causal convolution for K > 128. Same tiles, stage order and accumulation
-// order as conv_kernel, but the three column taps of a (frame tap dt, row tap dh, channel
-// chunk) group share their position rows: the input rows of column tap dw for output
-// positions m0 .. m0 + BM - 1 are positions m0 + (dh - 1) W + dw - 1 + r of the source
-// frame, so one slab of BM + 2 rows starting at m0 + (dh - 1) W - 1 serves all three, tap
-// dw reading the BM-row window that starts at slab row dw. A third of conv_kernel's
-// position rows move.
+// The unfused causal convolution and the upsample phases, for K > 128. Tiles and epilogue
+// as in conv_kernel. Stage order: causal, (frame tap dt, row tap dh), then the 32-channel
+// chunk, then the column tap dw (conv_kernel's order, so that both accumulate every output
+// in the same sequence); phases, row tap u, then the chunk, then the column tap v. The
+// INNER column taps of a group (3 causal, 2 per phase) read the same input rows shifted by
+// one position each: the input rows of column tap i for output positions m0 .. m0 + BM - 1
+// are positions m0 + (dh - 1) W + c0 + i + r of the source frame, c0 = -1 (causal) or
+// b - 1 (phase (a, b)), so one slab of BM + INNER - 1 rows starting at m0 + (dh - 1) W + c0
+// serves all of them, tap i reading the BM-row window that starts at slab row i. A third
+// (causal) or half (phases) of the position rows of conv_kernel move.
 // - Padding: slab rows above or below the frame read zeros through the frame's descriptor
-//   (a negative offset wraps past it). The window row of an output in column 0 (dw = 0) or
-//   column W - 1 (dw = 2) holds the neighbour across the image-row edge; such lanes read a
-//   64-byte zero row of LDS instead (one address select per fragment, chosen per tile).
+//   (a negative offset wraps past it). The window row of an output in column 0 for a tap
+//   with column offset -1, or in column W - 1 for offset +1, holds the neighbour across the
+//   image-row edge; such lanes read a 64-byte zero row of LDS instead (one address select
+//   per fragment, chosen per tile).
 // - Pipeline: NS weight stage buffers, weights moved L = NS - 1 stages ahead. The slab of
-//   group G moves in three parts, each right after the weights of one stage of group G - 1,
+//   group G moves in INNER parts, each right after the weights of one stage of group G - 1,
 //   into one of NSL slab buffers (enough that a buffer is retired before it is refilled).
-//   "Iteration" i issues the weights of stage i + L and then one slab block per wave (a
+//   "Iteration" i issues the weights of stage i + L and then SPW slab blocks per wave (a
 //   wave without a block of that part moves an out-of-range row: zeros into a dummy LDS
 //   block, no memory access), so every wave has the same moves in flight. Iterations
 //   -L .. -1 form the prologue. The wait before the barrier of iteration s lets exactly the
 //   moves issued after the weights of stage s + 1 stay in flight (vmcnt counts in issue
-//   order): a constant while every iteration has moved its slab block, counted per
-//   iteration in the last two groups.
+//   order): a constant while every iteration moves its slab blocks, counted per iteration
+//   in the last TAILG groups.
+// - A steady-state iteration is one basic block (cursors advance by selects, the frame
+//   descriptor is a select of precomputed ones), so the iteration's moves and the next
+//   stage's fragment reads are scheduled between the second phase's MFMAs: with one wave
+//   per SIMD nothing else would keep the matrix pipe busy while the wave issues them.
 // - Slab row r of the swizzled LDS layout keeps g(r) of conv_kernel; the window rows of a
-//   fragment are (multiple of 32) + (lane & 31) + dw, and g only reads row bits 1-3, so each
-//   (dw, 16-channel phase) has one per-lane chunk offset. Any 8 consecutive rows hit 8
+//   fragment are (multiple of 32) + (lane & 31) + i, and g only reads row bits 1-3, so each
+//   (i, 16-channel phase) has one per-lane chunk offset. Any 8 consecutive rows hit 8
 //   distinct 16-byte bank groups, whatever the window offset.
 constexpr int kSlabStages = 4;           // weight stage buffers of the slab kernel
 
-__host__ __device__ constexpr int slab_bufs(int ns) { return (ns - 1 + 6 + 2) / 3; }
+__host__ __device__ constexpr int slab_inner(int mode) { return mode == kPhase ? 2 : 3; }
 
-template <int BM, int BN, int NS>
+// Slab buffers: slab G starts moving L + INNER stages before stage INNER G and its buffer
+// must have been retired (after stage INNER (G - NSL) + INNER - 1): INNER NSL >= L + 2 INNER.
+__host__ __device__ constexpr int slab_bufs(int ns, int inner) {
+  return (ns - 1 + 2 * inner + inner - 1) / inner;
+}
+
+template <int BM, int BN, int NS, int MODE>
 constexpr int slab_lds_bytes() {
-  return NS * BN * kPK * 2 + slab_bufs(NS) * ((BM + 2 + 15) / 16) * 1024 + 1024 + 64;
+  return NS * BN * kPK * 2 +
+         slab_bufs(NS, slab_inner(MODE)) * ((BM + slab_inner(MODE) - 1 + 15) / 16) * 1024 + 1024 + 64 +
+         BN * 4;
 }
 
 // s_waitcnt vmcnt(n) for a wave-uniform n in [0, 15].
@@ -598,36 +666,40 @@ __device__ __forceinline__ void wait_vm_n(int n) {
   }
 }
 
-template <int BM, int BN, int WGM, int WGN, int NS>
+template <int BM, int BN, int WGM, int WGN, int NS, int MODE>
 __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_slab_kernel(ConvParams p) {
-  constexpr int NW = WGM * WGN, L = NS - 1, NSL = slab_bufs(NS);
+  static_assert(MODE == kCausal || MODE == kPhase, "slab modes");
+  constexpr int INNER = slab_inner(MODE);            // column taps per group
+  constexpr int TAPS = MODE == kPhase ? 4 : 27;
+  constexpr int NW = WGM * WGN, L = NS - 1, NSL = slab_bufs(NS, INNER);
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
   constexpr int TM = WTM / 32, TN = WTN / 32;
   static_assert(TM * 32 * WGM == BM && TN * 32 * WGN == BN, "tile shape");
-  static_assert(NS >= 4 && 3 * NSL >= L + 6, "pipeline depth");
+  static_assert(NS >= 4 && INNER * NSL >= L + 2 * INNER, "pipeline depth");
   constexpr int ROWB = kPK * 2;                      // bytes per LDS row
   constexpr int WSTAGE = BN * ROWB;                  // weight rows of one stage
-  constexpr int SMOVES = (BM + 2 + 15) / 16;         // 16-row moves per slab
+  constexpr int SMOVES = (BM + INNER - 1 + 15) / 16; // 16-row moves per slab
   constexpr int SLAB = SMOVES * 1024;
   constexpr int SLABS = NS * WSTAGE;                 // slab buffers follow the weight stages
   constexpr int DUMMY = SLABS + NSL * SLAB;          // 1 KB written by the dummy moves
   constexpr int ZROW = DUMMY + 1024;                 // 64 zero bytes
-  static_assert(ZROW + 64 == slab_lds_bytes<BM, BN, NS>(), "LDS layout");
+  constexpr int LBIAS = ZROW + 64;                   // the workgroup's BN biases
+  static_assert(LBIAS + BN * 4 == slab_lds_bytes<BM, BN, NS, MODE>(), "LDS layout");
   constexpr int IA = BN / 16, DW = IA / NW;          // weight moves per wave and stage
-  constexpr int SP = (SMOVES + 2) / 3;               // slab moves of parts 0 and 1
-  constexpr int SP2 = SMOVES - 2 * SP;               // ... and of part 2
+  constexpr int SP = (SMOVES + INNER - 1) / INNER;   // slab moves of each part but the last
+  constexpr int SPL = SMOVES - (INNER - 1) * SP;     // ... and of the last
   constexpr int SPW = (SP + NW - 1) / NW;            // slab moves per wave and part
-  static_assert(IA % NW == 0 && SP2 >= 0, "moves per wave");
+  static_assert(IA % NW == 0 && SPL >= 0, "moves per wave");
   constexpr int STEADY = SPW + (L - 2) * (DW + SPW); // moves after those of stage s + 1
   static_assert(STEADY + DW <= 15, "wait range");
-  constexpr int TAILG = (L + 5) / 3;                 // last groups, waited for exactly
+  constexpr int TAILG = (L + 2 * INNER - 1) / INNER; // last groups, waited for exactly
 
   extern __shared__ __align__(16) char smem[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar branches
 
-  // Workgroup -> tile, XCD-aware as in conv_kernel. Order inside a run: N tile, tile of the
-  // frame, frame, sample.
+  // Workgroup -> tile, XCD-aware as in conv_kernel. Order inside a run: N tile, phase, tile
+  // of the frame, frame, sample.
   int tile;
   {
     const int bid = blockIdx.x, nb = p.nblocks;
@@ -636,80 +708,93 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_slab_kernel(ConvParams
   }
   const int ntile = tile % p.tiles_n;
   tile /= p.tiles_n;
+  int phase = 0;
+  if (MODE == kPhase) {
+    phase = tile & 3;
+    tile >>= 2;
+  }
   const int mt = tile % p.tiles_f;
   tile /= p.tiles_f;
   const int t = tile % p.T;
   const int n = tile / p.T;
+  const int pa = phase >> 1, pb = phase & 1;
 
   const int C = p.C, K = p.K, H = p.H, W = p.W, T = p.T;
   const int HW = H * W;
   const uint32_t frame_bytes = (uint32_t)HW * C * 2;
   const int kpt = C / kPK;
-  const int NG = 9 * kpt;                            // groups, 3 stages each
-  const int KS = 3 * NG;
+  const int NG = (TAPS / INNER) * kpt;               // groups, INNER stages each
+  const int KS = INNER * NG;
   const int pos0 = mt * BM;
+  const int c0 = MODE == kPhase ? pb - 1 : -1;       // column offset of the slab's first row
   // This lane moves logical chunk lc of row (16 qi + (lane >> 2)); (row & 15) = lane >> 2.
   const int lc = (lane & 3) ^ ((lane >> 3) & 3) ^ ((lane >> 5) & 1);
 
-  const Rsrc wr = make_rsrc(p.w, (uint32_t)K * 27 * C * 2);
+  const Rsrc wr = make_rsrc(p.w + (MODE == kPhase ? (int64_t)phase * K * 4 * C : 0),
+                            (uint32_t)K * TAPS * C * 2);
   uint32_t wvo[DW];
 #pragma unroll
   for (int j = 0; j < DW; ++j) {
     int k = ntile * BN + (wave + NW * j) * 16 + (lane >> 2);
     if (k > K - 1) k = K - 1;                        // columns past K: computed, never stored
-    wvo[j] = ((uint32_t)k * 27 * C + lc * 8) * 2;
+    wvo[j] = ((uint32_t)k * TAPS * C + lc * 8) * 2;
   }
-  // Slab rows this lane moves in parts 0, 1, 2: slab row 16 q + lane / 4 with
-  // q = part * SP + wave + NW * j, i.e. position pos0 - 1 + row (plus (dh - 1) W per group).
-  uint32_t svo[3][SPW];
+  // Slab rows this lane moves in part k: slab row 16 q + lane / 4 with
+  // q = k * SP + wave + NW * j, i.e. position pos0 + c0 + row (plus (dh - 1) W per group).
+  uint32_t svo[INNER][SPW];
 #pragma unroll
-  for (int k = 0; k < 3; ++k)
+  for (int k = 0; k < INNER; ++k)
 #pragma unroll
     for (int j = 0; j < SPW; ++j) {
-      const int64_t pos = (int64_t)pos0 - 1 + 16 * (k * SP + wave + NW * j) + (lane >> 2);
+      const int64_t pos = (int64_t)pos0 + c0 + 16 * (k * SP + wave + NW * j) + (lane >> 2);
       svo[k][j] = (uint32_t)((pos * C + lc * 8) * 2);
     }
   // Slab moves of iteration i (i >= -L) per wave: SPW (real or dummy) while group
-  // (i + L) / 3 + 1 exists.
-  auto slab_moves = [&](int i) __attribute__((always_inline)) -> int { return (i + L) / 3 + 1 < NG ? SPW : 0; };
+  // (i + L) / INNER + 1 exists.
+  auto slab_moves = [&](int i) __attribute__((always_inline)) -> int {
+    return (i + L) / INNER + 1 < NG ? SPW : 0;
+  };
 
-  // Weight cursor (stage order: group (dt, dh), chunk, dw) and slab cursor (group). Both
-  // advance by selects and the slab's frame by a select, so that the moves of a
-  // steady-state iteration are one basic block and can be scheduled between MFMAs.
+  // Weight cursor (tap o * INNER + i, chunk ch) and slab cursor (group: tap row o, chunk).
+  // Both advance by selects.
   int wi = 0, wch = 0, wo = 0, wbi = 0;
   auto issue_w = [&]() __attribute__((always_inline)) {
     char* lw = smem + wbi * WSTAGE;
-    const uint32_t soff = __builtin_amdgcn_readfirstlane(((wo * 3 + wi) * C + wch * kPK) * 2);
+    const uint32_t soff = __builtin_amdgcn_readfirstlane(((wo * INNER + wi) * C + wch * kPK) * 2);
 #pragma unroll
     for (int j = 0; j < DW; ++j) dma16(wr, wvo[j], soff, lw + (wave + NW * j) * 1024);
     wbi = wbi == NS - 1 ? 0 : wbi + 1;
-    const bool wrap_i = wi == 2, wrap_c = wrap_i && wch == kpt - 1;
+    const bool wrap_i = wi == INNER - 1, wrap_c = wrap_i && wch == kpt - 1;
     wi = wrap_i ? 0 : wi + 1;
     wch = wrap_c ? 0 : (wrap_i ? wch + 1 : wch);
     wo += wrap_c ? 1 : 0;
   };
   // Descriptors of the source frames of frame taps dt = 0, 1, 2: frame t + dt - 2 of x, a
-  // cache frame, or (no cache) zeros.
-  Rsrc frs0, frs1;
+  // cache frame, or (no cache) zeros. The phases read frame t only.
   const Rsrc frs2 = make_rsrc(p.x + ((int64_t)n * T + t) * HW * C, frame_bytes);
-  if (t >= 2)
-    frs0 = make_rsrc(p.x + ((int64_t)n * T + t - 2) * HW * C, frame_bytes);
-  else if (p.cache)
-    frs0 = make_rsrc(p.cache + ((int64_t)n * 2 + t) * HW * C, frame_bytes);
-  else
-    frs0 = make_rsrc(p.x, 0);
-  if (t >= 1)
-    frs1 = make_rsrc(p.x + ((int64_t)n * T + t - 1) * HW * C, frame_bytes);
-  else if (p.cache)
-    frs1 = make_rsrc(p.cache + ((int64_t)n * 2 + t + 1) * HW * C, frame_bytes);
-  else
-    frs1 = make_rsrc(p.x, 0);
+  Rsrc frs0 = frs2, frs1 = frs2;
+  if (MODE == kCausal) {
+    if (t >= 2)
+      frs0 = make_rsrc(p.x + ((int64_t)n * T + t - 2) * HW * C, frame_bytes);
+    else if (p.cache)
+      frs0 = make_rsrc(p.cache + ((int64_t)n * 2 + t) * HW * C, frame_bytes);
+    else
+      frs0 = make_rsrc(p.x, 0);
+    if (t >= 1)
+      frs1 = make_rsrc(p.x + ((int64_t)n * T + t - 1) * HW * C, frame_bytes);
+    else if (p.cache)
+      frs1 = make_rsrc(p.cache + ((int64_t)n * 2 + t + 1) * HW * C, frame_bytes);
+    else
+      frs1 = make_rsrc(p.x, 0);
+  }
   Rsrc srs = frs0;
   int sdelta = 0, gch = 0, go = 0, gbuf = 0;
   auto issue_s = [&](auto part_c) __attribute__((always_inline)) {
     constexpr int PART = decltype(part_c)::value;
     if (PART == 0) {
-      const int dt = go / 3, dh = go - 3 * dt;
+      // dh: the row tap, stored + 1 (causal dh; phase u + a).
+      const int dt = MODE == kPhase ? 2 : go / 3;
+      const int dh = MODE == kPhase ? go + pa : go - 3 * dt;
       const Rsrc r0 = frs0, r1 = frs1, r2 = frs2;     // values: a select of lvalues would
       srs = dt == 0 ? r0 : dt == 1 ? r1 : r2;        // select their addresses
       sdelta = ((dh - 1) * W * C + gch * kPK) * 2;
@@ -717,11 +802,11 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_slab_kernel(ConvParams
 #pragma unroll
     for (int j = 0; j < SPW; ++j) {
       const int q = wave + NW * j;
-      const bool real = q < (PART < 2 ? SP : SP2);
+      const bool real = q < (PART < INNER - 1 ? SP : SPL);
       dma16(srs, real ? svo[PART][j] + (uint32_t)sdelta : kOOB, 0,
             real ? smem + SLABS + gbuf * SLAB + (PART * SP + q) * 1024 : smem + DUMMY);
     }
-    if (PART == 2) {
+    if (PART == INNER - 1) {
       gbuf = gbuf == NSL - 1 ? 0 : gbuf + 1;
       const bool wrap = gch == kpt - 1;
       gch = wrap ? 0 : gch + 1;
@@ -739,43 +824,45 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_slab_kernel(ConvParams
   };
 
   // Fragment reads. A (weights): rows (multiple of 32) + (lane & 31) of the stage buffer, as
-  // in conv_kernel. B (positions): window rows (multiple of 32) + (lane & 31) + dw of the
+  // in conv_kernel. B (positions): window rows (multiple of 32) + (lane & 31) + i of the
   // slab, or the zero row for an output at the image-row edge the tap crosses.
   const int wm = wave % WGM, wn = wave / WGM;
   const int gl = ((lane >> 1) & 3) ^ ((lane >> 3) & 1);
   const int rd = (lane & 31) * ROWB;
   const int ck0 = ((lane >> 5) ^ gl) << 4;
   const int ck1 = ((2 + (lane >> 5)) ^ gl) << 4;
-  int bo[3][2];
+  int bo[INNER][2];
 #pragma unroll
-  for (int dw = 0; dw < 3; ++dw) {
-    const int r = (lane & 31) + dw;
+  for (int i = 0; i < INNER; ++i) {
+    const int r = (lane & 31) + i;
     const int g = ((r >> 1) & 3) ^ ((r >> 3) & 1);
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) bo[dw][kk] = r * ROWB + (((2 * kk + (lane >> 5)) ^ g) << 4);
+    for (int kk = 0; kk < 2; ++kk) bo[i][kk] = r * ROWB + (((2 * kk + (lane >> 5)) ^ g) << 4);
   }
-  bool edge_l[TM], edge_r[TM];
+  bool edge[INNER][TM];
 #pragma unroll
   for (int j = 0; j < TM; ++j) {
     const int pos = pos0 + wm * WTM + 32 * j + (lane & 31);
     const int w_ = pos % W;
-    edge_l[j] = w_ == 0;
-    edge_r[j] = w_ == W - 1;
+#pragma unroll
+    for (int i = 0; i < INNER; ++i) {
+      const int coff = c0 + i;                       // the tap's column offset
+      edge[i][j] = (coff == -1 && w_ == 0) || (coff == 1 && w_ == W - 1);
+    }
   }
-  auto load_frags = [&](auto dw_c, bf16x8 (&a)[TN], bf16x8 (&b)[TM], int wbuf, int sbuf,
+  auto load_frags = [&](auto i_c, bf16x8 (&a)[TN], bf16x8 (&b)[TM], int wbuf, int sbuf,
                         int kk) __attribute__((always_inline)) {
-    constexpr int DWV = decltype(dw_c)::value;
+    constexpr int IV = decltype(i_c)::value;
     const char* abase = smem + wbuf * WSTAGE + rd + (kk ? ck1 : ck0);
 #pragma unroll
     for (int i = 0; i < TN; ++i)
       a[i] = *reinterpret_cast<const bf16x8*>(abase + (wn * WTN + i * 32) * ROWB);
-    const int boff = bo[DWV][kk];
+    const int boff = bo[IV][kk];
     const char* bbase = smem + SLABS + sbuf * SLAB + boff;
 #pragma unroll
     for (int j = 0; j < TM; ++j) {
       const char* ptr = bbase + (wm * WTM + j * 32) * ROWB;
-      if (DWV == 0 && edge_l[j]) ptr = smem + ZROW + (boff & 63);
-      if (DWV == 2 && edge_r[j]) ptr = smem + ZROW + (boff & 63);
+      if (edge[IV][j]) ptr = smem + ZROW + (boff & 63);
       b[j] = *reinterpret_cast<const bf16x8*>(ptr);
     }
   };
@@ -827,29 +914,33 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_slab_kernel(ConvParams
     if (RM > PD) __builtin_amdgcn_sched_group_barrier(0x008, RM - PD, 0);
   };
 
-  // Prologue: slab 0, then iterations -L .. -1; once the weights of stage 0 (and so slab 0,
-  // moved before them) have landed, the zero row written meanwhile is published too.
+  // Prologue: the bias load, slab 0, then iterations -L .. -1 (weights of stage u = i + L,
+  // part u % INNER of slab u / INNER + 1); once the weights of stage 0 (and so everything
+  // issued before them) have landed, the bias and the zero row are written to LDS and
+  // published with stage 0.
+  BiasStage<BN> bias;
+  bias.issue(p, ntile, tid);
   if (tid < 4) *reinterpret_cast<uint4*>(smem + ZROW + 16 * tid) = make_uint4(0, 0, 0, 0);
   issue_s(IC<0>{});
   issue_s(IC<1>{});
-  issue_s(IC<2>{});
-  // Iteration i's moves: weights of stage i + L, then part (i + L) % 3 of its slab.
+  if constexpr (INNER > 2) issue_s(IC<2>{});
+  static_assert(L >= 3 && L <= 5 && INNER <= 3, "prologue");
   issue_w();
-  issue_s(IC<0>{});
+  issue_s(IC<0 % INNER>{});
   issue_w();
-  issue_s(IC<1>{});
+  issue_s(IC<1 % INNER>{});
   issue_w();
-  issue_s(IC<2>{});
+  issue_s(IC<2 % INNER>{});
   if constexpr (L > 3) {
     issue_w();
-    issue_s(IC<0>{});
+    issue_s(IC<3 % INNER>{});
   }
   if constexpr (L > 4) {
     issue_w();
-    issue_s(IC<1>{});
+    issue_s(IC<4 % INNER>{});
   }
-  static_assert(L <= 5, "prologue");
   wait_vm_n(in_flight_after(-1, -1));
+  bias.commit(reinterpret_cast<float*>(smem + LBIAS), tid);
   wait_lgkm0();
   stage_barrier();
   bf16x8 a0[TN], b0[TM], a1[TN], b1[TM];
@@ -858,10 +949,10 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_slab_kernel(ConvParams
   // Iteration s: second phase's fragments of stage s, first-phase MFMAs; wait for the own
   // moves of stage s + 1; barrier: stage s + 1 published, stage s - 1 retired; the moves of
   // iteration s; first phase's fragments of stage s + 1 during the second-phase MFMAs.
-  auto step = [&](auto dw_c, auto steady_c, int s) __attribute__((always_inline)) {
-    constexpr int DWV = decltype(dw_c)::value;
-    constexpr int NXT = DWV == 2 ? 0 : DWV + 1;
-    load_frags(dw_c, a1, b1, wbuf, sbuf, 1);
+  auto step = [&](auto i_c, auto steady_c, int s) __attribute__((always_inline)) {
+    constexpr int IV = decltype(i_c)::value;
+    constexpr int NXT = IV == INNER - 1 ? 0 : IV + 1;
+    load_frags(i_c, a1, b1, wbuf, sbuf, 1);
     mfmas(a0, b0);
     interleave();
     __builtin_amdgcn_sched_barrier(0);
@@ -871,14 +962,14 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_slab_kernel(ConvParams
       wait_vm_n(in_flight_after(s, s - 1));
     stage_barrier();
     wbuf = wbuf == NS - 1 ? 0 : wbuf + 1;
-    if (DWV == 2) sbuf = sbuf == NSL - 1 ? 0 : sbuf + 1;
+    if (IV == INNER - 1) sbuf = sbuf == NSL - 1 ? 0 : sbuf + 1;
     if constexpr (decltype(steady_c)::value) {
-      // the weights of stage s + L and a slab block both exist
+      // the weights of stage s + L and the slab blocks both exist
       issue_w();
-      issue_s(IC<(DWV + L) % 3>{});
+      issue_s(IC<(IV + L) % INNER>{});
     } else {
       if (s + L < KS) issue_w();
-      if ((s + L) / 3 + 1 < NG) issue_s(IC<(DWV + L) % 3>{});
+      if ((s + L) / INNER + 1 < NG) issue_s(IC<(IV + L) % INNER>{});
       __builtin_amdgcn_sched_barrier(0);
     }
     load_frags(IC<NXT>{}, a0, b0, wbuf, sbuf, 0);
@@ -889,28 +980,28 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_slab_kernel(ConvParams
       interleave();
     __builtin_amdgcn_sched_barrier(0);
   };
-  // Groups before the last TAILG (s <= KS - 3 TAILG - 1 < KS - 3 - L): iteration s and
-  // every iteration i in s + 1 - L .. s - 1 move a slab block (i + L < KS - 3) and the
-  // weights of stage i + L.
-  static_assert(3 * TAILG >= L + 3, "tail");
+  // Groups before the last TAILG (s <= KS - INNER TAILG - 1 < KS - INNER - L): iteration s
+  // moves the weights of stage s + L and a slab part, and so did every iteration before it.
+  static_assert(INNER * TAILG >= L + INNER, "tail");
   for (int g = 0; g < NG - TAILG; ++g) {
-    step(IC<0>{}, IC<1>{}, 3 * g);
-    step(IC<1>{}, IC<1>{}, 3 * g + 1);
-    step(IC<2>{}, IC<1>{}, 3 * g + 2);
+    step(IC<0>{}, IC<1>{}, INNER * g);
+    step(IC<1>{}, IC<1>{}, INNER * g + 1);
+    if constexpr (INNER > 2) step(IC<2>{}, IC<1>{}, INNER * g + 2);
   }
   for (int g = NG - TAILG; g < NG - 1; ++g) {
-    step(IC<0>{}, IC<0>{}, 3 * g);
-    step(IC<1>{}, IC<0>{}, 3 * g + 1);
-    step(IC<2>{}, IC<0>{}, 3 * g + 2);
+    step(IC<0>{}, IC<0>{}, INNER * g);
+    step(IC<1>{}, IC<0>{}, INNER * g + 1);
+    if constexpr (INNER > 2) step(IC<2>{}, IC<0>{}, INNER * g + 2);
   }
-  step(IC<0>{}, IC<0>{}, KS - 3);
-  step(IC<1>{}, IC<0>{}, KS - 2);
-  load_frags(IC<2>{}, a1, b1, wbuf, sbuf, 1);
+  step(IC<0>{}, IC<0>{}, KS - INNER);
+  if constexpr (INNER > 2) step(IC<1>{}, IC<0>{}, KS - 2);
+  load_frags(IC<INNER - 1>{}, a1, b1, wbuf, sbuf, 1);
   mfmas(a0, b0);
   mfmas(a1, b1);
 
-  store_tile<kCausal, TN, TM, WTM, WTN>(acc, p, n, (int64_t)t * HW + pos0, (int64_t)(t + 1) * HW,
-                                        ntile * BN + wn * WTN, wm, lane, 0);
+  store_tile<MODE, TN, TM, WTM, WTN>(acc, p, n, (int64_t)t * HW + pos0, (int64_t)(t + 1) * HW,
+                                     ntile * BN + wn * WTN, wm, lane, phase,
+                                     reinterpret_cast<const float*>(smem + LBIAS) + wn * WTN);
 }
 
 // ---------------------------------------------------------------- the output head
@@ -1138,18 +1229,18 @@ static TileCfg make_cfg(int c) {
   t.bm = BM;
   t.bn = BN;
   t.fn = conv_kernel<BM, BN, WGM, WGN, NS, MODE, FUSE>;
-  t.lds = NS * (BM + BN) * kPK * 2 + (FUSE ? c * 16 : 0);
+  t.lds = NS * (BM + BN) * kPK * 2 + (FUSE ? c * 16 : 0) + BN * 4;
   t.threads = 64 * WGM * WGN;
   return t;
 }
 
-template <int BM, int BN, int WGM, int WGN>
+template <int BM, int BN, int WGM, int WGN, int MODE>
 static TileCfg make_slab_cfg() {
   TileCfg t;
   t.bm = BM;
   t.bn = BN;
-  t.fn = conv_slab_kernel<BM, BN, WGM, WGN, kSlabStages>;
-  t.lds = slab_lds_bytes<BM, BN, kSlabStages>();
+  t.fn = conv_slab_kernel<BM, BN, WGM, WGN, kSlabStages, MODE>;
+  t.lds = slab_lds_bytes<BM, BN, kSlabStages, MODE>();
   t.threads = 64 * WGM * WGN;
   return t;
 }
@@ -1165,9 +1256,9 @@ static int candidates(int bn, int c, TileCfg* out) {
       // 0.81 ms). The slab kernel: 4 waves of 128 x 128 (accumulators in AGPRs), a third
       // fewer fragment reads per MFMA; its moves are scheduled between MFMAs, so one wave
       // per SIMD keeps the matrix pipe fed (latent block 0.600 vs 0.632 ms with 8 waves).
-      if constexpr (MODE == kCausal && !FUSE) {
-        out[n++] = make_slab_cfg<256, 256, 2, 2>();
-        out[n++] = make_slab_cfg<224, 256, 1, 4>();
+      if constexpr ((MODE == kCausal || MODE == kPhase) && !FUSE) {
+        out[n++] = make_slab_cfg<256, 256, 2, 2, MODE>();
+        out[n++] = make_slab_cfg<224, 256, 1, 4, MODE>();
       } else {
         out[n++] = make_cfg<256, 256, 2, 4, kStages, MODE, FUSE>(c);
       }

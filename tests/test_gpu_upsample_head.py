@@ -30,6 +30,10 @@ DEV = "cuda"
     (1, 3, 11, 20, 128, 192, True),
     (2, 1, 9, 13, 512, 512, True),
     (1, 1, 1, 1, 64, 8, False),           # a single pixel: every tap but one is padding
+    # K > 128: the slab kernel (two column taps per slab, image-row edges from a zero row)
+    (1, 2, 1, 1, 128, 256, True),         # a single pixel
+    (1, 1, 5, 1, 256, 256, False),        # one column: both row edges in every window
+    (2, 1, 3, 40, 128, 264, True),        # K over two N tiles, the second ragged
 ])
 def test_upsample_small(n, t, h, w, c, k, bias):
     print("case upsample", (n, t, h, w, c, k, bias), flush=True)
