@@ -60,6 +60,31 @@ struct ConvParams {
 };
 
 
+constexpr int kRsrcFlags = 0x00020000;   // descriptor dword 3 (gfx9 raw buffer, 32-bit data)
+constexpr uint32_t kOOB = 0x80000000u;   // an offset past every descriptor built here
+
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+
+__device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcFlags);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+__device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// Workgroup barrier without the memory fence of __syncthreads (which would also wait for
+// every outstanding LDS move); LDS-move completion is handled by the counted waits.
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Epilogue shared by the convolution kernels. Lane l of a 32x32 accumulator tile holds
 // column m = l % 32 and rows k = 8 * (r / 4) + 4 * (l / 32) + r % 4 of element r; the
 // tile's k rows start at kbase + 32 * i, its m columns at m0 + wm * WTM + 32 * j; columns
@@ -158,6 +183,112 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[TN][TM], const Co
     body(IC<0>{});
 }
 
+// Epilogue through LDS, for the causal and phase forms: one store instruction of the direct
+// form above writes 8 bytes per lane to 64 cache lines (the 32 positions of a fragment are
+// K channels apart), and a wave's 64 of them queue behind the CU's address unit. Here each
+// wave stages fp32 (acc + bias) of 32 positions x its WTN channels in its own LDS area
+// (after a workgroup barrier: the area held operand stages), reads it back as 8 channels
+// per lane and adds the residual, loaded 16 contiguous bytes per lane before the first
+// store. A store instruction then covers 64 / (WTN / 8) positions x WTN channels: 8 lines.
+// Loads and stores go through raw-buffer descriptors over the tile's output (and residual)
+// frame, so rows past the frame read zeros and drop their stores without a branch.
+// Numerics as in store_tile: one rounding of acc + bias (+ residual). Used when K % 8 == 0,
+// so that every 16-byte access is aligned.
+// Staging layout: row r (position) of WTN * 4 bytes; the 16-byte chunk c (4 channels) sits
+// at c ^ (r & SWZ), SWZ = min(15, WTN / 4 - 1), so 8 consecutive rows at one chunk, and 8
+// chunks of one row, hit distinct bank groups.
+template <int MODE, int TN, int TM, int WTM, int WTN>
+__device__ __forceinline__ void store_tile_staged(const f32x16 (&acc)[TN][TM], const ConvParams& p, int n,
+                                                  int t, int pos0, int kbase, int wm, int lane,
+                                                  int phase, const float* lbias, char* stage) {
+  static_assert(MODE == kCausal || MODE == kPhase, "staged epilogue modes");
+  constexpr int ROW = WTN * 4;                       // staging row bytes
+  constexpr int LPR = WTN / 8;                       // lanes per row on the way out
+  constexpr int RPI = 64 / LPR;                      // rows per instruction
+  constexpr int NI = 32 / RPI;                       // instructions per 32 rows
+  static_assert(LPR * RPI == 64 && RPI * NI == 32, "staging shape");
+  constexpr int SWZ = WTN / 4 < 16 ? WTN / 4 - 1 : 15;   // chunk swizzle stays inside the row
+  const int K = p.K, H = p.H, W = p.W, T = p.T;
+  const int HW = H * W;
+  const int pa = phase >> 1, pb = phase & 1;
+  const int g = lane % LPR;                          // 8-channel group of this lane
+  const int k0 = kbase + 8 * g;
+  // The tile's frame of y: HW positions (causal) or 2H x 2W (phases), K channels each.
+  const int64_t fpos = MODE == kCausal ? (int64_t)HW : 4 * (int64_t)HW;
+  const int64_t fidx = (int64_t)n * T + t;
+  const Rsrc ys = make_rsrc(p.y + fidx * fpos * K, (uint32_t)(fpos * K * 2));
+  const bool kfull = kbase + WTN <= K;               // wave-uniform: no channel tail
+  auto out_off = [&](int ml) -> uint32_t {           // ml: position within the frame
+    if (MODE == kCausal) return (uint32_t)(((int64_t)ml * K + k0) * 2);
+    const int h_ = ml / W, w_ = ml - h_ * W;
+    return (uint32_t)(((((int64_t)(2 * h_ + pa)) * (2 * W) + 2 * w_ + pb) * K + k0) * 2);
+  };
+  // Residual of every row this lane stores, before any store.
+  u32x4 rv[MODE == kCausal ? TM : 1][MODE == kCausal ? NI : 1];
+  if (MODE == kCausal && p.res) {
+    const Rsrc rs = make_rsrc(p.res + fidx * fpos * K, (uint32_t)(fpos * K * 2));
+#pragma unroll
+    for (int j = 0; j < TM; ++j)
+#pragma unroll
+      for (int it = 0; it < NI; ++it) {
+        const int ml = pos0 + wm * WTM + 32 * j + it * RPI + lane / LPR;
+        // past the frame: zeros; past K (a tail lane): the next row's channels, never used
+        rv[MODE == kCausal ? j : 0][MODE == kCausal ? it : 0] =
+            __builtin_amdgcn_raw_buffer_load_b128(rs, out_off(ml), 0, 0);
+      }
+  }
+  stage_barrier();                                   // every wave is done with the operand stages
+#pragma unroll
+  for (int j = 0; j < TM; ++j) {
+    {
+      const int r = lane & 31;
+#pragma unroll
+      for (int i = 0; i < TN; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int kr = i * 32 + 8 * q + 4 * (lane >> 5);
+          const float4 b = *reinterpret_cast<const float4*>(lbias + kr);
+          float4 v;
+          v.x = acc[i][j][4 * q + 0] + b.x;
+          v.y = acc[i][j][4 * q + 1] + b.y;
+          v.z = acc[i][j][4 * q + 2] + b.z;
+          v.w = acc[i][j][4 * q + 3] + b.w;
+          *reinterpret_cast<float4*>(stage + r * ROW + (((kr >> 2) ^ (r & SWZ)) << 4)) = v;
+        }
+    }
+    wait_lgkm0();                                    // this wave's rows are in its area
+#pragma unroll
+    for (int it = 0; it < NI; ++it) {
+      const int r = it * RPI + lane / LPR;
+      const float4 lo = *reinterpret_cast<const float4*>(stage + r * ROW + (((2 * g) ^ (r & SWZ)) << 4));
+      const float4 hi = *reinterpret_cast<const float4*>(stage + r * ROW + (((2 * g + 1) ^ (r & SWZ)) << 4));
+      float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      if (MODE == kCausal && p.res) {
+        const u32x4 rr = rv[MODE == kCausal ? j : 0][MODE == kCausal ? it : 0];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[2 * e] += bf16_lo(rr[e]);
+          v[2 * e + 1] += bf16_hi(rr[e]);
+        }
+      }
+      u32x4 o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(v[2 * e], v[2 * e + 1]);
+      const int ml = pos0 + wm * WTM + 32 * j + r;
+      if (kfull) {
+        __builtin_amdgcn_raw_buffer_store_b128(o, ys, out_off(ml), 0, 0);   // past the frame: dropped
+      } else if (k0 < K && ml < HW) {
+        uint16_t* dst = p.y + fidx * fpos * K + out_off(ml) / 2;
+        if (k0 + 8 <= K)
+          *reinterpret_cast<uint4*>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
+        else
+          *reinterpret_cast<uint2*>(dst) = make_uint2(o[0], o[1]);
+      }
+    }
+    wait_lgkm0();                                    // reads done before the next rows land
+  }
+}
+
 // The bias of the workgroup's BN output channels (zeros past K or without a bias) into
 // LDS: each of the first BN / 4 threads loads 16 bytes at issue_bias() and stores them at
 // commit_bias(), which must come after a wait that covers the load (the load is issued
@@ -243,15 +374,7 @@ __global__ __launch_bounds__(256) void cache_out_kernel(
 
 constexpr int kPK = 32;                  // channels per stage
 constexpr int kStages = 4;               // LDS stage buffers (a fifth measured no faster)
-constexpr int kRsrcFlags = 0x00020000;   // descriptor dword 3 (gfx9 raw buffer, 32-bit data)
-constexpr uint32_t kOOB = 0x80000000u;   // an offset past every descriptor built here
 
-typedef __amdgpu_buffer_rsrc_t Rsrc;
-typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
-
-__device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcFlags);
-}
 
 // 16 bytes per lane from r at voff + soff into LDS at lds + 16 * lane (lds wave-uniform).
 __device__ __forceinline__ void dma16(Rsrc r, uint32_t voff, uint32_t soff, void* lds) {
@@ -263,20 +386,6 @@ __device__ __forceinline__ uint4 load16(Rsrc r, uint32_t voff, uint32_t soff) {
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
-__device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
-
-// Workgroup barrier without the memory fence of __syncthreads (which would also wait for
-// every outstanding LDS move); LDS-move completion is handled by the counted waits.
-__device__ __forceinline__ void stage_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
 
 template <int BM, int BN, int WGM, int WGN, int NS, int MODE, bool FUSE>
 __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_kernel(ConvParams p) {
@@ -588,8 +697,17 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_kernel(ConvParams p) {
   mfmas(a0, b0);
   mfmas(a1, b1);
 
-  store_tile<MODE, TN, TM, WTM, WTN>(acc, p, n, (int64_t)t * HW + mt * BM, (int64_t)(t + 1) * HW,
-                                     ntile * BN + wn * WTN, wm, lane, phase, lbias + wn * WTN);
+  if constexpr (MODE == kHead) {
+    store_tile<MODE, TN, TM, WTM, WTN>(acc, p, n, (int64_t)t * HW + mt * BM, (int64_t)(t + 1) * HW,
+                                       ntile * BN + wn * WTN, wm, lane, phase, lbias + wn * WTN);
+  } else if (K % 8 == 0) {                           // rows of y 16-byte aligned
+    static_assert(NW * 32 * WTN * 4 <= NS * STAGE, "epilogue staging fits the stages");
+    store_tile_staged<MODE, TN, TM, WTM, WTN>(acc, p, n, t, mt * BM, ntile * BN + wn * WTN, wm, lane, phase,
+                                              lbias + wn * WTN, smem + wave * (32 * WTN * 4));
+  } else {
+    store_tile<MODE, TN, TM, WTM, WTN>(acc, p, n, (int64_t)t * HW + mt * BM, (int64_t)(t + 1) * HW,
+                                       ntile * BN + wn * WTN, wm, lane, phase, lbias + wn * WTN);
+  }
 }
 
 // ---------------------------------------------------------------- slab form
@@ -999,9 +1117,14 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_slab_kernel(ConvParams
   mfmas(a0, b0);
   mfmas(a1, b1);
 
-  store_tile<MODE, TN, TM, WTM, WTN>(acc, p, n, (int64_t)t * HW + pos0, (int64_t)(t + 1) * HW,
-                                     ntile * BN + wn * WTN, wm, lane, phase,
-                                     reinterpret_cast<const float*>(smem + LBIAS) + wn * WTN);
+  static_assert(NW * 32 * WTN * 4 <= SLABS, "epilogue staging fits the weight stages");
+  const float* lb = reinterpret_cast<const float*>(smem + LBIAS) + wn * WTN;
+  if (K % 8 == 0)                                    // rows of y 16-byte aligned
+    store_tile_staged<MODE, TN, TM, WTM, WTN>(acc, p, n, t, pos0, ntile * BN + wn * WTN, wm, lane, phase,
+                                              lb, smem + wave * (32 * WTN * 4));
+  else
+    store_tile<MODE, TN, TM, WTM, WTN>(acc, p, n, (int64_t)t * HW + pos0, (int64_t)(t + 1) * HW,
+                                       ntile * BN + wn * WTN, wm, lane, phase, lb);
 }
 
 // ---------------------------------------------------------------- the output head
@@ -1366,6 +1489,13 @@ static bool conv_common_checks(const uint16_t* x, sgn_dims d, const uint16_t* w,
   if ((d.h + 2) * d.w * d.c * 2 >= ((int64_t)1 << 31)) {
     set_error("%s: a frame of H=%lld x W=%lld x C=%lld exceeds the 2 GiB frame limit", fn,
               (long long)d.h, (long long)d.w, (long long)d.c);
+    return false;
+  }
+  // The epilogue writes (and reads the residual) through one descriptor per output frame:
+  // H x W x K, or 2H x 2W x K for the upsample, also under 2 GiB.
+  if (4 * d.h * d.w * (int64_t)k * 2 >= ((int64_t)1 << 31)) {
+    set_error("%s: an output frame of 4 x H=%lld x W=%lld x K=%d exceeds the 2 GiB frame limit", fn,
+              (long long)d.h, (long long)d.w, k);
     return false;
   }
   return true;
