@@ -44,7 +44,9 @@ class GnConv:
     """silu(group_norm(src)) -> causal conv on the GPU, with its buffers.
 
     Unfused (default): gn_silu_stats, gn_silu_apply into ``act``, causal_conv3d on ``act``.
-    Fused: gn_silu_stats, then causal_conv3d applying the norm in its operand load."""
+    Fused: gn_silu_stats, then causal_conv3d applying the norm in its operand load.
+    ``next_gc``: the conv also emits the statistics of its output for that GnConv
+    (causal_conv3d_next_stats), which then skips its own statistics pass (``stats_ready``)."""
 
     def __init__(self, shape, k, groups, eps, gamma, beta, w, dev, fused, head=False):
         n, t, h, w_, c = shape
@@ -53,13 +55,24 @@ class GnConv:
         self.stats = torch.empty((n, groups, 2), dtype=torch.float64, device=dev)
         self.ws = torch.empty(sga.gn_silu_stats_workspace(shape, groups), dtype=torch.uint8, device=dev)
         self.act = None if fused else torch.empty(shape, dtype=torch.bfloat16, device=dev)
+        self.shape, self.k = shape, k
+        self.nws = None
+
+    def next_ws(self, producer_shape, producer_k):
+        """Workspace for a producer conv that emits this GnConv's statistics."""
+        if self.nws is None:
+            need = sga.causal_conv3d_next_stats_workspace(producer_shape, producer_k, self.g)
+            self.nws = torch.empty(max(need, 16), dtype=torch.uint8, device=self.stats.device)
+        return self.nws
 
     def fuse(self):
         return (self.stats, self.gamma, self.beta, self.eps, self.g)
 
-    def __call__(self, src, y, cache_in=None, cache_out=None, residual=None, timer=None):
-        sga.gn_silu_stats(src, self.g, self.stats, self.ws)
-        mark(timer, "gn_silu_stats")
+    def __call__(self, src, y, cache_in=None, cache_out=None, residual=None, timer=None, next_gc=None,
+                 stats_ready=False):
+        if not stats_ready:
+            sga.gn_silu_stats(src, self.g, self.stats, self.ws)
+            mark(timer, "gn_silu_stats")
         if self.fused:
             a, fuse = src, self.fuse()
         else:
@@ -69,6 +82,11 @@ class GnConv:
         if self.head:
             sga.head_conv_d2s(a, self.w, cache_in, None, fuse=fuse, video=y, cache_out=cache_out)
             mark(timer, "head_conv_d2s" + (" (fused)" if fuse else ""))
+        elif next_gc is not None:
+            sga.causal_conv3d_next_stats(a, self.w, next_gc.g, cache_in, residual=residual, fuse=fuse, y=y,
+                                         cache_out=cache_out, stats=next_gc.stats,
+                                         ws=next_gc.next_ws(self.shape, self.k))
+            mark(timer, "causal_conv3d_next_stats" + (" (fused)" if fuse else ""))
         else:
             sga.causal_conv3d(a, self.w, cache_in, residual=residual, fuse=fuse, y=y, cache_out=cache_out)
             mark(timer, "causal_conv3d" + (" (fused)" if fuse else ""))
@@ -82,7 +100,7 @@ class GnConv:
             sga.causal_conv3d(a, self.w, cache_in, residual=residual, fuse=fuse, y=y)
 
 
-def build_step(wl, dev, fused):
+def build_step(wl, dev, fused, separate_stats=False):
     """Allocate inputs for workload ``wl``; return (step, conv_only, gn_inputs, flops, info)."""
     g, eps = wl.groups, wl.eps
     gamma, beta = wl.gamma(1, dev), wl.beta(1, dev)
@@ -137,12 +155,16 @@ def build_step(wl, dev, fused):
         del xp
 
         def step(timer=None):
-            gcs[0](x, hbuf, caches[0], caches[2], timer=timer)
-            gcs[1](hbuf, y, caches[1], caches[3], residual=x, timer=timer)
+            # conv1's epilogue emits norm2's statistics: no statistics pass over h
+            nxt = None if separate_stats else gcs[1]
+            gcs[0](x, hbuf, caches[0], caches[2], timer=timer, next_gc=nxt)
+            gcs[1](hbuf, y, caches[1], caches[3], residual=x, timer=timer, stats_ready=nxt is not None)
 
         conv = conv_flops(wl.n, wl.t, wl.h, wl.w, wl.c, wl.c)
         return (step, lambda: gcs[0].conv_only(x, hbuf, caches[0]), (x, gcs[0]), 2 * conv, conv,
-                {"conv": "2 x %d->%d 3x3x3 causal" % (wl.c, wl.c)}, conv_name)
+                {"conv": "2 x %d->%d 3x3x3 causal" % (wl.c, wl.c),
+                 "norm2_statistics": "gn_silu_stats over h" if separate_stats
+                 else "from conv1's epilogue (causal_conv3d_next_stats)"}, conv_name)
     # head
     x = wl.x(dev)
     w = wl.conv_weight(1, dev)
@@ -300,6 +322,9 @@ def main():
     ap.add_argument("--no-ceilings", action="store_true", help="skip the box-ceiling probes")
     ap.add_argument("--fused", action="store_true",
                     help="apply GroupNorm+SiLU inside the conv's operand load instead of gn_silu_apply")
+    ap.add_argument("--separate-stats", action="store_true",
+                    help="full-resolution block: take norm2's statistics with gn_silu_stats over h "
+                         "instead of from conv1's epilogue")
     ap.add_argument("--profile-pass", action="store_true",
                     help="for hardware-counter runs: one warm-up step, then 5 launches of the dominant "
                          "kernel and 3 plain copies of 1 GiB (the counters' scale), nothing else")
@@ -314,7 +339,8 @@ def main():
     sga.load_library()
     dev = "cuda:0"
     wl = WORKLOADS[args.config]
-    step, conv_only, gn_in, flops, conv_launch_flops, info, conv_name = build_step(wl, dev, args.fused)
+    step, conv_only, gn_in, flops, conv_launch_flops, info, conv_name = build_step(wl, dev, args.fused,
+                                                                                    args.separate_stats)
 
     if args.profile_pass:
         step()

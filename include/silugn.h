@@ -128,6 +128,42 @@ int causal_conv3d(const uint16_t* x, sgn_dims d, const uint16_t* cache_in,
                   const sgn_gn* fuse, uint16_t* y, uint16_t* cache_out, hipStream_t stream);
 
 /*
+ * Bytes of device workspace causal_conv3d_next_stats needs for input dims d, K
+ * output channels and next_groups groups (0 if the arguments are invalid).
+ */
+size_t causal_conv3d_next_stats_workspace(sgn_dims d, int k, int next_groups);
+
+/*
+ * causal_conv3d_next_stats -- causal_conv3d, and the GroupNorm statistics of its
+ * output y for the GroupNorm that follows it.
+ * Defined by: binding.cpp page, Decoder::conv (the producer convolution's fused
+ * epilogue prepares the next convolution's normalized input: the next norm is
+ * folded into the producer) and Decoder::resnet (conv1 -> norm2 -> conv2). A
+ * GroupNorm needs statistics over the whole tensor before it can be applied, so
+ * what the epilogue can take over is the statistics pass over y.
+ *
+ * All arguments before next_groups as in causal_conv3d (same checks, same y and
+ * cache_out). Then:
+ *   next_stats  device fp64 [N][next_groups][2]: mean and biased variance of each
+ *               (n, g) over y's channels g*K/G .. (g+1)*K/G - 1 and all T*H*W
+ *               positions -- what gn_silu_stats(y, next_groups) returns, the sums
+ *               taken in a different fixed order (equal up to fp64 rounding).
+ *   ws          device workspace of causal_conv3d_next_stats_workspace(d, k,
+ *               next_groups) bytes, 16-byte aligned, overwritten.
+ * The statistics come from the convolution's epilogue when K % 8 == 0 and K/G is a
+ * multiple of 8 dividing the kernel's N tile; otherwise gn_silu_stats runs over y.
+ * Errors: next_groups must divide K and y's GroupNorm must be one gn_silu_stats
+ * accepts (K % 8 == 0; K/G = 1, 2, 4 or a multiple of 8), else SGN_EINVAL; a
+ * missing or short workspace is SGN_EWORKSPACE; ws, next_stats and y must not
+ * overlap (SGN_EALIAS).
+ */
+int causal_conv3d_next_stats(const uint16_t* x, sgn_dims d, const uint16_t* cache_in,
+                             const uint16_t* w, int k, const float* bias,
+                             const uint16_t* residual, const sgn_gn* fuse, uint16_t* y,
+                             uint16_t* cache_out, int next_groups, double* next_stats,
+                             void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
  * upsample2x_prepare_weights -- HOST function: the four 2x2 phase kernels of a
  * nearest-x2 + 3x3 convolution.
  * Defined by: binding.cpp page, prepare() ("Nearest-x2 + 3x3 convolution equals

@@ -36,7 +36,8 @@ class sgn_gn(ctypes.Structure):
 
 
 EXPORTS = ["sgn_last_error", "gn_silu_stats_workspace", "gn_silu_stats", "gn_silu_apply",
-           "causal_conv3d", "upsample2x_prepare_weights", "upsample2x_conv_phases", "head_conv_d2s"]
+           "causal_conv3d", "causal_conv3d_next_stats_workspace", "causal_conv3d_next_stats",
+           "upsample2x_prepare_weights", "upsample2x_conv_phases", "head_conv_d2s"]
 
 _lib = None
 
@@ -57,6 +58,9 @@ def load_library(path: str = LIB_PATH):
         "gn_silu_stats": (i32, [vp, sgn_dims, i32, vp, vp, sz, vp]),
         "gn_silu_apply": (i32, [vp, sgn_dims, i32, vp, vp, vp, f32, vp, vp]),
         "causal_conv3d": (i32, [vp, sgn_dims, vp, vp, i32, vp, vp, gnp, vp, vp, vp]),
+        "causal_conv3d_next_stats_workspace": (sz, [sgn_dims, i32, i32]),
+        "causal_conv3d_next_stats": (i32, [vp, sgn_dims, vp, vp, i32, vp, vp, gnp, vp, vp, i32, vp, vp,
+                                           sz, vp]),
         "upsample2x_prepare_weights": (i32, [vp, i32, i32, vp]),
         "upsample2x_conv_phases": (i32, [vp, sgn_dims, vp, i32, vp, vp, vp]),
         "head_conv_d2s": (i32, [vp, sgn_dims, vp, vp, vp, gnp, i32, vp, vp, vp]),
@@ -137,6 +141,30 @@ def causal_conv3d(x, w, cache_in=None, bias=None, residual=None, fuse=None, y=No
     _check(lib.causal_conv3d(_ptr(x), _dims(x), _ptr(cache_in), _ptr(w), k, _ptr(bias), _ptr(residual),
                              gp, _ptr(y), _ptr(cache_out), _stream(x)))
     return y
+
+
+def causal_conv3d_next_stats_workspace(dims, k: int, next_groups: int) -> int:
+    return int(load_library().causal_conv3d_next_stats_workspace(sgn_dims(*dims), k, next_groups))
+
+
+def causal_conv3d_next_stats(x, w, next_groups: int, cache_in=None, bias=None, residual=None, fuse=None,
+                             y=None, cache_out=None, stats=None, ws=None):
+    """causal_conv3d, plus the GroupNorm statistics (fp64 [N, G, 2]) of its output; returns (y, stats)."""
+    lib = load_library()
+    k = w.shape[0]
+    if y is None:
+        y = torch.empty(x.shape[:4] + (k,), dtype=torch.bfloat16, device=x.device)
+    if stats is None:
+        stats = torch.empty((x.shape[0], next_groups, 2), dtype=torch.float64, device=x.device)
+    d = _dims(x)
+    need = lib.causal_conv3d_next_stats_workspace(d, k, next_groups)
+    if ws is None:
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    gp, _keep = _gn(fuse)
+    _check(lib.causal_conv3d_next_stats(_ptr(x), d, _ptr(cache_in), _ptr(w), k, _ptr(bias), _ptr(residual), gp,
+                                        _ptr(y), _ptr(cache_out), next_groups, _ptr(stats), _ptr(ws),
+                                        ws.numel() * ws.element_size(), _stream(x)))
+    return y, stats
 
 
 def upsample2x_prepare_weights(w3x3):

@@ -57,6 +57,10 @@ struct ConvParams {
   int64_t mper;              // output positions per sample (and per phase)
   int nblocks;
   int clamp;
+  // Statistics of y for the next GroupNorm (causal, staged epilogue), or nws == null:
+  // partial sums S, Q of every (sample, group, tile) in the layout gn_stats_finalize reads.
+  double* nws;
+  int ngroups, ncg;          // groups over K, channels per group (a multiple of 8 dividing BN)
 };
 
 
@@ -197,8 +201,12 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[TN][TM], const Co
 // Staging layout: row r (position) of WTN * 4 bytes; the 16-byte chunk c (4 channels) sits
 // at c ^ (r & SWZ), SWZ = min(15, WTN / 4 - 1), so 8 consecutive rows at one chunk, and 8
 // chunks of one row, hit distinct bank groups.
+struct Sums {
+  double s, q;
+};
+
 template <int MODE, int TN, int TM, int WTM, int WTN>
-__device__ __forceinline__ void store_tile_staged(const f32x16 (&acc)[TN][TM], const ConvParams& p, int n,
+__device__ __forceinline__ Sums store_tile_staged(const f32x16 (&acc)[TN][TM], const ConvParams& p, int n,
                                                   int t, int pos0, int kbase, int wm, int lane,
                                                   int phase, const float* lbias, char* stage) {
   static_assert(MODE == kCausal || MODE == kPhase, "staged epilogue modes");
@@ -223,6 +231,9 @@ __device__ __forceinline__ void store_tile_staged(const f32x16 (&acc)[TN][TM], c
     const int h_ = ml / W, w_ = ml - h_ * W;
     return (uint32_t)(((((int64_t)(2 * h_ + pa)) * (2 * W) + 2 * w_ + pb) * K + k0) * 2);
   };
+  // Statistics for the next GroupNorm: this lane's stored values and their exact squares.
+  const bool stats = MODE == kCausal && p.nws != nullptr;
+  double ss = 0.0, sq = 0.0;
   // Residual of every row this lane stores, before any store.
   u32x4 rv[MODE == kCausal ? TM : 1][MODE == kCausal ? NI : 1];
   if (MODE == kCausal && p.res) {
@@ -275,6 +286,16 @@ __device__ __forceinline__ void store_tile_staged(const f32x16 (&acc)[TN][TM], c
 #pragma unroll
       for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(v[2 * e], v[2 * e + 1]);
       const int ml = pos0 + wm * WTM + 32 * j + r;
+      if (stats && ml < HW && k0 < K) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const double lo2 = bf16_lo(o[e]), hi2 = bf16_hi(o[e]);
+          ss += lo2;
+          ss += hi2;
+          sq = fma(lo2, lo2, sq);
+          sq = fma(hi2, hi2, sq);
+        }
+      }
       if (kfull) {
         __builtin_amdgcn_raw_buffer_store_b128(o, ys, out_off(ml), 0, 0);   // past the frame: dropped
       } else if (k0 < K && ml < HW) {
@@ -286,6 +307,44 @@ __device__ __forceinline__ void store_tile_staged(const f32x16 (&acc)[TN][TM], c
       }
     }
     wait_lgkm0();                                    // reads done before the next rows land
+  }
+  return Sums{ss, sq};
+}
+
+// Statistics for the next GroupNorm, per workgroup: every lane's (S, Q) of the rounded
+// values it stored (8 channels of one group, its rows) goes to LDS; then one thread per
+// group of the tile adds the lanes holding that group in a fixed order (waves by channel
+// block, then row block; lanes by channel, then row) and writes the tile's partial where
+// gn_stats_finalize reads it: ws[((n * G + g) * 2 + {0, 1}) * nblk + blk], nblk = T x tiles
+// per frame, blk = t x tiles per frame + mt. A group lies inside one N tile (BN % cg == 0).
+template <int NW, int WGM, int WTN, int BN>
+__device__ __forceinline__ void next_stats_partials(const ConvParams& p, int n, int t, int mt, int ntile,
+                                                    int wave, int lane, Sums sums, double* red) {
+  constexpr int LPR = WTN / 8, RPI = 64 / LPR;
+  red[(wave * 64 + lane) * 2 + 0] = sums.s;
+  red[(wave * 64 + lane) * 2 + 1] = sums.q;
+  __syncthreads();
+  const int tid = threadIdx.x, cg = p.ncg;
+  const int k_lo = ntile * BN;
+  const int kt = p.K - k_lo < BN ? p.K - k_lo : BN;   // channels of this N tile
+  if (tid < kt / cg) {
+    const int c_begin = tid * cg;                   // the group's first channel in the tile
+    double S = 0.0, Q = 0.0;
+    for (int wn = 0; wn < NW / WGM; ++wn)
+      for (int wm = 0; wm < WGM; ++wm)
+        for (int c8 = 0; c8 < LPR; ++c8) {
+          const int ch = wn * WTN + 8 * c8;
+          if (ch < c_begin || ch >= c_begin + cg) continue;
+          for (int rr = 0; rr < RPI; ++rr) {
+            const int e = ((wn * WGM + wm) * 64 + rr * LPR + c8) * 2;
+            S += red[e];
+            Q += red[e + 1];
+          }
+        }
+    const int nblk = p.T * p.tiles_f, blk = t * p.tiles_f + mt;
+    double* o = p.nws + (((int64_t)n * p.ngroups + k_lo / cg + tid) * 2) * nblk;
+    o[blk] = S;
+    o[nblk + blk] = Q;
   }
 }
 
@@ -701,9 +760,13 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_kernel(ConvParams p) {
     store_tile<MODE, TN, TM, WTM, WTN>(acc, p, n, (int64_t)t * HW + mt * BM, (int64_t)(t + 1) * HW,
                                        ntile * BN + wn * WTN, wm, lane, phase, lbias + wn * WTN);
   } else if (K % 8 == 0) {                           // rows of y 16-byte aligned
-    static_assert(NW * 32 * WTN * 4 <= NS * STAGE, "epilogue staging fits the stages");
-    store_tile_staged<MODE, TN, TM, WTM, WTN>(acc, p, n, t, mt * BM, ntile * BN + wn * WTN, wm, lane, phase,
-                                              lbias + wn * WTN, smem + wave * (32 * WTN * 4));
+    static_assert(NW * 32 * WTN * 4 + NW * 64 * 16 <= NS * STAGE, "epilogue staging fits the stages");
+    const Sums sums = store_tile_staged<MODE, TN, TM, WTM, WTN>(
+        acc, p, n, t, mt * BM, ntile * BN + wn * WTN, wm, lane, phase, lbias + wn * WTN,
+        smem + wave * (32 * WTN * 4));
+    if (MODE == kCausal && p.nws)
+      next_stats_partials<NW, WGM, WTN, BN>(p, n, t, mt, ntile, wave, lane, sums,
+                                            reinterpret_cast<double*>(smem + NW * 32 * WTN * 4));
   } else {
     store_tile<MODE, TN, TM, WTM, WTN>(acc, p, n, (int64_t)t * HW + mt * BM, (int64_t)(t + 1) * HW,
                                        ntile * BN + wn * WTN, wm, lane, phase, lbias + wn * WTN);
@@ -1119,10 +1182,14 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_slab_kernel(ConvParams
 
   static_assert(NW * 32 * WTN * 4 <= SLABS, "epilogue staging fits the weight stages");
   const float* lb = reinterpret_cast<const float*>(smem + LBIAS) + wn * WTN;
-  if (K % 8 == 0)                                    // rows of y 16-byte aligned
-    store_tile_staged<MODE, TN, TM, WTM, WTN>(acc, p, n, t, pos0, ntile * BN + wn * WTN, wm, lane, phase,
-                                              lb, smem + wave * (32 * WTN * 4));
-  else
+  if (K % 8 == 0) {                                  // rows of y 16-byte aligned
+    const Sums sums = store_tile_staged<MODE, TN, TM, WTM, WTN>(
+        acc, p, n, t, pos0, ntile * BN + wn * WTN, wm, lane, phase, lb, smem + wave * (32 * WTN * 4));
+    static_assert(NW * 32 * WTN * 4 + NW * 64 * 16 <= SLABS + NSL * SLAB, "statistics area");
+    if (MODE == kCausal && p.nws)
+      next_stats_partials<NW, WGM, WTN, BN>(p, n, t, mt, ntile, wave, lane, sums,
+                                            reinterpret_cast<double*>(smem + NW * 32 * WTN * 4));
+  } else
     store_tile<MODE, TN, TM, WTM, WTN>(acc, p, n, (int64_t)t * HW + pos0, (int64_t)(t + 1) * HW,
                                        ntile * BN + wn * WTN, wm, lane, phase, lb);
 }
@@ -1530,12 +1597,31 @@ static int check_fuse(const sgn_gn* f, sgn_dims d, const char* fn) {
 
 using namespace sgn;
 
-extern "C" int causal_conv3d(const uint16_t* x, sgn_dims d, const uint16_t* cache_in,
-                             const uint16_t* w, int k, const float* bias, const uint16_t* residual,
-                             const sgn_gn* fuse, uint16_t* y, uint16_t* cache_out,
-                             hipStream_t stream) {
-  const char* fn = "causal_conv3d";
-  clear_error();
+namespace sgn {
+
+// The GroupNorm statistics of y requested by causal_conv3d_next_stats.
+struct NextStats {
+  int groups;
+  double* stats;
+  void* ws;
+  size_t ws_bytes;
+};
+
+// Workspace of causal_conv3d_next_stats: the larger of its two paths (partial sums of the
+// epilogue, sized for the smallest M tile; or gn_silu_stats over y).
+static size_t next_stats_bytes(sgn_dims d, int k, int groups) {
+  const int64_t tiles_f = (d.h * d.w + 223) / 224;
+  const size_t fused = (size_t)d.n * groups * 2 * (size_t)(d.t * tiles_f) * sizeof(double);
+  sgn_dims yd = d;
+  yd.c = k;
+  const size_t plain = gn_silu_stats_workspace(yd, groups);
+  return fused > plain ? fused : plain;
+}
+
+static int causal_conv_impl(const char* fn, const uint16_t* x, sgn_dims d, const uint16_t* cache_in,
+                            const uint16_t* w, int k, const float* bias, const uint16_t* residual,
+                            const sgn_gn* fuse, uint16_t* y, uint16_t* cache_out, const NextStats* ns,
+                            hipStream_t stream) {
   if (!conv_common_checks(x, d, w, k, y, fn)) return SGN_EINVAL;
   int rc = check_fuse(fuse, d, fn);
   if (rc) return rc;
@@ -1580,9 +1666,89 @@ extern "C" int causal_conv3d(const uint16_t* x, sgn_dims d, const uint16_t* cach
   p.mper = d.t * d.h * d.w;
   const TileCfg cfg = fuse ? choose_tile<kCausal, true>(d.h * d.w, d.t, k, p.C, d.n)
                            : choose_tile<kCausal, false>(d.h * d.w, d.t, k, p.C, d.n);
+  // Statistics of y from the epilogue when its lanes hold whole 8-channel slices of one group
+  // inside one N tile; otherwise from gn_silu_stats over y after the convolution.
+  const int ncg = ns ? k / ns->groups : 0;
+  const bool in_epilogue = ns && k % 8 == 0 && ncg % 8 == 0 && cfg.bn % ncg == 0;
+  if (in_epilogue) {
+    p.nws = static_cast<double*>(ns->ws);
+    p.ngroups = ns->groups;
+    p.ncg = ncg;
+  }
   if (!launch_conv(cfg, p, d.n, 1, stream, fn)) return SGN_ELAUNCH;
   if (cache_out && !launch_cache_out(x, d, cache_in, fuse, cache_out, stream)) return SGN_ELAUNCH;
+  if (in_epilogue) {
+    const double length = (double)ncg * (double)(d.t * d.h * d.w);
+    if (!launch_gn_finalize(p.nws, (int)(d.t * p.tiles_f), ns->groups, d.n, length, ns->stats, stream))
+      return SGN_ELAUNCH;
+  } else if (ns) {
+    sgn_dims yd = d;
+    yd.c = k;
+    const int rc = gn_silu_stats(y, yd, ns->groups, ns->stats, ns->ws, ns->ws_bytes, stream);
+    if (rc != SGN_OK) return rc;
+  }
   return SGN_OK;
+}
+
+}  // namespace sgn
+
+extern "C" int causal_conv3d(const uint16_t* x, sgn_dims d, const uint16_t* cache_in,
+                             const uint16_t* w, int k, const float* bias, const uint16_t* residual,
+                             const sgn_gn* fuse, uint16_t* y, uint16_t* cache_out,
+                             hipStream_t stream) {
+  clear_error();
+  return causal_conv_impl("causal_conv3d", x, d, cache_in, w, k, bias, residual, fuse, y, cache_out,
+                          nullptr, stream);
+}
+
+extern "C" size_t causal_conv3d_next_stats_workspace(sgn_dims d, int k, int next_groups) {
+  if (d.n <= 0 || d.t <= 0 || d.h <= 0 || d.w <= 0 || k < 8 || next_groups <= 0 || k % next_groups)
+    return 0;
+  return next_stats_bytes(d, k, next_groups);
+}
+
+extern "C" int causal_conv3d_next_stats(const uint16_t* x, sgn_dims d, const uint16_t* cache_in,
+                                        const uint16_t* w, int k, const float* bias,
+                                        const uint16_t* residual, const sgn_gn* fuse, uint16_t* y,
+                                        uint16_t* cache_out, int next_groups, double* next_stats,
+                                        void* ws, size_t ws_bytes, hipStream_t stream) {
+  const char* fn = "causal_conv3d_next_stats";
+  clear_error();
+  if (next_groups <= 0 || k % next_groups != 0) {
+    set_error("%s: next_groups=%d must divide K=%d", fn, next_groups, k);
+    return SGN_EINVAL;
+  }
+  {
+    sgn_dims yd = d;
+    yd.c = k;
+    if (gn_silu_stats_workspace(yd, next_groups) == 0) {
+      set_error("%s: a GroupNorm of K=%d channels in %d groups is not supported (see gn_silu_stats)", fn, k,
+                next_groups);
+      return SGN_EINVAL;
+    }
+  }
+  if (!next_stats || ((uintptr_t)next_stats & 7)) {
+    set_error("%s: next_stats must be an 8-byte aligned device pointer", fn);
+    return !next_stats ? SGN_EINVAL : SGN_EALIGN;
+  }
+  if (!dims_ok(d, fn)) return SGN_EINVAL;
+  const size_t need = next_stats_bytes(d, k, next_groups);
+  if (!ws || ws_bytes < need) {
+    set_error("%s: workspace of %zu bytes required, got %zu", fn, need, ws ? ws_bytes : 0);
+    return SGN_EWORKSPACE;
+  }
+  if (!aligned16(ws)) {
+    set_error("%s: workspace must be 16-byte aligned", fn);
+    return SGN_EALIGN;
+  }
+  const size_t yb = (size_t)(d.n * d.t * d.h * d.w) * k * 2;
+  const size_t sb = (size_t)d.n * next_groups * 2 * sizeof(double);
+  if (overlap(ws, ws_bytes, y, yb) || overlap(next_stats, sb, y, yb) || overlap(ws, ws_bytes, next_stats, sb)) {
+    set_error("%s: the workspace, next_stats and y must not overlap", fn);
+    return SGN_EALIAS;
+  }
+  const NextStats ns = {next_groups, next_stats, ws, ws_bytes};
+  return causal_conv_impl(fn, x, d, cache_in, w, k, bias, residual, fuse, y, cache_out, &ns, stream);
 }
 
 extern "C" int upsample2x_conv_phases(const uint16_t* x, sgn_dims d, const uint16_t* w_phase, int k,

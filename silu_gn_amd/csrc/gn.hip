@@ -313,6 +313,12 @@ extern "C" int gn_silu_stats(const uint16_t* x, sgn_dims d, int groups, double* 
   return SGN_OK;
 }
 
+bool sgn::launch_gn_finalize(const double* ws, int nblk, int groups, int64_t n, double length,
+                        double* stats, hipStream_t stream) {
+  gn_stats_finalize<<<dim3(groups, (unsigned)n), kThreads, 0, stream>>>(ws, nblk, groups, length, stats);
+  return launch_ok("GroupNorm statistics (finalize)");
+}
+
 extern "C" int gn_silu_apply(const uint16_t* x, sgn_dims d, int groups, const double* stats,
                              const float* gamma, const float* beta, float eps, uint16_t* y,
                              hipStream_t stream) {

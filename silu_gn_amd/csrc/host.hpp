@@ -25,4 +25,10 @@ bool dims_ok(sgn_dims d, const char* fn);
 // Checks hipGetLastError after a launch; records the HIP message on failure.
 bool launch_ok(const char* what);
 
+// GroupNorm statistics from per-block partial sums (gn.hip): ws holds, for every sample n
+// and group g, nblk sums S then nblk sums Q at ws[((n * groups + g) * 2) * nblk]; stats
+// receives mean = S / length and the biased variance Q / length - mean^2 per (n, g).
+bool launch_gn_finalize(const double* ws, int nblk, int groups, int64_t n, double length,
+                        double* stats, hipStream_t stream);
+
 }  // namespace sgn

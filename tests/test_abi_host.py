@@ -95,6 +95,36 @@ def test_conv_rejects():
          EINVAL)
 
 
+def test_next_stats_workspace_size():
+    lib = sga.load_library()
+    ws = lib.causal_conv3d_next_stats_workspace(D(), 256, 32)
+    assert ws >= lib.gn_silu_stats_workspace(D(c=256), 32) > 0      # covers the gn_silu_stats route
+    assert ws >= 1 * 32 * 2 * 2 * 1 * 8                              # and the epilogue's partials
+    assert lib.causal_conv3d_next_stats_workspace(D(), 256, 48) == 0  # groups does not divide K
+    assert lib.causal_conv3d_next_stats_workspace(D(t=0), 256, 32) == 0
+
+
+def test_next_stats_rejects():
+    lib = sga.load_library()
+    far = FAKE + (1 << 32)
+    w = FAKE + (1 << 30)
+    big = 1 << 30
+
+    def call(k=256, groups=32, stats=far + (1 << 31), ws=far + (1 << 33), ws_bytes=big, y=far):
+        return lib.causal_conv3d_next_stats(FAKE, D(), None, w, k, None, None, None, y, None, groups, stats, ws,
+                                            ws_bytes, None)
+    _err(call(groups=48), EINVAL)                      # groups must divide K
+    _err(call(stats=None), EINVAL)
+    _err(call(stats=far + (1 << 31) + 4), EALIGN)
+    _err(call(ws=None), EWORKSPACE)
+    _err(call(ws_bytes=16), EWORKSPACE)
+    _err(call(ws=far + (1 << 33) + 8), EALIGN)
+    _err(call(ws=far + 64), EALIAS)                    # workspace inside y
+    _err(call(k=6, groups=3), EINVAL)                  # the convolution's own checks (K % 4)
+    _err(call(k=12, groups=3), EINVAL)                 # y's GroupNorm: K % 8 (gn_silu_stats)
+    _err(call(k=96, groups=8), EINVAL)                 # y's GroupNorm: 12 channels per group
+
+
 def test_upsample_and_head_reject():
     lib = sga.load_library()
     far = FAKE + (1 << 32)

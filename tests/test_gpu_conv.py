@@ -206,3 +206,63 @@ def test_fullres_conv_full_size_sampled():
     torch.cuda.synchronize()
     xc = x.cpu()
     _sampled_fused_check(xc, wt, ci.cpu(), gamma, beta, wl.groups, wl.eps, y, residual=xc, seed=4)
+
+
+@pytest.mark.parametrize("shape,k,groups,fused,res", [
+    ((1, 3, 16, 16, 256), 256, 32, False, True),     # slab kernel, 8 channels per group, residual
+    ((1, 2, 5, 37, 256), 1024, 32, False, False),    # four N tiles, 32 channels per group, ragged M
+    ((1, 3, 9, 20, 128), 128, 16, False, False),     # conv_kernel (K <= 128)
+    ((2, 2, 7, 9, 256), 256, 32, True, False),       # GroupNorm fused in, statistics out, two samples
+    ((1, 2, 6, 10, 64), 64, 32, False, False),       # 2 channels per group: the gn_silu_stats route
+    ((1, 2, 6, 10, 64), 72, 9, False, False),        # 72 channels in a 128-wide N tile, 9 groups
+    ((1, 2, 6, 10, 64), 96, 4, False, False),        # 24 per group, not dividing the N tile: gn_silu_stats
+])
+def test_conv_next_stats(shape, k, groups, fused, res):
+    """causal_conv3d_next_stats: y as causal_conv3d, and GroupNorm statistics of y."""
+    print("case next stats", shape, k, groups, fused, res, flush=True)
+    n, t, h, w, c = shape
+    seed = n + t + h + w + c + k + groups
+    x = sg.normal(shape, seed, sg.X, mean=0.1)
+    wt = _w(k, c, seed)
+    ci = sg.normal((n, 2, h, w, c), seed, sg.X_PREV)
+    b = sg.normal((k,), seed, sg.BETA2, std=0.5, dtype=torch.float32)
+    r = sg.normal((n, t, h, w, k), seed, sg.GAMMA2) if res else None
+    xd, wd, cd, bd = x.to(DEV), wt.to(DEV), ci.to(DEV), b.to(DEV)
+    rd = r.to(DEV) if res else None
+    fuse, act = None, vals(x)
+    if fused:
+        gamma, beta = _gn_params(c, seed)
+        st_in = sga.gn_silu_stats(xd, 32)
+        fuse = (st_in, gamma.to(DEV), beta.to(DEV), 1e-5, 32)
+        a64, _ = ogn.gn_silu(vals(x), 32, gamma.numpy(), beta.numpy(), 1e-5)
+        act = obf16.decode(obf16.round_rne(a64))
+    y1 = sga.causal_conv3d(xd, wd, cd, bd, rd, fuse)
+    y2, st = sga.causal_conv3d_next_stats(xd, wd, groups, cd, bd, rd, fuse)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    st = st.cpu().numpy()
+    # the same values summed in another fixed order
+    ref = sga.gn_silu_stats(y2, groups).cpu().numpy()
+    np.testing.assert_allclose(st, ref, rtol=1e-12, atol=1e-14)
+    # the oracle: statistics of its convolution rounded once to bf16; y may differ from that
+    # rounding by one bf16 ulp in places, which bounds the difference of the statistics
+    o, _ = oconv.causal_conv3d(act, vals(wt), vals(ci), b.numpy(), vals(r) if res else None)
+    ob = obf16.decode(obf16.round_rne(o))
+    mean, var = ogn.group_stats(ob, groups)
+    scale = np.sqrt(np.mean(ob.astype(np.float64) ** 2))
+    np.testing.assert_allclose(st[..., 0], mean, rtol=0, atol=2.0 ** -7 * scale)
+    np.testing.assert_allclose(st[..., 1], var, rtol=2.0 ** -6, atol=2.0 ** -7 * scale * scale)
+
+
+def test_conv_next_stats_fullres_workload():
+    """[1,16,352,624,256] -> K = 256, G = 32 (the full-resolution block's conv1 -> norm2):
+    13728 tiles per sample; the epilogue's statistics equal gn_silu_stats over y."""
+    wl = WORKLOADS[4]
+    print("case next stats full-resolution workload", flush=True)
+    x = wl.x(device=DEV)
+    wt = wl.conv_weight(1, device=DEV)
+    cache = wl.x_prev(device=DEV)[:, -2:].contiguous()
+    y, st = sga.causal_conv3d_next_stats(x, wt, wl.groups, cache)
+    ref = sga.gn_silu_stats(y, wl.groups)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(st.cpu().numpy(), ref.cpu().numpy(), rtol=1e-12, atol=1e-14)
