@@ -14,6 +14,10 @@ FastVideo ``wan22_vae_decode/solution/binding.cpp``):
 * ``groupnorm``  -- per (sample, group) mean and biased variance; z = (x - mean)
                     / sqrt(var + eps) * gamma + beta; silu(z) = z / (1 + e^-z)
                     (group_norm_silu.py docstring and its apply kernel).
+* ``rmsnorm``    -- the per-position RMS norm + SiLU the pages' decoder runs before its
+                    output head (binding.cpp, the comment above Decoder::output_head):
+                    z = x * gain / sqrt(mean_c(x^2) + eps), silu(z). The formula is
+                    not printed on the pages; this is the usual RMS norm (the reading).
 * ``conv``       -- the causal 3x3x3 convolution over cat(cache, input) with
                     1-pixel spatial zero padding and the 2-frame cache
                     (binding.cpp, Decoder::conv); nearest-x2 upsample + 3x3
