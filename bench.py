@@ -10,7 +10,8 @@ Other workloads: --config 1..5 (see synthgen/workloads.py).
 Prints ONE JSON line. ``value`` = algorithmic conv FLOPs of a step / step time
 (TFLOP/s). ``roofline`` is the conv kernel alone (HIP events on the stream it runs
 on) against the bf16 dense MFMA peak; ``gn_silu`` is gn_silu_stats + gn_silu_apply on
-the same tensor at 6 bytes/element against HBM peak; ``box_ceilings`` is what this GPU
+the same tensor at 6 bytes/element against HBM peak; ``rms_silu`` is the output head's
+RMS norm + SiLU on that tensor at 4 bytes/element; ``box_ceilings`` is what this GPU
 sustains for those two resources (libsgnprobe.so: bf16 MFMA with random and with
 constant operand bits, HBM streaming read and copy), with each fraction repeated
 against it; ``cpu_baseline`` is the fp64 oracle on the host over a bounded sample
@@ -386,6 +387,8 @@ def main():
     stats_ms = time_loop(lambda: sga.gn_silu_stats(x, g, gc.stats, gc.ws), iters)
     apply_ms = time_loop(lambda: sga.gn_silu_apply(x, g, gc.stats, gc.gamma, gc.beta, wl.eps, y=yb), iters)
     gn_bytes = 6.0 * x.numel()
+    # the output head's norm (RMS norm + SiLU, one read and one write) on the same tensor
+    rms_ms = time_loop(lambda: sga.rms_silu(x, gc.gamma, 1e-6, y=yb), iters) if x.shape[-1] % 64 == 0 else None
     achieved = conv_launch_flops / (conv_ms * 1e-3) / 1e12
     gn_gbps = gn_bytes / ((stats_ms + apply_ms) * 1e-3) / 1e9
     flushed = None
@@ -447,6 +450,11 @@ def main():
                     "bytes_per_element": 6},
         "stages_ms": {k: round(v, 4) for k, v in stages.items()},
     }
+    if rms_ms:
+        rms_gbps = 4.0 * x.numel() / (rms_ms * 1e-3) / 1e9
+        out["rms_silu"] = {"GB/s": round(rms_gbps, 1), "peak": PEAK_HBM_GBPS,
+                           "frac": round(rms_gbps / PEAK_HBM_GBPS, 4), "ms": round(rms_ms, 4),
+                           "bytes_per_element": 4}
     if flushed:
         out["gn_silu"]["cold_cache"] = flushed
     if ceilings:
@@ -458,6 +466,8 @@ def main():
                  4.0 * x.numel() / (ceilings["hbm_copy_GB/s"] * 1e9))
         out["gn_silu"]["box_GB/s"] = round(gn_bytes / box_s / 1e9, 1)
         out["gn_silu"]["frac_of_box"] = round(gn_gbps / (gn_bytes / box_s / 1e9), 4)
+        if rms_ms:
+            out["rms_silu"]["frac_of_box"] = round(rms_gbps / ceilings["hbm_copy_GB/s"], 4)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(out), flush=True)

@@ -100,6 +100,24 @@ int gn_silu_apply(const uint16_t* x, sgn_dims d, int groups, const double* stats
                   hipStream_t stream);
 
 /*
+ * rms_silu -- RMS norm + SiLU per position.
+ * Defined by: binding.cpp page, the comment above Decoder::output_head (the decoder
+ * normalizes with an RMS norm followed by SiLU, with a per-channel gain: norm_pad(x,
+ * gain, ...)). The pages do not print the formula; the usual RMS norm is read:
+ *
+ *   z[p, c] = x[p, c] * gain[c] / sqrt(mean_c(x[p, :]^2) + eps)
+ *   y[p, c] = RNE_bf16( z * sigmoid(z) )
+ *
+ * for every position p = (n, t, h, w) on its own (no statistics across positions).
+ * The mean of squares and z are formed in fp64, the SiLU in fp32 as in
+ * gn_silu_apply. x, y: bf16 (N,T,H,W,C), 16-byte aligned, y == x allowed (in
+ * place), any other overlap is SGN_EALIAS; gain: device fp32 [C]; eps > 0.
+ * Requires C % 64 == 0 with C <= 4096, else SGN_EINVAL.
+ */
+int rms_silu(const uint16_t* x, sgn_dims d, const float* gain, float eps, uint16_t* y,
+             hipStream_t stream);
+
+/*
  * causal_conv3d -- causal 3x3x3 convolution with a 2-frame temporal cache.
  * Defined by: FastVideo wan22_vae_decode binding.cpp page, Decoder::conv (front
  * temporal padding of kt-1 = 2 frames taken from the per-conv cache, spatial

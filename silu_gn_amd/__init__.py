@@ -35,7 +35,7 @@ class sgn_gn(ctypes.Structure):
                 ("eps", ctypes.c_float), ("groups", ctypes.c_int)]
 
 
-EXPORTS = ["sgn_last_error", "gn_silu_stats_workspace", "gn_silu_stats", "gn_silu_apply",
+EXPORTS = ["sgn_last_error", "gn_silu_stats_workspace", "gn_silu_stats", "gn_silu_apply", "rms_silu",
            "causal_conv3d", "causal_conv3d_next_stats_workspace", "causal_conv3d_next_stats",
            "upsample2x_prepare_weights", "upsample2x_conv_phases", "head_conv_d2s"]
 
@@ -57,6 +57,7 @@ def load_library(path: str = LIB_PATH):
         "gn_silu_stats_workspace": (sz, [sgn_dims, i32]),
         "gn_silu_stats": (i32, [vp, sgn_dims, i32, vp, vp, sz, vp]),
         "gn_silu_apply": (i32, [vp, sgn_dims, i32, vp, vp, vp, f32, vp, vp]),
+        "rms_silu": (i32, [vp, sgn_dims, vp, f32, vp, vp]),
         "causal_conv3d": (i32, [vp, sgn_dims, vp, vp, i32, vp, vp, gnp, vp, vp, vp]),
         "causal_conv3d_next_stats_workspace": (sz, [sgn_dims, i32, i32]),
         "causal_conv3d_next_stats": (i32, [vp, sgn_dims, vp, vp, i32, vp, vp, gnp, vp, vp, i32, vp, vp,
@@ -125,6 +126,15 @@ def gn_silu_apply(x, groups: int, stats, gamma, beta, eps: float, y=None):
         y = torch.empty_like(x)
     _check(lib.gn_silu_apply(_ptr(x), _dims(x), groups, _ptr(stats), _ptr(gamma), _ptr(beta),
                              float(eps), _ptr(y), _stream(x)))
+    return y
+
+
+def rms_silu(x, gain, eps: float, y=None):
+    """bf16 silu(rms_norm(x)) per position over the channels; ``y`` may be ``x`` (in place)."""
+    lib = load_library()
+    if y is None:
+        y = torch.empty_like(x)
+    _check(lib.rms_silu(_ptr(x), _dims(x), _ptr(gain), float(eps), _ptr(y), _stream(x)))
     return y
 
 

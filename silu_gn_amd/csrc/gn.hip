@@ -257,6 +257,76 @@ static bool gn_shape_ok(sgn_dims d, int groups, const char* fn) {
   return true;
 }
 
+
+// ---------------------------------------------------------------- RMS norm + SiLU
+// Per position (no statistics across positions): z = x * gain / sqrt(mean_c x^2 + eps),
+// out = RNE_bf16(z * sigmoid(z)). LPP lanes (a power of two, >= C/8 up to 64) share one
+// position, each holding PPL packets of 8 channels (lanes past C/8 hold none); a wave covers
+// 64 / LPP positions, U groups of them per iteration (U x PPL packets in flight per lane).
+// Each lane sums the exact squares of its values in fp64 (x*x has 16 significant bits) and
+// the LPP lanes add their sums by a xor butterfly: the same order for every position. The
+// pre-activation x * (gain * rstd) is formed in fp64 and the SiLU in fp32 by
+// activate_packet, as in gn_silu_apply.
+template <int LPP, int PPL, int U>
+__global__ __launch_bounds__(kThreads) void rms_silu_kernel(const uint4* __restrict__ x, uint4* __restrict__ y,
+                                                            int64_t positions, int cp,
+                                                            const float* __restrict__ gain, double eps,
+                                                            double channels) {
+  constexpr int PPW = 64 / LPP;                      // positions per wave
+  const int lane = threadIdx.x & 63;
+  const int sub = lane / LPP, li = lane % LPP;
+  float g[PPL][8];
+#pragma unroll
+  for (int j = 0; j < PPL; ++j) {
+    const int col = li + j * LPP;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) g[j][i] = col < cp ? gain[col * 8 + i] : 0.0f;
+  }
+  const int64_t wave = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  const int64_t stride = (int64_t)gridDim.x * (kThreads / 64) * U * PPW;
+  for (int64_t base = wave * U * PPW; base < positions; base += stride) {
+    uint4 v[U][PPL];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t pos = base + u * PPW + sub;
+#pragma unroll
+      for (int j = 0; j < PPL; ++j) {
+        const int col = li + j * LPP;
+        v[u][j] = pos < positions && col < cp ? load_stream(x + pos * cp + col) : make_uint4(0, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t pos = base + u * PPW + sub;
+      double ss = 0.0;
+#pragma unroll
+      for (int j = 0; j < PPL; ++j) {
+        const uint32_t d[4] = {v[u][j].x, v[u][j].y, v[u][j].z, v[u][j].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const double a = (double)bf16_lo(d[i]), b = (double)bf16_hi(d[i]);
+          ss = fma(a, a, ss);
+          ss = fma(b, b, ss);
+        }
+      }
+#pragma unroll
+      for (int o = LPP / 2; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+      const double rstd = 1.0 / sqrt(ss / channels + eps);
+#pragma unroll
+      for (int j = 0; j < PPL; ++j) {
+        const int col = li + j * LPP;
+        Affine a[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          a[i].s = (double)g[j][i] * rstd;
+          a[i].b = 0.0;
+        }
+        if (pos < positions && col < cp) store_stream(y + pos * cp + col, activate_packet(v[u][j], a));
+      }
+    }
+  }
+}
+
 }  // namespace sgn
 
 using namespace sgn;
@@ -349,5 +419,54 @@ extern "C" int gn_silu_apply(const uint16_t* x, sgn_dims d, int groups, const do
       reinterpret_cast<const uint4*>(x), reinterpret_cast<uint4*>(y), positions, g.cp, g.rstep,
       g.rows_per_block, stats, gamma, beta, (double)eps, groups, cg);
   if (!launch_ok("gn_silu_apply")) return SGN_ELAUNCH;
+  return SGN_OK;
+}
+
+extern "C" int rms_silu(const uint16_t* x, sgn_dims d, const float* gain, float eps, uint16_t* y,
+                        hipStream_t stream) {
+  clear_error();
+  if (!dims_ok(d, "rms_silu")) return SGN_EINVAL;
+  if (d.c % 64 != 0 || d.c > 4096) {
+    set_error("rms_silu: C=%lld must be a multiple of 64, at most 4096", (long long)d.c);
+    return SGN_EINVAL;
+  }
+  if (!x || !gain || !y) {
+    set_error("rms_silu: x, gain and y are required");
+    return SGN_EINVAL;
+  }
+  if (!(eps > 0.0f) || !isfinite(eps)) {
+    set_error("rms_silu: eps must be a positive finite number");
+    return SGN_EINVAL;
+  }
+  if (!aligned16(x) || !aligned16(y) || ((uintptr_t)gain & 3)) {
+    set_error("rms_silu: x, y must be 16-byte aligned (gain 4)");
+    return SGN_EALIGN;
+  }
+  const size_t bytes = (size_t)(d.n * d.t * d.h * d.w * d.c) * 2;
+  if ((const void*)x != (const void*)y && overlap(x, bytes, y, bytes)) {
+    set_error("rms_silu: y partially overlaps x (only y == x is allowed)");
+    return SGN_EALIAS;
+  }
+  const int64_t positions = d.n * d.t * d.h * d.w;
+  const int cp = (int)(d.c / 8);
+  const uint4* xp = reinterpret_cast<const uint4*>(x);
+  uint4* yp = reinterpret_cast<uint4*>(y);
+  const double e = (double)eps, c = (double)d.c;
+  // LPP = the power of two >= C/8 (8 .. 64), then PPL packets per lane past 64 lanes;
+  // per block: 4 waves x (64 / LPP positions) x U groups.
+  auto launch = [&](auto kernel, int64_t per_block) {
+    int64_t blocks = (positions + per_block - 1) / per_block;
+    const int resident = resident_blocks((const void*)kernel);
+    if (blocks > resident) blocks = resident;
+    kernel<<<dim3((unsigned)blocks), kThreads, 0, stream>>>(xp, yp, positions, cp, gain, e, c);
+  };
+  if (cp <= 8) launch(rms_silu_kernel<8, 1, 4>, 4 * 8 * 4);
+  else if (cp <= 16) launch(rms_silu_kernel<16, 1, 4>, 4 * 4 * 4);
+  else if (cp <= 32) launch(rms_silu_kernel<32, 1, 4>, 4 * 2 * 4);
+  else if (cp <= 64) launch(rms_silu_kernel<64, 1, 4>, 4 * 1 * 4);
+  else if (cp <= 128) launch(rms_silu_kernel<64, 2, 2>, 4 * 1 * 2);
+  else if (cp <= 256) launch(rms_silu_kernel<64, 4, 1>, 4);
+  else launch(rms_silu_kernel<64, 8, 1>, 4);
+  if (!launch_ok("rms_silu")) return SGN_ELAUNCH;
   return SGN_OK;
 }

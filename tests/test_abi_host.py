@@ -78,6 +78,20 @@ def test_apply_rejects():
     _err(lib.gn_silu_apply(FAKE, D(), 32, FAKE, FAKE, FAKE, 1e-5, FAKE + 4104, None), EALIGN)
 
 
+def test_rms_rejects():
+    lib = sga.load_library()
+    far = FAKE + (1 << 32)
+    _err(lib.rms_silu(FAKE, D(c=96), FAKE, 1e-6, far, None), EINVAL)          # C % 64
+    _err(lib.rms_silu(FAKE, D(c=8192), FAKE, 1e-6, far, None), EINVAL)        # C > 4096
+    _err(lib.rms_silu(FAKE, D(), None, 1e-6, far, None), EINVAL)
+    _err(lib.rms_silu(FAKE, D(), FAKE, 0.0, far, None), EINVAL)               # eps
+    _err(lib.rms_silu(FAKE, D(), FAKE, float("nan"), far, None), EINVAL)
+    _err(lib.rms_silu(FAKE + 8, D(), FAKE, 1e-6, far, None), EALIGN)
+    _err(lib.rms_silu(FAKE, D(), FAKE + 2, 1e-6, far, None), EALIGN)
+    _err(lib.rms_silu(FAKE, D(), FAKE, 1e-6, FAKE + 16, None), EALIAS)        # partial overlap
+    _err(lib.rms_silu(FAKE, D(t=0), FAKE, 1e-6, far, None), EINVAL)
+
+
 def test_conv_rejects():
     lib = sga.load_library()
     far = FAKE + (1 << 32)
