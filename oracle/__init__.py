@@ -24,10 +24,16 @@ FastVideo ``wan22_vae_decode/solution/binding.cpp``):
                     convolution in its direct form and, only to check the
                     identity, the four 2x2 phases (binding.cpp, prepare());
                     the output head with a 2x2 depth-to-space.
+* ``upblock``    -- the rest of an up block (binding.cpp, the seam after the resnets of
+                    blocks 0 and 1, and the resampler's last pass): the causal 3x1x1 time
+                    convolution writing two frames per input frame, the first pass's first
+                    frame passed through; the DupUp3D shortcut (channel repeat, then
+                    unfold to ft x fs x fs). Neither formula is printed on the pages; the
+                    module docstring states the readings.
 
 Every function is pinned by ``tests/test_oracle_*.py`` against brute force,
 closed forms, invariants or an independent library routine. Parity unpinned:
 agreement with the real Wan2.2 decoder (trained weights, real latents, the
 head's channel order), which needs data this repository does not have.
 """
-from . import bf16, groupnorm, conv  # noqa: F401
+from . import bf16, groupnorm, conv, rmsnorm, upblock  # noqa: F401
