@@ -181,6 +181,37 @@ def build_step(wl, dev, fused, separate_stats=False):
             "head_conv_d2s" + (" (fused GroupNorm+SiLU)" if fused else ""))
 
 
+def up_block_extras(wl, dev, iters):
+    """The up block's other steps at this workload's shape, each launched alone (HIP events):
+    latent: time_upsample_conv (3x1x1 causal conv C -> 2C, halves to frames, steady-state
+    pass with a cache); upsample: the phases with the DupUp3D shortcut of a block input of
+    x's shape (ft = 1) against the phases alone."""
+    if wl.kind == "latent":
+        x = wl.x(dev)
+        wt = sg.normal((2 * wl.c, 3, wl.c), wl.seed, sg.W_TIME, std=1 / math.sqrt(3 * wl.c), device=dev)
+        ci = wl.x_prev(dev)[:, -2:].contiguous()
+        y = torch.empty((wl.n, 2 * wl.t, wl.h, wl.w, wl.c), dtype=torch.bfloat16, device=dev)
+        ms = time_loop(lambda: sga.time_upsample_conv(x, wt, False, ci, y=y), iters)
+        fl = 2.0 * wl.n * wl.t * wl.h * wl.w * (2 * wl.c) * 3 * wl.c
+        tf = fl / (ms * 1e-3) / 1e12
+        return {"time_upsample": {"ms": round(ms, 4), "TFLOP/s": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
+                                  "frac": round(tf / PEAK_BF16_TFLOPS, 4), "flop_per_launch": fl,
+                                  "shape": "x %s -> y [%d,%d,%d,%d,%d] (K = %d)" % (
+                                      list(wl.shape), wl.n, 2 * wl.t, wl.h, wl.w, wl.c, 2 * wl.c)}}
+    if wl.kind == "upsample":
+        x = wl.x(dev)
+        src = sg.normal(wl.shape, wl.seed, sg.X_BLOCK, device=dev)
+        wp = sga.upsample2x_prepare_weights(wl.up_weight()).to(dev)
+        u = torch.empty((wl.n, wl.t, 2 * wl.h, 2 * wl.w, wl.c), dtype=torch.bfloat16, device=dev)
+        plain = time_loop(lambda: sga.upsample2x_conv_phases(x, wp, y=u), iters)
+        with_sc = time_loop(lambda: sga.upsample2x_conv_phases_shortcut(x, wp, src, 1, False, y=u), iters)
+        fl = conv_flops(wl.n, wl.t, wl.h, wl.w, wl.c, wl.c, taps=16)
+        return {"upsample_shortcut": {"ms": round(with_sc, 4), "ms_without_shortcut": round(plain, 4),
+                                      "TFLOP/s": round(fl / (with_sc * 1e-3) / 1e12, 2),
+                                      "shortcut": "DupUp3D of a %s block input, ft = 1" % list(wl.shape)}}
+    return {}
+
+
 def mark(timer, name):
     if timer is not None:
         timer.append((name, torch.cuda.Event(enable_timing=True)))
@@ -450,6 +481,7 @@ def main():
                     "bytes_per_element": 6},
         "stages_ms": {k: round(v, 4) for k, v in stages.items()},
     }
+    out.update(up_block_extras(wl, dev, iters))
     if rms_ms:
         rms_gbps = 4.0 * x.numel() / (rms_ms * 1e-3) / 1e9
         out["rms_silu"] = {"GB/s": round(rms_gbps, 1), "peak": PEAK_HBM_GBPS,

@@ -212,6 +212,56 @@ int upsample2x_conv_phases(const uint16_t* x, sgn_dims d, const uint16_t* w_phas
                            const float* bias, uint16_t* y, hipStream_t stream);
 
 /*
+ * upsample2x_conv_phases_shortcut -- upsample2x_conv_phases plus the DupUp3D
+ * shortcut of the up block's input, added before the one rounding.
+ * Defined by: binding.cpp page, Decoder::up_block (the resampler's last pass
+ * interleaves the four phases and adds the bias and the DupUp3D shortcut of the
+ * block's input). The pages do not print DupUp3D; the reading used:
+ *
+ *   y[n,f,Y,X,k] = RNE_bf16( phases + bias[k]
+ *        + sc[n, tt / ft, Y / 2, X / 2, (k F + o) / rep] ),
+ *   tt = f + first (ft - 1), o = ((tt % ft) 2 + Y % 2) 2 + X % 2,
+ *   F = 4 ft, rep = K F / C_in,
+ * i.e. every input channel repeated rep times, read as (k, time, row, column)
+ * sub-positions and unfolded ft x 2 x 2; on the video's first pass the first
+ * ft - 1 output frames are dropped.
+ *   shortcut  bf16 (N, T_in, H, W, C_in) with the phases' N, H, W, and
+ *             T = ft T_in - first (ft - 1) (x's T); C_in = K or 2K
+ *   ft        1 or 2 (the block upsamples time too); first 0 or 1
+ * Requires K % 8 == 0 as well as upsample2x_conv_phases' shapes; y must not overlap
+ * the shortcut (SGN_EALIAS). Other shapes are SGN_EINVAL.
+ */
+int upsample2x_conv_phases_shortcut(const uint16_t* x, sgn_dims d, const uint16_t* w_phase, int k,
+                                    const float* bias, const uint16_t* shortcut, sgn_dims sd,
+                                    int ft, int first, uint16_t* y, hipStream_t stream);
+
+/*
+ * time_upsample_conv -- temporal x2 of an up block: a causal 3x1x1 convolution to
+ * 2C channels whose two halves become two consecutive output frames.
+ * Defined by: binding.cpp page, Decoder::up_block, the seam after the resnets of
+ * blocks 0 and 1 (time_upsample: the causal time convolution with its own 2-frame
+ * cache and no normalisation writes the frame-interleaved tensor directly; on the
+ * video's first pass the first frame is not convolved and goes straight to the
+ * output). The layout of the halves is a reading:
+ *
+ *   nf = T - first,  P = cat_T(cache_in, x[:, first:])   (cache_in NULL: zeros)
+ *   z[n,i,h,w,k] = bias[k] + sum_{dt in 0..2} sum_c w[k,dt,c] * P[n, i+dt, h, w, c]
+ *   y[n, first + 2i + s, h, w, c] = RNE_bf16( z[n,i,h,w, s C + c] ),  s = 0, 1
+ *   y[n, 0] = x[n, 0] when first (bit copy)
+ * bf16 products accumulated in fp32.
+ *   x         bf16 (N,T,H,W,C), T >= 1 (T = 1 with first: only the copied frame)
+ *   cache_in  bf16 (N,2,H,W,C) or NULL; w bf16 (2C,3,C), dt = 0 the oldest frame
+ *   bias      fp32 [2C] or NULL
+ *   y         bf16 (N, first + 2 nf, H, W, C)
+ *   cache_out bf16 (N,2,H,W,C) = P[:, nf:nf+2], or NULL
+ * Requires C % 64 == 0 with C <= 2048. Outputs must not overlap the inputs or
+ * each other (SGN_EALIAS); other shapes are SGN_EINVAL.
+ */
+int time_upsample_conv(const uint16_t* x, sgn_dims d, const uint16_t* cache_in,
+                       const uint16_t* w, const float* bias, int first, uint16_t* y,
+                       uint16_t* cache_out, hipStream_t stream);
+
+/*
  * head_conv_d2s -- the decoder's output head: causal 3x3x3 convolution to 12
  * channels followed by a 2x2 depth-to-space into an RGB video.
  * Defined by: binding.cpp page, Decoder::output_head (norm + SiLU + causal pad,

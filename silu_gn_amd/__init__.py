@@ -37,7 +37,8 @@ class sgn_gn(ctypes.Structure):
 
 EXPORTS = ["sgn_last_error", "gn_silu_stats_workspace", "gn_silu_stats", "gn_silu_apply", "rms_silu",
            "causal_conv3d", "causal_conv3d_next_stats_workspace", "causal_conv3d_next_stats",
-           "upsample2x_prepare_weights", "upsample2x_conv_phases", "head_conv_d2s"]
+           "upsample2x_prepare_weights", "upsample2x_conv_phases", "upsample2x_conv_phases_shortcut",
+           "time_upsample_conv", "head_conv_d2s"]
 
 _lib = None
 
@@ -64,6 +65,8 @@ def load_library(path: str = LIB_PATH):
                                            sz, vp]),
         "upsample2x_prepare_weights": (i32, [vp, i32, i32, vp]),
         "upsample2x_conv_phases": (i32, [vp, sgn_dims, vp, i32, vp, vp, vp]),
+        "upsample2x_conv_phases_shortcut": (i32, [vp, sgn_dims, vp, i32, vp, vp, sgn_dims, i32, i32, vp, vp]),
+        "time_upsample_conv": (i32, [vp, sgn_dims, vp, vp, vp, i32, vp, vp, vp]),
         "head_conv_d2s": (i32, [vp, sgn_dims, vp, vp, vp, gnp, i32, vp, vp, vp]),
     }
     for name, (res, args) in sigs.items():
@@ -195,6 +198,30 @@ def upsample2x_conv_phases(x, w_phase, bias=None, y=None):
     if y is None:
         y = torch.empty((n, t, 2 * h, 2 * wd, k), dtype=torch.bfloat16, device=x.device)
     _check(lib.upsample2x_conv_phases(_ptr(x), _dims(x), _ptr(w_phase), k, _ptr(bias), _ptr(y), _stream(x)))
+    return y
+
+
+def upsample2x_conv_phases_shortcut(x, w_phase, shortcut, ft: int, first: bool, bias=None, y=None):
+    """upsample2x_conv_phases plus the DupUp3D shortcut of ``shortcut`` (the block input)."""
+    lib = load_library()
+    k = w_phase.shape[2]
+    n, t, h, wd, _ = x.shape
+    if y is None:
+        y = torch.empty((n, t, 2 * h, 2 * wd, k), dtype=torch.bfloat16, device=x.device)
+    _check(lib.upsample2x_conv_phases_shortcut(_ptr(x), _dims(x), _ptr(w_phase), k, _ptr(bias), _ptr(shortcut),
+                                               _dims(shortcut), int(ft), int(bool(first)), _ptr(y), _stream(x)))
+    return y
+
+
+def time_upsample_conv(x, w, first: bool, cache_in=None, bias=None, y=None, cache_out=None):
+    """Temporal x2: causal 3x1x1 conv to 2C channels, halves to frames; y (N, first + 2 (T - first), H, W, C)."""
+    lib = load_library()
+    n, t, h, wd, c = x.shape
+    first = int(bool(first))
+    if y is None:
+        y = torch.empty((n, first + 2 * (t - first), h, wd, c), dtype=torch.bfloat16, device=x.device)
+    _check(lib.time_upsample_conv(_ptr(x), _dims(x), _ptr(cache_in), _ptr(w), _ptr(bias), first, _ptr(y),
+                                  _ptr(cache_out), _stream(x)))
     return y
 
 

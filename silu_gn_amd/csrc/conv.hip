@@ -38,7 +38,7 @@ struct IC {
   static constexpr int value = V;
 };
 
-enum Mode { kCausal = 0, kPhase = 1, kHead = 2 };
+enum Mode { kCausal = 0, kPhase = 1, kHead = 2, kTime = 3 };
 
 struct ConvParams {
   const uint16_t* x;
@@ -61,6 +61,15 @@ struct ConvParams {
   // partial sums S, Q of every (sample, group, tile) in the layout gn_stats_finalize reads.
   double* nws;
   int ngroups, ncg;          // groups over K, channels per group (a multiple of 8 dividing BN)
+  // Temporal x2 (kTime): x holds Tx frames per sample and the convolution reads them from
+  // frame x0 on; y holds To frames per sample, and output frame first + 2 t + s takes
+  // channels s K/2 .. (s + 1) K/2 - 1 of the convolution's frame t.
+  int Tx, x0, To, first;
+  // DupUp3D shortcut added by the phase epilogue, or sc == null: the block input, sc_T
+  // frames of sc_C channels per sample at the phase convolution's H x W; time factor sc_ft,
+  // sc_first = the first ft - 1 output frames are dropped.
+  const uint16_t* sc;
+  int sc_T, sc_C, sc_ft, sc_first;
 };
 
 
@@ -209,7 +218,7 @@ template <int MODE, int TN, int TM, int WTM, int WTN>
 __device__ __forceinline__ Sums store_tile_staged(const f32x16 (&acc)[TN][TM], const ConvParams& p, int n,
                                                   int t, int pos0, int kbase, int wm, int lane,
                                                   int phase, const float* lbias, char* stage) {
-  static_assert(MODE == kCausal || MODE == kPhase, "staged epilogue modes");
+  static_assert(MODE == kCausal || MODE == kPhase || MODE == kTime, "staged epilogue modes");
   constexpr int ROW = WTN * 4;                       // staging row bytes
   constexpr int LPR = WTN / 8;                       // lanes per row on the way out
   constexpr int RPI = 64 / LPR;                      // rows per instruction
@@ -221,16 +230,40 @@ __device__ __forceinline__ Sums store_tile_staged(const f32x16 (&acc)[TN][TM], c
   const int pa = phase >> 1, pb = phase & 1;
   const int g = lane % LPR;                          // 8-channel group of this lane
   const int k0 = kbase + 8 * g;
-  // The tile's frame of y: HW positions (causal) or 2H x 2W (phases), K channels each.
-  const int64_t fpos = MODE == kCausal ? (int64_t)HW : 4 * (int64_t)HW;
+  // The tile's span of y: one frame of HW positions (causal) or 2H x 2W (phases), K channels
+  // each; for the temporal x2 the two output frames first + 2t, first + 2t + 1 of K / 2
+  // channels (same bytes), channel k0 going to the second when k0 >= K / 2.
+  const int64_t fpos = MODE == kPhase ? 4 * (int64_t)HW : (int64_t)HW;
   const int64_t fidx = (int64_t)n * T + t;
-  const Rsrc ys = make_rsrc(p.y + fidx * fpos * K, (uint32_t)(fpos * K * 2));
+  const int KH = K / 2;
+  const int sub = MODE == kTime && k0 >= KH ? 1 : 0;
+  const int64_t ybase = MODE == kTime ? ((int64_t)n * p.To + p.first + 2 * t) * HW * KH : fidx * fpos * K;
+  const Rsrc ys = make_rsrc(p.y + ybase, (uint32_t)(fpos * K * 2));
   const bool kfull = kbase + WTN <= K;               // wave-uniform: no channel tail
   auto out_off = [&](int ml) -> uint32_t {           // ml: position within the frame
     if (MODE == kCausal) return (uint32_t)(((int64_t)ml * K + k0) * 2);
+    if (MODE == kTime)                               // past the frame: dropped (not the next frame)
+      return ml < HW ? (uint32_t)((((int64_t)sub * HW + ml) * KH + k0 - sub * KH) * 2) : kOOB;
     const int h_ = ml / W, w_ = ml - h_ * W;
     return (uint32_t)(((((int64_t)(2 * h_ + pa)) * (2 * W) + 2 * w_ + pb) * K + k0) * 2);
   };
+  // DupUp3D shortcut (phases): output channel c of phase (pa, pb) in output frame t reads
+  // source channel (c F + o) / rep of frame (t + first (ft - 1)) / ft, with F = 4 ft,
+  // o = (a 2 + pa) 2 + pb, a = (t + first (ft - 1)) % ft and rep = K F / Cs. The host admits
+  // Cs = K (source channel c) and Cs = 2K (source channel 2c + o / rep): a lane's 8 output
+  // channels read 16 or 32 contiguous source bytes. Uniform per tile.
+  const bool shortcut = MODE == kPhase && p.sc != nullptr;
+  Rsrc scs = make_rsrc(p.y, 0);
+  int sc_step = 1, sc_e = 0;
+  if (shortcut) {
+    const int tt = t + p.sc_first * (p.sc_ft - 1);
+    const int tsrc = tt / p.sc_ft, a = tt - tsrc * p.sc_ft;
+    const int F = 4 * p.sc_ft;
+    const int rep = K * F / p.sc_C;
+    sc_step = p.sc_C / K;
+    sc_e = ((a * 2 + pa) * 2 + pb) / rep;
+    scs = make_rsrc(p.sc + ((int64_t)n * p.sc_T + tsrc) * HW * p.sc_C, (uint32_t)((int64_t)HW * p.sc_C * 2));
+  }
   // Statistics for the next GroupNorm: this lane's stored values and their exact squares.
   const bool stats = MODE == kCausal && p.nws != nullptr;
   double ss = 0.0, sq = 0.0;
@@ -251,6 +284,17 @@ __device__ __forceinline__ Sums store_tile_staged(const f32x16 (&acc)[TN][TM], c
   stage_barrier();                                   // every wave is done with the operand stages
 #pragma unroll
   for (int j = 0; j < TM; ++j) {
+    // Shortcut rows of this fragment row block, issued before its staging writes.
+    u32x4 sv[MODE == kPhase ? NI : 1][2];
+    if (shortcut) {
+#pragma unroll
+      for (int it = 0; it < NI; ++it) {
+        const int ml = pos0 + wm * WTM + 32 * j + it * RPI + lane / LPR;
+        const uint32_t so = (uint32_t)(((int64_t)ml * p.sc_C + k0 * sc_step) * 2);
+        sv[MODE == kPhase ? it : 0][0] = __builtin_amdgcn_raw_buffer_load_b128(scs, so, 0, 0);
+        if (sc_step == 2) sv[MODE == kPhase ? it : 0][1] = __builtin_amdgcn_raw_buffer_load_b128(scs, so + 16, 0, 0);
+      }
+    }
     {
       const int r = lane & 31;
 #pragma unroll
@@ -282,6 +326,23 @@ __device__ __forceinline__ Sums store_tile_staged(const f32x16 (&acc)[TN][TM], c
           v[2 * e + 1] += bf16_hi(rr[e]);
         }
       }
+      if (shortcut) {
+        const u32x4 s0 = sv[MODE == kPhase ? it : 0][0];
+        if (sc_step == 1) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            v[2 * e] += bf16_lo(s0[e]);
+            v[2 * e + 1] += bf16_hi(s0[e]);
+          }
+        } else {                                     // source channels 2c + sc_e
+          const u32x4 s1 = sv[MODE == kPhase ? it : 0][1];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            v[e] += sc_e ? bf16_hi(s0[e]) : bf16_lo(s0[e]);
+            v[4 + e] += sc_e ? bf16_hi(s1[e]) : bf16_lo(s1[e]);
+          }
+        }
+      }
       u32x4 o;
 #pragma unroll
       for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(v[2 * e], v[2 * e + 1]);
@@ -299,7 +360,7 @@ __device__ __forceinline__ Sums store_tile_staged(const f32x16 (&acc)[TN][TM], c
       if (kfull) {
         __builtin_amdgcn_raw_buffer_store_b128(o, ys, out_off(ml), 0, 0);   // past the frame: dropped
       } else if (k0 < K && ml < HW) {
-        uint16_t* dst = p.y + fidx * fpos * K + out_off(ml) / 2;
+        uint16_t* dst = p.y + ybase + out_off(ml) / 2;
         if (k0 + 8 <= K)
           *reinterpret_cast<uint4*>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
         else
@@ -365,12 +426,13 @@ struct BiasStage {
   }
 };
 
-// cache_out = the last 2 frames of P = cat(cache_in, a); frames of x are activated when
-// fused (same per-thread column layout and activate_packet as gn_silu_apply).
+// cache_out = the last 2 frames of P = cat(cache_in, a), a = frames x0 .. x0 + T - 1 of the
+// Tx frames per sample of x; frames of x are activated when fused (same per-thread column
+// layout and activate_packet as gn_silu_apply).
 __global__ __launch_bounds__(256) void cache_out_kernel(
-    const uint4* x, const uint4* cache_in, uint4* cache_out, int T, int64_t hw, int cp, int rstep,
-    int64_t rows_per_block, const double* stats, const float* gamma, const float* beta, double eps,
-    int groups) {
+    const uint4* x, const uint4* cache_in, uint4* cache_out, int T, int Tx, int x0, int64_t hw, int cp,
+    int rstep, int64_t rows_per_block, const double* stats, const float* gamma, const float* beta,
+    double eps, int groups) {
   const int tid = threadIdx.x, n = blockIdx.y;
   if (tid >= rstep * cp) return;
   const int col = tid % cp;
@@ -390,7 +452,7 @@ __global__ __launch_bounds__(256) void cache_out_kernel(
     const int pf = T + f;                            // frame of P = cat(cache_in, x)
     uint4 v;
     if (pf >= 2) {
-      v = x[(((int64_t)n * T + pf - 2) * hw + s) * cp + col];
+      v = x[(((int64_t)n * Tx + x0 + pf - 2) * hw + s) * cp + col];
       if (stats) v = activate_packet(v, a);
     } else if (cache_in) {
       v = cache_in[(((int64_t)n * 2 + pf) * hw + s) * cp + col];
@@ -399,6 +461,15 @@ __global__ __launch_bounds__(256) void cache_out_kernel(
     }
     cache_out[(((int64_t)n * 2 + f) * hw + s) * cp + col] = v;
   }
+}
+
+// y[n, 0] = x[n, 0] for every sample n (packets of 8 channels per frame; xs, ys: packets
+// per sample of x and y): the frame the temporal x2 passes through on the first pass.
+__global__ __launch_bounds__(256) void copy_first_frame_kernel(const uint4* __restrict__ x, uint4* __restrict__ y,
+                                                              int64_t packets, int64_t xs, int64_t ys) {
+  const int64_t n = blockIdx.y;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < packets; i += (int64_t)gridDim.x * 256)
+    y[n * ys + i] = x[n * xs + i];
 }
 
 // ---------------------------------------------------------------- the convolution kernel
@@ -449,12 +520,13 @@ __device__ __forceinline__ uint4 load16(Rsrc r, uint32_t voff, uint32_t soff) {
 template <int BM, int BN, int WGM, int WGN, int NS, int MODE, bool FUSE>
 __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_kernel(ConvParams p) {
   constexpr int NW = WGM * WGN;
-  constexpr int TAPS = MODE == kPhase ? 4 : 27;
-  constexpr int INNER = MODE == kPhase ? 1 : 3;      // taps sharing a channel chunk in a row
+  constexpr int TAPS = MODE == kPhase ? 4 : MODE == kTime ? 3 : 27;
+  constexpr int INNER = MODE == kCausal || MODE == kHead ? 3 : 1;   // taps sharing a channel chunk in a row
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
   constexpr int TM = WTM / 32, TN = WTN / 32;
   static_assert(TM * 32 * WGM == BM && TN * 32 * WGN == BN, "tile shape");
   static_assert(BM % 16 == 0 && BN % 16 == 0 && NS >= 4, "pipeline shape");
+  static_assert(MODE != kTime || !FUSE, "the temporal x2 reads its input as it is");
   constexpr int ROWB = kPK * 2;                      // bytes per LDS row
   constexpr int STAGE = (BN + BM) * ROWB;
   constexpr int IA = BN / 16, IB = BM / 16;          // 1 KB moves (16 rows) per stage
@@ -532,6 +604,10 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_kernel(ConvParams p) {
       dt = 2;
       dh = (tap >> 1) + pa;                          // row offset u + a - 1, stored +1
       dw = (tap & 1) + pb;
+    } else if (MODE == kTime) {
+      dt = tap;                                      // 3 x 1 x 1: the same position
+      dh = 1;
+      dw = 1;
     } else {
       dt = tap / 9;
       dh = (tap / 3) % 3;
@@ -540,7 +616,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_kernel(ConvParams p) {
     const int tf = t + dt - 2;
     from_x = tf >= 0;
     if (tf >= 0)
-      prs = make_rsrc(p.x + ((int64_t)n * T + tf) * HW * C, frame_bytes);
+      prs = make_rsrc(p.x + (MODE == kTime ? (int64_t)n * p.Tx + p.x0 + tf : (int64_t)n * T + tf) * HW * C,
+                      frame_bytes);
     else if (p.cache)
       prs = make_rsrc(p.cache + ((int64_t)n * 2 + tf + 2) * HW * C, frame_bytes);
     else
@@ -767,7 +844,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_kernel(ConvParams p) {
     if (MODE == kCausal && p.nws)
       next_stats_partials<NW, WGM, WTN, BN>(p, n, t, mt, ntile, wave, lane, sums,
                                             reinterpret_cast<double*>(smem + NW * 32 * WTN * 4));
-  } else {
+  } else if constexpr (MODE != kTime) {               // the temporal x2 needs K % 16 == 0
     store_tile<MODE, TN, TM, WTM, WTN>(acc, p, n, (int64_t)t * HW + mt * BM, (int64_t)(t + 1) * HW,
                                        ntile * BN + wn * WTN, wm, lane, phase, lbias + wn * WTN);
   }
@@ -1512,8 +1589,9 @@ static bool launch_conv(const TileCfg& cfg, ConvParams& p, int64_t n_samples, in
   return launch_ok(fn);
 }
 
+// cache_out of a causal convolution over frames x0 .. x0 + T - 1 (T = d.t - x0) of x.
 static bool launch_cache_out(const uint16_t* x, sgn_dims d, const uint16_t* cache_in,
-                             const sgn_gn* fuse, uint16_t* cache_out, hipStream_t stream) {
+                             const sgn_gn* fuse, uint16_t* cache_out, hipStream_t stream, int x0 = 0) {
   const int cp = (int)(d.c / 8);
   int rstep = 256 / cp;
   if (rstep < 1) rstep = 1;
@@ -1526,7 +1604,7 @@ static bool launch_cache_out(const uint16_t* x, sgn_dims d, const uint16_t* cach
   blocks = (positions + rows - 1) / rows;
   cache_out_kernel<<<dim3((unsigned)blocks, (unsigned)d.n), 256, 0, stream>>>(
       reinterpret_cast<const uint4*>(x), reinterpret_cast<const uint4*>(cache_in),
-      reinterpret_cast<uint4*>(cache_out), (int)d.t, hw, cp, rstep, rows,
+      reinterpret_cast<uint4*>(cache_out), (int)d.t - x0, (int)d.t, x0, hw, cp, rstep, rows,
       fuse ? fuse->stats : nullptr, fuse ? fuse->gamma : nullptr, fuse ? fuse->beta : nullptr,
       fuse ? (double)fuse->eps : 0.0, fuse ? fuse->groups : 1);
   return launch_ok("cache_out");
@@ -1751,10 +1829,17 @@ extern "C" int causal_conv3d_next_stats(const uint16_t* x, sgn_dims d, const uin
   return causal_conv_impl(fn, x, d, cache_in, w, k, bias, residual, fuse, y, cache_out, &ns, stream);
 }
 
-extern "C" int upsample2x_conv_phases(const uint16_t* x, sgn_dims d, const uint16_t* w_phase, int k,
-                                      const float* bias, uint16_t* y, hipStream_t stream) {
-  const char* fn = "upsample2x_conv_phases";
-  clear_error();
+namespace sgn {
+
+// The DupUp3D shortcut of upsample2x_conv_phases_shortcut: the up block's input.
+struct Shortcut {
+  const uint16_t* src;
+  sgn_dims d;
+  int ft, first;
+};
+
+static int upsample_impl(const char* fn, const uint16_t* x, sgn_dims d, const uint16_t* w_phase, int k,
+                         const float* bias, const Shortcut* sc, uint16_t* y, hipStream_t stream) {
   if (!conv_common_checks(x, d, w_phase, k, y, fn)) return SGN_EINVAL;
   if (!aligned16(x) || !aligned16(w_phase) || !aligned16(y) || (bias && !aligned16(bias))) {
     set_error("%s: tensors (and bias) must be 16-byte aligned", fn);
@@ -1768,6 +1853,43 @@ extern "C" int upsample2x_conv_phases(const uint16_t* x, sgn_dims d, const uint1
     return SGN_EALIAS;
   }
   ConvParams p = {};
+  if (sc) {
+    const sgn_dims& s = sc->d;
+    if (!sc->src || !dims_ok(s, fn)) {
+      if (!sc->src) set_error("%s: the shortcut source is required", fn);
+      return SGN_EINVAL;
+    }
+    if ((sc->ft != 1 && sc->ft != 2) || (sc->first != 0 && sc->first != 1)) {
+      set_error("%s: ft must be 1 or 2 and first 0 or 1", fn);
+      return SGN_EINVAL;
+    }
+    if (s.n != d.n || s.h != d.h || s.w != d.w || d.t != sc->ft * s.t - sc->first * (sc->ft - 1)) {
+      set_error("%s: the shortcut source (N=%lld, T=%lld, H=%lld, W=%lld) does not match x under ft=%d, first=%d",
+                fn, (long long)s.n, (long long)s.t, (long long)s.h, (long long)s.w, sc->ft, sc->first);
+      return SGN_EINVAL;
+    }
+    if (k % 8 != 0 || (s.c != k && s.c != 2 * (int64_t)k)) {
+      set_error("%s: the shortcut needs K %% 8 == 0 and C_in = K or 2K (K=%d, C_in=%lld)", fn, k, (long long)s.c);
+      return SGN_EINVAL;
+    }
+    if ((s.h * s.w + 256) * s.c * 2 >= ((int64_t)1 << 31)) {
+      set_error("%s: a shortcut frame exceeds the 2 GiB frame limit", fn);
+      return SGN_EINVAL;
+    }
+    if (!aligned16(sc->src)) {
+      set_error("%s: the shortcut source must be 16-byte aligned", fn);
+      return SGN_EALIGN;
+    }
+    if (overlap(y, yb, sc->src, (size_t)(s.n * s.t * s.h * s.w * s.c) * 2)) {
+      set_error("%s: y overlaps the shortcut source", fn);
+      return SGN_EALIAS;
+    }
+    p.sc = sc->src;
+    p.sc_T = (int)s.t;
+    p.sc_C = (int)s.c;
+    p.sc_ft = sc->ft;
+    p.sc_first = sc->first;
+  }
   p.x = x;
   p.w = w_phase;
   p.bias = bias;
@@ -1780,6 +1902,88 @@ extern "C" int upsample2x_conv_phases(const uint16_t* x, sgn_dims d, const uint1
   p.mper = d.t * d.h * d.w;
   const TileCfg cfg = choose_tile<kPhase, false>(d.h * d.w, d.t, k, p.C, d.n * 4);
   if (!launch_conv(cfg, p, d.n, 4, stream, fn)) return SGN_ELAUNCH;
+  return SGN_OK;
+}
+
+}  // namespace sgn
+
+extern "C" int upsample2x_conv_phases(const uint16_t* x, sgn_dims d, const uint16_t* w_phase, int k,
+                                      const float* bias, uint16_t* y, hipStream_t stream) {
+  clear_error();
+  return upsample_impl("upsample2x_conv_phases", x, d, w_phase, k, bias, nullptr, y, stream);
+}
+
+extern "C" int upsample2x_conv_phases_shortcut(const uint16_t* x, sgn_dims d, const uint16_t* w_phase, int k,
+                                               const float* bias, const uint16_t* shortcut, sgn_dims sd, int ft,
+                                               int first, uint16_t* y, hipStream_t stream) {
+  clear_error();
+  const Shortcut sc = {shortcut, sd, ft, first};
+  return upsample_impl("upsample2x_conv_phases_shortcut", x, d, w_phase, k, bias, &sc, y, stream);
+}
+
+extern "C" int time_upsample_conv(const uint16_t* x, sgn_dims d, const uint16_t* cache_in, const uint16_t* w,
+                                  const float* bias, int first, uint16_t* y, uint16_t* cache_out,
+                                  hipStream_t stream) {
+  const char* fn = "time_upsample_conv";
+  clear_error();
+  if (first != 0 && first != 1) {
+    set_error("%s: first must be 0 or 1", fn);
+    return SGN_EINVAL;
+  }
+  if (!dims_ok(d, fn)) return SGN_EINVAL;
+  if (d.c > 2048) {
+    set_error("%s: C=%lld must be at most 2048 (2C output channels)", fn, (long long)d.c);
+    return SGN_EINVAL;
+  }
+  const int k = 2 * (int)d.c;
+  if (!conv_common_checks(x, d, w, k, y, fn)) return SGN_EINVAL;
+  if (!aligned16(x) || !aligned16(w) || !aligned16(y) || (cache_in && !aligned16(cache_in)) ||
+      (cache_out && !aligned16(cache_out)) || (bias && !aligned16(bias))) {
+    set_error("%s: tensors (and bias) must be 16-byte aligned", fn);
+    return SGN_EALIGN;
+  }
+  const int64_t hw = d.h * d.w;
+  const int64_t nf = d.t - first;
+  const int64_t to = first + 2 * nf;
+  const size_t xb = (size_t)(d.n * d.t * hw * d.c) * 2;
+  const size_t yb = (size_t)(d.n * to * hw * d.c) * 2;
+  const size_t cb = (size_t)(d.n * 2 * hw * d.c) * 2;
+  const size_t wb = (size_t)k * 3 * d.c * 2;
+  if (overlap(y, yb, x, xb) || overlap(y, yb, w, wb) || (cache_in && overlap(y, yb, cache_in, cb)) ||
+      (cache_out && (overlap(cache_out, cb, x, xb) || overlap(cache_out, cb, y, yb) ||
+                     overlap(cache_out, cb, w, wb) || (cache_in && overlap(cache_out, cb, cache_in, cb))))) {
+    set_error("%s: an output overlaps an input or the other output", fn);
+    return SGN_EALIAS;
+  }
+  if (nf > 0) {
+    ConvParams p = {};
+    p.x = x;
+    p.cache = cache_in;
+    p.w = w;
+    p.bias = bias;
+    p.y = y;
+    p.T = (int)nf;
+    p.H = (int)d.h;
+    p.W = (int)d.w;
+    p.C = (int)d.c;
+    p.K = k;
+    p.mper = nf * hw;
+    p.Tx = (int)d.t;
+    p.x0 = first;
+    p.To = (int)to;
+    p.first = first;
+    const TileCfg cfg = choose_tile<kTime, false>(hw, nf, k, p.C, d.n);
+    if (!launch_conv(cfg, p, d.n, 1, stream, fn)) return SGN_ELAUNCH;
+  }
+  if (first) {
+    const int64_t packets = hw * d.c / 8;
+    int64_t blocks = (packets + 255) / 256;
+    if (blocks > 1024) blocks = 1024;
+    copy_first_frame_kernel<<<dim3((unsigned)blocks, (unsigned)d.n), 256, 0, stream>>>(
+        reinterpret_cast<const uint4*>(x), reinterpret_cast<uint4*>(y), packets, d.t * packets, to * packets);
+    if (!launch_ok(fn)) return SGN_ELAUNCH;
+  }
+  if (cache_out && !launch_cache_out(x, d, cache_in, nullptr, cache_out, stream, first)) return SGN_ELAUNCH;
   return SGN_OK;
 }
 

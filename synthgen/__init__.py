@@ -116,3 +116,4 @@ def uniform(shape, seed: int, tensor_id: int, lo: float, hi: float,
 
 # Tensor ids within one configuration's seed.
 X, GAMMA1, BETA1, W1, X_PREV, OFFSETS, GAMMA2, BETA2, W2, W_UP = range(10)
+W_TIME, X_BLOCK = 10, 11          # the temporal x2's weight; an up block's input (its shortcut source)

@@ -148,6 +148,39 @@ def test_upsample_and_head_reject():
     _err(lib.head_conv_d2s(FAKE, D(), None, FAKE + (1 << 30), None, None, 0, FAKE + 256, None, None), EALIAS)
 
 
+def test_time_upsample_rejects():
+    lib = sga.load_library()
+    far = FAKE + (1 << 32)
+    w = FAKE + (1 << 30)
+    _err(lib.time_upsample_conv(FAKE, D(), None, w, None, 2, far, None, None), EINVAL)           # first
+    _err(lib.time_upsample_conv(FAKE, D(c=96), None, w, None, 0, far, None, None), EINVAL)       # C % 64
+    _err(lib.time_upsample_conv(FAKE, D(c=4096), None, w, None, 0, far, None, None), EINVAL)     # 2C > 4096
+    _err(lib.time_upsample_conv(FAKE, D(), None, None, None, 0, far, None, None), EINVAL)
+    _err(lib.time_upsample_conv(FAKE, D(), None, w, None, 0, far + 8, None, None), EALIGN)
+    _err(lib.time_upsample_conv(FAKE, D(), None, w, None, 0, FAKE + 64, None, None), EALIAS)     # y inside x
+    _err(lib.time_upsample_conv(FAKE, D(), None, w, None, 1, far, far + 64, None), EALIAS)       # cache_out in y
+
+
+def test_upsample_shortcut_rejects():
+    lib = sga.load_library()
+    far = FAKE + (1 << 32)
+    w = FAKE + (1 << 30)
+    src = FAKE + (1 << 34)
+
+    def call(d=D(t=3), k=64, sd=D(t=2), ft=2, first=1, sc=src, y=far):
+        return lib.upsample2x_conv_phases_shortcut(FAKE, d, w, k, None, sc, sd, ft, first, y, None)
+    _err(call(sc=None), EINVAL)
+    _err(call(ft=3), EINVAL)
+    _err(call(first=2), EINVAL)
+    _err(call(sd=D(t=3)), EINVAL)                   # T = ft T_in - first (ft - 1) = 3 needs T_in = 2
+    _err(call(sd=sga.sgn_dims(1, 2, 5, 4, 64)), EINVAL)   # H differs
+    _err(call(sd=D(t=2, c=96)), EINVAL)             # C_in must be K or 2K
+    _err(call(k=60, sd=D(t=2, c=60)), EINVAL)       # K % 8
+    _err(call(sc=src + 8), EALIGN)
+    _err(call(y=src + 64), EALIAS)                  # y overlaps the shortcut source
+    _err(call(d=D(t=2), sd=D(t=2), ft=1, first=0, y=FAKE + 32), EALIAS)   # the phases' own checks
+
+
 @pytest.mark.parametrize("k,c", [(4, 8), (16, 64)])
 def test_prepare_phase_weights_matches_oracle(k, c):
     w = torch.randn(k, 3, 3, c, generator=torch.Generator().manual_seed(k + c)).to(torch.bfloat16)
