@@ -1287,8 +1287,13 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_slab_kernel(ConvParams
 //   complete after input frame t + 2.
 // - A unit of work is (input frame, input row h + dh - 1, the wave's chunk). Its 50 input
 //   columns w0 - 1 .. w0 + 48 (64-byte rows) move global -> LDS with buffer_load ... lds
-//   into the wave's own ring of kHeadRing units, two units ahead; each wave waits only for
-//   its own moves (counted vmcnt), so the ring needs no barrier.
+//   into the wave's own ring of 3 units, two units ahead; each wave waits only for its own
+//   moves (counted vmcnt), so the ring needs no barrier.
+// - With two waves per SIMD and one instruction per wave per issue cycle, the kernel is
+//   bound by instruction issue as much as by the matrix pipe: the loop over a group of 3
+//   frames is unrolled so that a unit's ring slot, row tap and accumulator slots are
+//   constants, every LDS read is a per-lane base (one per column tap) plus an immediate,
+//   and the frame descriptors are built once per group.
 // - The B operand of a column tap dw is the 16-row LDS window starting at row 16 s + dw:
 //   one input row staged once serves all 3 column taps and, through the frame ring, all 3
 //   frame taps (9 MFMAs per window set). The 16-byte chunks of row r sit at chunk
@@ -1301,7 +1306,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_slab_kernel(ConvParams
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 constexpr int kHeadSeg = 3;              // 16-column segments per workgroup (W = 624: 13 blocks)
 constexpr int kHeadRows = 64;            // LDS rows per unit (50 used: 48 columns + 2 edges)
-constexpr int kHeadRing = 3;             // units per wave in LDS
+constexpr int kHeadRing = 3;             // units per wave in LDS (u % 3 = the unit's row tap)
 
 
 template <int NW>
@@ -1318,16 +1323,19 @@ __global__ __launch_bounds__(64 * NW, 1) void head_kernel(ConvParams p, int wblo
   f32x4* red = reinterpret_cast<f32x4*>(smem + NW * kHeadRing * UNIT);   // [2][NW][seg][64]
   float* sbias = reinterpret_cast<float*>(red + 2 * NW * kHeadSeg * 64);
 
-  // Workgroup -> (n, h, column block), XCD-aware: each XCD takes a contiguous run, so the
-  // workgroups of neighbouring rows -- which read the same input rows -- share its L2.
+  // Workgroup -> (n, column block, h), rows fastest and XCD-aware: each XCD takes a
+  // contiguous run, so the workgroups it runs at once are consecutive rows of one column
+  // block, and each input row -- read by the workgroups of 3 neighbouring rows -- comes
+  // from HBM about once (with columns fastest, the third reader of a row started only after
+  // the first had finished, and the row was read again).
   int blk;
   {
     const int bid = blockIdx.x, nb = p.nblocks;
     const int xcd = bid & 7, idx = bid >> 3, q = nb >> 3, r = nb & 7;
     blk = xcd < r ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
   }
-  const int wb = blk % wblocks;
-  const int h = (blk / wblocks) % H;
+  const int h = blk % H;
+  const int wb = (blk / H) % wblocks;
   const int n = blk / (wblocks * H);
   const int w0 = wb * (16 * kHeadSeg);
 
@@ -1370,66 +1378,80 @@ __global__ __launch_bounds__(64 * NW, 1) void head_kernel(ConvParams p, int wblo
     if (pf < 2 && p.cache) return make_rsrc(p.cache + ((int64_t)n * 2 + pf) * HW * C, frame_bytes);
     return make_rsrc(p.x, 0);
   };
-  // Units in order u = pf * 3 + dh; unit u lives in ring slot u % kHeadRing.
-  auto issue = [&](int u) {
-    const int pf = u / 3, dh = u - 3 * (u / 3);
-    const Rsrc rs = frame_rsrc(pf);
-    const uint32_t row = (uint32_t)((h + dh - 1) * W * C * 2);   // may wrap: out of range
-    char* dst = ring + (u % kHeadRing) * UNIT;
+  // Byte offset of input row h + dh - 1 in a frame (row -1 wraps: out of range).
+  uint32_t rowoff[3];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dma16(rs, pvo[i] + row, 0, dst + i * 1024);
+  for (int dh = 0; dh < 3; ++dh) rowoff[dh] = (uint32_t)((h + dh - 1) * W * C * 2);
+  // Unit (frame pf, row tap dh) goes to ring slot dh.
+  auto issue = [&](const Rsrc& rs, auto DH_) __attribute__((always_inline)) {
+    constexpr int DH = decltype(DH_)::value;
+    char* dst = ring + DH * UNIT;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma16(rs, pvo[i] + rowoff[DH], 0, dst + i * 1024);
   };
-  auto window = [&](const char* base, int r0) {     // rows r0 .. r0 + 15, chunk g
-    const int r = r0 + j;
-    return *reinterpret_cast<const bf16x8*>(base + r * 64 + ((g ^ ((r >> 1) & 3)) << 4));
-  };
-  // Unit of frame pf = 3 q + U, row dh: 3 column taps x 3 frame taps per segment into the
-  // ring slots of output frames pf - dt (slot (U - dt) mod 3).
-  auto compute_unit = [&](int u, auto U_, int dh) {
+  // Window of column tap dw in segment s: rows 16 s + dw + j at chunk g ^ ((row >> 1) & 3);
+  // 16 s does not change row bits 1-2, so per lane one base per dw, plus s KB.
+  uint32_t woff[3];
+#pragma unroll
+  for (int dw = 0; dw < 3; ++dw) {
+    const int r = dw + j;
+    woff[dw] = (uint32_t)(ring - smem) + r * 64 + ((g ^ ((r >> 1) & 3)) << 4);
+  }
+  // Unit of frame pf = 3 q + U, row tap DH (in slot DH): 3 column taps x 3 frame taps per
+  // segment into the accumulator slots of output frames pf - dt (slot (U - dt) mod 3). All
+  // 9 windows are read before the first MFMA.
+  auto compute_unit = [&](auto U_, auto DH_) __attribute__((always_inline)) {
     constexpr int U = decltype(U_)::value;
-    const char* base = ring + (u % kHeadRing) * UNIT;
+    constexpr int DH = decltype(DH_)::value;
+    bf16x8 bb[kHeadSeg][3];
 #pragma unroll
-    for (int s = 0; s < kHeadSeg; ++s)
+    for (int sg = 0; sg < kHeadSeg; ++sg)
+#pragma unroll
+      for (int dw = 0; dw < 3; ++dw)
+        bb[sg][dw] = *reinterpret_cast<const bf16x8*>(smem + woff[dw] + DH * UNIT + sg * 1024);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int sg = 0; sg < kHeadSeg; ++sg)
 #pragma unroll
       for (int dw = 0; dw < 3; ++dw) {
-        const bf16x8 bb = window(base, 16 * s + dw);
 #pragma unroll
         for (int dt = 0; dt < 3; ++dt) {
           const int slot = ((U - dt) % 3 + 3) % 3;
-          acc[slot][s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[dt * 9 + dh * 3 + dw], bb, acc[slot][s], 0, 0, 0);
+          acc[slot][sg] =
+              __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[dt * 9 + DH * 3 + dw], bb[sg][dw], acc[slot][sg], 0, 0, 0);
         }
       }
   };
 
-  // Output frame t (ring slot S) is complete: add the waves' partial sums through LDS (two
-  // buffers, one barrier per frame), then wave w < kHeadSeg writes segment w; the slot is
-  // cleared for output frame t + 3. Slots of frames before 0 only collect the taps that
+  // Output frame t (accumulator slot S) is complete: add the waves' partial sums through LDS
+  // (two buffers, one barrier per frame), then wave w < kHeadSeg writes segment w; the slot
+  // is cleared for output frame t + 3. Slots of frames before 0 only collect the taps that
   // reach before the first frame: they are cleared without a store.
   int rb = 0;
-  auto retire = [&](int t, auto S_) {
+  auto retire = [&](int t, auto S_) __attribute__((always_inline)) {
     constexpr int S = decltype(S_)::value;
     if (t < 0) {
 #pragma unroll
-      for (int s = 0; s < kHeadSeg; ++s) acc[S][s] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int sg = 0; sg < kHeadSeg; ++sg) acc[S][sg] = f32x4{0.f, 0.f, 0.f, 0.f};
       return;
     }
     f32x4* rr = red + rb * (NW * kHeadSeg * 64);
 #pragma unroll
-    for (int s = 0; s < kHeadSeg; ++s) {
-      rr[(wave * kHeadSeg + s) * 64 + lane] = acc[S][s];
-      acc[S][s] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int sg = 0; sg < kHeadSeg; ++sg) {
+      rr[(wave * kHeadSeg + sg) * 64 + lane] = acc[S][sg];
+      acc[S][sg] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     // LDS writes complete, then the barrier: not __syncthreads, whose fence would also
     // wait for the moves in flight.
     wait_lgkm0();
     stage_barrier();
     if (t < T && g < 3 && wave < kHeadSeg) {
-      const int s = wave;
-      const int col = w0 + 16 * s + j;
+      const int sg = wave;
+      const int col = w0 + 16 * sg + j;
       if (col < W) {
-        f32x4 v = rr[s * 64 + lane];
+        f32x4 v = rr[sg * 64 + lane];
 #pragma unroll
-        for (int q = 1; q < NW; ++q) v += rr[(q * kHeadSeg + s) * 64 + lane];
+        for (int q = 1; q < NW; ++q) v += rr[(q * kHeadSeg + sg) * 64 + lane];
         float o[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -1447,29 +1469,40 @@ __global__ __launch_bounds__(64 * NW, 1) void head_kernel(ConvParams p, int wblo
 
   // Frames in groups of three; without a cache the first group skips the two zero frames
   // (a separate copy of the group, so both keep static registers). Frames past T + 1 read
-  // zeros and store nothing. Unit u + 2's moves are in flight while unit u computes.
+  // zeros and store nothing. Units go in order (frame, row tap); the moves of the next two
+  // units are in flight while one computes.
   const int groups3 = (T + 2 + 2) / 3;
-  issue(0);
-  issue(1);
-  auto group = [&](int q, auto SKIP_) {
+  {
+    const Rsrc f0 = frame_rsrc(0);
+    issue(f0, IC<0>{});
+    issue(f0, IC<1>{});
+  }
+  auto group = [&](int q, auto SKIP_) __attribute__((always_inline)) {
     constexpr bool SKIP = decltype(SKIP_)::value != 0;
-    const int ub = 9 * q;
-#pragma unroll
-    for (int k = 0; k < 9; ++k) {
-      wait_vm<4>();                                  // this wave's moves of unit ub + k landed
-      const int dh = k % 3;
-      if (k < 3) {
-        if (!SKIP) compute_unit(ub + k, IC<0>{}, dh);
-      } else if (k < 6) {
-        if (!SKIP) compute_unit(ub + k, IC<1>{}, dh);
-      } else {
-        compute_unit(ub + k, IC<2>{}, dh);
-      }
-      issue(ub + k + 2);                             // into the slot unit ub + k - 1 used
-      if (k == 2) retire(3 * q - 2, IC<1>{});
-      if (k == 5) retire(3 * q - 1, IC<2>{});
-      if (k == 8) retire(3 * q, IC<0>{});
-    }
+    // frames 3q .. 3q + 3: the group's own and the first of the next (units run 2 ahead)
+    const Rsrc fr0 = frame_rsrc(3 * q), fr1 = frame_rsrc(3 * q + 1), fr2 = frame_rsrc(3 * q + 2),
+               fr3 = frame_rsrc(3 * q + 3);
+    auto step = [&](auto K_) __attribute__((always_inline)) {
+      constexpr int K = decltype(K_)::value;
+      constexpr int U = K / 3, DH = K % 3;
+      constexpr int KN = K + 2, UN = KN / 3, DHN = KN % 3;   // the unit issued after this one
+      wait_vm<4>();                                  // this wave's moves of this unit landed
+      if (!SKIP || U == 2) compute_unit(IC<U>{}, IC<DH>{});
+      const Rsrc& rn = UN == 0 ? fr0 : UN == 1 ? fr1 : UN == 2 ? fr2 : fr3;
+      issue(rn, IC<DHN>{});                          // into the slot this unit's row tap used
+      if (K == 2) retire(3 * q - 2, IC<1>{});
+      if (K == 5) retire(3 * q - 1, IC<2>{});
+      if (K == 8) retire(3 * q, IC<0>{});
+    };
+    step(IC<0>{});
+    step(IC<1>{});
+    step(IC<2>{});
+    step(IC<3>{});
+    step(IC<4>{});
+    step(IC<5>{});
+    step(IC<6>{});
+    step(IC<7>{});
+    step(IC<8>{});
   };
   if (p.cache)
     group(0, IC<0>{});
