@@ -887,7 +887,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_kernel(ConvParams p) {
 //   distinct 16-byte bank groups, whatever the window offset.
 constexpr int kSlabStages = 4;           // weight stage buffers of the slab kernel
 
-__host__ __device__ constexpr int slab_inner(int mode) { return mode == kPhase ? 2 : 3; }
+__host__ __device__ constexpr int slab_inner(int mode) { return mode == kPhase ? 2 : mode == kTime ? 1 : 3; }
 
 // Slab buffers: slab G starts moving L + INNER stages before stage INNER G and its buffer
 // must have been retired (after stage INNER (G - NSL) + INNER - 1): INNER NSL >= L + 2 INNER.
@@ -902,7 +902,7 @@ constexpr int slab_lds_bytes() {
          BN * 4;
 }
 
-// s_waitcnt vmcnt(n) for a wave-uniform n in [0, 15].
+// s_waitcnt vmcnt(n) for a wave-uniform n in [0, 31].
 __device__ __forceinline__ void wait_vm_n(int n) {
   switch (n) {
     case 0: wait_vm<0>(); break;
@@ -920,15 +920,31 @@ __device__ __forceinline__ void wait_vm_n(int n) {
     case 12: wait_vm<12>(); break;
     case 13: wait_vm<13>(); break;
     case 14: wait_vm<14>(); break;
-    default: wait_vm<15>(); break;
+    case 15: wait_vm<15>(); break;
+    case 16: wait_vm<16>(); break;
+    case 17: wait_vm<17>(); break;
+    case 18: wait_vm<18>(); break;
+    case 19: wait_vm<19>(); break;
+    case 20: wait_vm<20>(); break;
+    case 21: wait_vm<21>(); break;
+    case 22: wait_vm<22>(); break;
+    case 23: wait_vm<23>(); break;
+    case 24: wait_vm<24>(); break;
+    case 25: wait_vm<25>(); break;
+    case 26: wait_vm<26>(); break;
+    case 27: wait_vm<27>(); break;
+    case 28: wait_vm<28>(); break;
+    case 29: wait_vm<29>(); break;
+    case 30: wait_vm<30>(); break;
+    default: wait_vm<31>(); break;
   }
 }
 
 template <int BM, int BN, int WGM, int WGN, int NS, int MODE>
 __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_slab_kernel(ConvParams p) {
-  static_assert(MODE == kCausal || MODE == kPhase, "slab modes");
+  static_assert(MODE == kCausal || MODE == kPhase || MODE == kTime, "slab modes");
   constexpr int INNER = slab_inner(MODE);            // column taps per group
-  constexpr int TAPS = MODE == kPhase ? 4 : 27;
+  constexpr int TAPS = MODE == kPhase ? 4 : MODE == kTime ? 3 : 27;
   constexpr int NW = WGM * WGN, L = NS - 1, NSL = slab_bufs(NS, INNER);
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
   constexpr int TM = WTM / 32, TN = WTN / 32;
@@ -949,7 +965,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_slab_kernel(ConvParams
   constexpr int SPW = (SP + NW - 1) / NW;            // slab moves per wave and part
   static_assert(IA % NW == 0 && SPL >= 0, "moves per wave");
   constexpr int STEADY = SPW + (L - 2) * (DW + SPW); // moves after those of stage s + 1
-  static_assert(STEADY + DW <= 15, "wait range");
+  static_assert(STEADY + DW <= 31, "wait range");
   constexpr int TAILG = (L + 2 * INNER - 1) / INNER; // last groups, waited for exactly
 
   extern __shared__ __align__(16) char smem[];
@@ -984,7 +1000,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_slab_kernel(ConvParams
   const int NG = (TAPS / INNER) * kpt;               // groups, INNER stages each
   const int KS = INNER * NG;
   const int pos0 = mt * BM;
-  const int c0 = MODE == kPhase ? pb - 1 : -1;       // column offset of the slab's first row
+  const int c0 = MODE == kPhase ? pb - 1 : MODE == kTime ? 0 : -1;   // column offset of slab row 0
   // This lane moves logical chunk lc of row (16 qi + (lane >> 2)); (row & 15) = lane >> 2.
   const int lc = (lane & 3) ^ ((lane >> 3) & 3) ^ ((lane >> 5) & 1);
 
@@ -1028,18 +1044,20 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_slab_kernel(ConvParams
     wo += wrap_c ? 1 : 0;
   };
   // Descriptors of the source frames of frame taps dt = 0, 1, 2: frame t + dt - 2 of x, a
-  // cache frame, or (no cache) zeros. The phases read frame t only.
-  const Rsrc frs2 = make_rsrc(p.x + ((int64_t)n * T + t) * HW * C, frame_bytes);
+  // cache frame, or (no cache) zeros. The phases read frame t only. The temporal x2 reads
+  // x from frame x0 on, Tx frames per sample.
+  const int64_t xf0 = MODE == kTime ? (int64_t)n * p.Tx + p.x0 : (int64_t)n * T;
+  const Rsrc frs2 = make_rsrc(p.x + (xf0 + t) * HW * C, frame_bytes);
   Rsrc frs0 = frs2, frs1 = frs2;
-  if (MODE == kCausal) {
+  if (MODE == kCausal || MODE == kTime) {
     if (t >= 2)
-      frs0 = make_rsrc(p.x + ((int64_t)n * T + t - 2) * HW * C, frame_bytes);
+      frs0 = make_rsrc(p.x + (xf0 + t - 2) * HW * C, frame_bytes);
     else if (p.cache)
       frs0 = make_rsrc(p.cache + ((int64_t)n * 2 + t) * HW * C, frame_bytes);
     else
       frs0 = make_rsrc(p.x, 0);
     if (t >= 1)
-      frs1 = make_rsrc(p.x + ((int64_t)n * T + t - 1) * HW * C, frame_bytes);
+      frs1 = make_rsrc(p.x + (xf0 + t - 1) * HW * C, frame_bytes);
     else if (p.cache)
       frs1 = make_rsrc(p.cache + ((int64_t)n * 2 + t + 1) * HW * C, frame_bytes);
     else
@@ -1050,9 +1068,9 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_slab_kernel(ConvParams
   auto issue_s = [&](auto part_c) __attribute__((always_inline)) {
     constexpr int PART = decltype(part_c)::value;
     if (PART == 0) {
-      // dh: the row tap, stored + 1 (causal dh; phase u + a).
-      const int dt = MODE == kPhase ? 2 : go / 3;
-      const int dh = MODE == kPhase ? go + pa : go - 3 * dt;
+      // dh: the row tap, stored + 1 (causal dh; phase u + a; the temporal x2's one row).
+      const int dt = MODE == kPhase ? 2 : MODE == kTime ? go : go / 3;
+      const int dh = MODE == kPhase ? go + pa : MODE == kTime ? 1 : go - 3 * dt;
       const Rsrc r0 = frs0, r1 = frs1, r2 = frs2;     // values: a select of lvalues would
       srs = dt == 0 ? r0 : dt == 1 ? r1 : r2;        // select their addresses
       sdelta = ((dh - 1) * W * C + gch * kPK) * 2;
@@ -1180,7 +1198,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_slab_kernel(ConvParams
   bias.issue(p, ntile, tid);
   if (tid < 4) *reinterpret_cast<uint4*>(smem + ZROW + 16 * tid) = make_uint4(0, 0, 0, 0);
   issue_s(IC<0>{});
-  issue_s(IC<1>{});
+  if constexpr (INNER > 1) issue_s(IC<1>{});
   if constexpr (INNER > 2) issue_s(IC<2>{});
   static_assert(L >= 3 && L <= 5 && INNER <= 3, "prologue");
   issue_w();
@@ -1243,15 +1261,16 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_slab_kernel(ConvParams
   static_assert(INNER * TAILG >= L + INNER, "tail");
   for (int g = 0; g < NG - TAILG; ++g) {
     step(IC<0>{}, IC<1>{}, INNER * g);
-    step(IC<1>{}, IC<1>{}, INNER * g + 1);
+    if constexpr (INNER > 1) step(IC<1>{}, IC<1>{}, INNER * g + 1);
     if constexpr (INNER > 2) step(IC<2>{}, IC<1>{}, INNER * g + 2);
   }
   for (int g = NG - TAILG; g < NG - 1; ++g) {
     step(IC<0>{}, IC<0>{}, INNER * g);
-    step(IC<1>{}, IC<0>{}, INNER * g + 1);
+    if constexpr (INNER > 1) step(IC<1>{}, IC<0>{}, INNER * g + 1);
     if constexpr (INNER > 2) step(IC<2>{}, IC<0>{}, INNER * g + 2);
   }
-  step(IC<0>{}, IC<0>{}, KS - INNER);
+  // the last group: all its stages but the last (that one follows, without moves)
+  if constexpr (INNER > 1) step(IC<0>{}, IC<0>{}, KS - INNER);
   if constexpr (INNER > 2) step(IC<1>{}, IC<0>{}, KS - 2);
   load_frags(IC<INNER - 1>{}, a1, b1, wbuf, sbuf, 1);
   mfmas(a0, b0);
@@ -1266,9 +1285,10 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_slab_kernel(ConvParams
     if (MODE == kCausal && p.nws)
       next_stats_partials<NW, WGM, WTN, BN>(p, n, t, mt, ntile, wave, lane, sums,
                                             reinterpret_cast<double*>(smem + NW * 32 * WTN * 4));
-  } else
+  } else if constexpr (MODE != kTime) {               // the temporal x2 needs K % 16 == 0
     store_tile<MODE, TN, TM, WTM, WTN>(acc, p, n, (int64_t)t * HW + pos0, (int64_t)(t + 1) * HW,
                                        ntile * BN + wn * WTN, wm, lane, phase, lb);
+  }
 }
 
 // ---------------------------------------------------------------- the output head
@@ -1556,7 +1576,7 @@ static int candidates(int bn, int c, TileCfg* out) {
       // 0.81 ms). The slab kernel: 4 waves of 128 x 128 (accumulators in AGPRs), a third
       // fewer fragment reads per MFMA; its moves are scheduled between MFMAs, so one wave
       // per SIMD keeps the matrix pipe fed (latent block 0.600 vs 0.632 ms with 8 waves).
-      if constexpr ((MODE == kCausal || MODE == kPhase) && !FUSE) {
+      if constexpr ((MODE == kCausal || MODE == kPhase || MODE == kTime) && !FUSE) {
         out[n++] = make_slab_cfg<256, 256, 2, 2, MODE>();
         out[n++] = make_slab_cfg<224, 256, 1, 4, MODE>();
       } else {
