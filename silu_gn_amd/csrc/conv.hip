@@ -972,8 +972,10 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_slab_kernel(ConvParams
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar branches
 
-  // Workgroup -> tile, XCD-aware as in conv_kernel. Order inside a run: N tile, phase, tile
-  // of the frame, frame, sample.
+  // Workgroup -> tile, XCD-aware as in conv_kernel. Order inside a run: N tile, phase,
+  // frame, tile of the frame, sample: tiles at one position of consecutive frames share two
+  // of their three source frames, and with frames fastest they run at the same time (the
+  // upsample block's conv 4.53 -> 4.40 ms; with a 4 MB L2 per XCD the gain is small).
   int tile;
   {
     const int bid = blockIdx.x, nb = p.nblocks;
@@ -987,10 +989,10 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_slab_kernel(ConvParams
     phase = tile & 3;
     tile >>= 2;
   }
-  const int mt = tile % p.tiles_f;
-  tile /= p.tiles_f;
   const int t = tile % p.T;
-  const int n = tile / p.T;
+  tile /= p.T;
+  const int mt = tile % p.tiles_f;
+  const int n = tile / p.tiles_f;
   const int pa = phase >> 1, pb = phase & 1;
 
   const int C = p.C, K = p.K, H = p.H, W = p.W, T = p.T;
