@@ -428,38 +428,42 @@ struct BiasStage {
 
 // cache_out = the last 2 frames of P = cat(cache_in, a), a = frames x0 .. x0 + T - 1 of the
 // Tx frames per sample of x; frames of x are activated when fused (same per-thread column
-// layout and activate_packet as gn_silu_apply).
+// layout and activate_packet as gn_silu_apply). A row of cp packets is covered by
+// tpr = min(cp, 256) threads, each taking every tpr-th packet; rstep rows per block pass.
 __global__ __launch_bounds__(256) void cache_out_kernel(
     const uint4* x, const uint4* cache_in, uint4* cache_out, int T, int Tx, int x0, int64_t hw, int cp,
     int rstep, int64_t rows_per_block, const double* stats, const float* gamma, const float* beta,
     double eps, int groups) {
   const int tid = threadIdx.x, n = blockIdx.y;
-  if (tid >= rstep * cp) return;
-  const int col = tid % cp;
-  Affine a[8];
-  if (stats) {
-    const int cg = cp * 8 / groups;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) a[i] = channel_affine(stats, gamma, beta, eps, groups, cg, n, col * 8 + i);
-  }
+  const int tpr = cp < 256 ? cp : 256;
+  if (tid >= rstep * tpr) return;
+  const int c0 = tid % tpr;
   const int64_t positions = 2 * hw;
   const int64_t start = (int64_t)blockIdx.x * rows_per_block;
   int64_t end = start + rows_per_block;
   if (end > positions) end = positions;
-  for (int64_t q = start + tid / cp; q < end; q += rstep) {
-    const int f = (int)(q / hw);                     // 0 or 1
-    const int64_t s = q - f * hw;
-    const int pf = T + f;                            // frame of P = cat(cache_in, x)
-    uint4 v;
-    if (pf >= 2) {
-      v = x[(((int64_t)n * Tx + x0 + pf - 2) * hw + s) * cp + col];
-      if (stats) v = activate_packet(v, a);
-    } else if (cache_in) {
-      v = cache_in[(((int64_t)n * 2 + pf) * hw + s) * cp + col];
-    } else {
-      v = make_uint4(0, 0, 0, 0);
+  for (int col = c0; col < cp; col += tpr) {
+    Affine a[8];
+    if (stats) {
+      const int cg = cp * 8 / groups;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) a[i] = channel_affine(stats, gamma, beta, eps, groups, cg, n, col * 8 + i);
     }
-    cache_out[(((int64_t)n * 2 + f) * hw + s) * cp + col] = v;
+    for (int64_t q = start + tid / tpr; q < end; q += rstep) {
+      const int f = (int)(q / hw);                   // 0 or 1
+      const int64_t s = q - f * hw;
+      const int pf = T + f;                          // frame of P = cat(cache_in, x)
+      uint4 v;
+      if (pf >= 2) {
+        v = x[(((int64_t)n * Tx + x0 + pf - 2) * hw + s) * cp + col];
+        if (stats) v = activate_packet(v, a);
+      } else if (cache_in) {
+        v = cache_in[(((int64_t)n * 2 + pf) * hw + s) * cp + col];
+      } else {
+        v = make_uint4(0, 0, 0, 0);
+      }
+      cache_out[(((int64_t)n * 2 + f) * hw + s) * cp + col] = v;
+    }
   }
 }
 

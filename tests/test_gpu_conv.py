@@ -41,6 +41,9 @@ def _gn_params(c, seed):
         reason="K past one 256 tile: faulted the GPU once under a since-removed kernel "
                "revision with no cause shown; kept off the GPU until one is")),
     (1, 2, 7, 9, 512, 264, False, True, False),      # K past one 256 tile, ragged
+    (1, 2, 3, 4, 4096, 64, True, True, False),       # the largest C: cache rows of 512 packets
+    (2, 1, 3, 4, 4096, 128, False, False, True),     # ... without a cache (zeros), two samples
+    (1, 2, 3, 5, 64, 4096, True, True, True),        # the largest K: 16 N tiles
 ])
 def test_conv_small(n, t, h, w, c, k, cache, bias, res):
     print("case", (n, t, h, w, c, k, cache, bias, res), flush=True)
@@ -73,6 +76,7 @@ def _fused_case(shape, k, groups, seed, cache=True):
     ((1, 3, 16, 16, 64), 64, 32),
     ((2, 1, 7, 9, 256), 32, 32),
     ((1, 3, 5, 37, 1024), 256, 32),
+    ((1, 2, 3, 4, 2048), 64, 32),                   # the largest C the fused load takes
 ])
 def test_fused_equals_apply_then_conv_and_oracle(shape, k, groups):
     print("case fused", shape, k, groups, flush=True)

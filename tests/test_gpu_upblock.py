@@ -39,6 +39,7 @@ def _time_inputs(n, t, h, w, c, cache, bias, seed):
     (2, 3, 4, 5, 256, True, False, False),
     (1, 2, 3, 5, 320, False, True, True),
     (1, 2, 5, 6, 1024, True, True, True),
+    (1, 2, 3, 3, 2048, True, True, True),      # the largest C: K = 4096, 16 N tiles
 ])
 def test_time_upsample_small(n, t, h, w, c, first, cache, bias):
     print("case time_upsample", (n, t, h, w, c, first, cache, bias), flush=True)
