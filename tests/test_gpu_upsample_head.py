@@ -34,6 +34,8 @@ DEV = "cuda"
     (1, 2, 1, 1, 128, 256, True),         # a single pixel
     (1, 1, 5, 1, 256, 256, False),        # one column: both row edges in every window
     (2, 1, 3, 40, 128, 264, True),        # K over two N tiles, the second ragged
+    (1, 1, 2, 3, 4096, 64, True),         # the largest C
+    (1, 2, 2, 3, 64, 4096, True),         # the largest K: 16 N tiles per phase
 ])
 def test_upsample_small(n, t, h, w, c, k, bias):
     print("case upsample", (n, t, h, w, c, k, bias), flush=True)
@@ -74,6 +76,8 @@ def test_upsample_workload_sampled():
     (1, 16, 6, 33, 256, False, False, False, False),
     (2, 2, 3, 17, 128, True, False, True, False),
     (1, 1, 1, 1, 256, True, True, False, False),
+    (1, 2, 3, 4, 4096, True, True, False, False),   # the largest C (the generic tile)
+    (1, 2, 3, 4, 2048, True, True, True, True),     # the largest fused C
 ])
 def test_head_small(n, t, h, w, c, cache, bias, clamp, fused):
     print("case head", (n, t, h, w, c, cache, bias, clamp, fused), flush=True)
