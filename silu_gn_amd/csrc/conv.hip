@@ -1307,12 +1307,12 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_slab_kernel(ConvParams
 //   output channels x 32 input channels, rows 12-15 zero). The waves' partial sums are
 //   added through LDS when an output frame is complete. Eight waves (two per SIMD) cover
 //   C = 256, four cover C = 128.
-// - A workgroup owns one output row h and 48 columns (3 segments of 16) for every frame,
+// - A workgroup owns one output row h and 64 columns (4 segments of 16) for every frame,
 //   and streams the input frames of P = cat(cache, x) once: frame p feeds output frames
 //   p - dt, dt = 0..2, held in a ring of 3 accumulators per segment. Output frame t is
 //   complete after input frame t + 2.
-// - A unit of work is (input frame, input row h + dh - 1, the wave's chunk). Its 50 input
-//   columns w0 - 1 .. w0 + 48 (64-byte rows) move global -> LDS with buffer_load ... lds
+// - A unit of work is (input frame, input row h + dh - 1, the wave's chunk). Its 66 input
+//   columns w0 - 1 .. w0 + 64 (64-byte rows) move global -> LDS with buffer_load ... lds
 //   into the wave's own ring of 3 units, two units ahead; each wave waits only for its own
 //   moves (counted vmcnt), so the ring needs no barrier.
 // - With two waves per SIMD and one instruction per wave per issue cycle, the kernel is
@@ -1330,8 +1330,10 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_slab_kernel(ConvParams
 // The epilogue adds the bias, clamps if asked, and writes the 2x2 depth-to-space video
 // (channel k = 4c + 2dy + dx) as 4-byte pairs, 64 contiguous bytes per 16 columns.
 typedef __attribute__((ext_vector_type(4))) float f32x4;
-constexpr int kHeadSeg = 3;              // 16-column segments per workgroup (W = 624: 13 blocks)
-constexpr int kHeadRows = 64;            // LDS rows per unit (50 used: 48 columns + 2 edges)
+constexpr int kHeadSeg = 4;              // 16-column segments per workgroup (W = 624: 10 blocks)
+constexpr int kHeadRows = 80;            // LDS rows per unit (66 used: 64 columns + 2 edges)
+constexpr int kHeadMoves = kHeadRows / 16; // 1 KB moves per unit and wave
+constexpr int kHeadRed = 1;              // reduction buffers (one: a barrier before the writes)
 constexpr int kHeadRing = 3;             // units per wave in LDS (u % 3 = the unit's row tap)
 
 
@@ -1346,8 +1348,8 @@ __global__ __launch_bounds__(64 * NW, 1) void head_kernel(ConvParams p, int wblo
   const uint32_t frame_bytes = (uint32_t)HW * C * 2;
   constexpr int UNIT = kHeadRows * 64;               // bytes per unit in LDS
   char* ring = smem + wave * (kHeadRing * UNIT);
-  f32x4* red = reinterpret_cast<f32x4*>(smem + NW * kHeadRing * UNIT);   // [2][NW][seg][64]
-  float* sbias = reinterpret_cast<float*>(red + 2 * NW * kHeadSeg * 64);
+  f32x4* red = reinterpret_cast<f32x4*>(smem + NW * kHeadRing * UNIT);   // [kHeadRed][NW][seg][64]
+  float* sbias = reinterpret_cast<float*>(red + kHeadRed * NW * kHeadSeg * 64);
 
   // Workgroup -> (n, column block, h), rows fastest and XCD-aware: each XCD takes a
   // contiguous run, so the workgroups it runs at once are consecutive rows of one column
@@ -1381,11 +1383,11 @@ __global__ __launch_bounds__(64 * NW, 1) void head_kernel(ConvParams p, int wblo
   // 16 i + l / 4 (column w0 - 1 + row) at physical chunk l & 3, i.e. it loads logical chunk
   // (l & 3) ^ ((row >> 1) & 3) = (l & 3) ^ ((l >> 3) & 3). Rows past 49 and columns outside
   // the frame get kOOB (zeros, no memory access); adding a row offset keeps them out of range.
-  uint32_t pvo[4];
+  uint32_t pvo[kHeadMoves];
   {
     const int lc = (lane & 3) ^ ((lane >> 3) & 3);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < kHeadMoves; ++i) {
       const int r = 16 * i + (lane >> 2), col = w0 - 1 + r;
       pvo[i] = (r < 16 * kHeadSeg + 2 && col >= 0 && col < W)
                    ? ((uint32_t)col * C + wave * 32 + lc * 8) * 2 : kOOB;
@@ -1413,7 +1415,7 @@ __global__ __launch_bounds__(64 * NW, 1) void head_kernel(ConvParams p, int wblo
     constexpr int DH = decltype(DH_)::value;
     char* dst = ring + DH * UNIT;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dma16(rs, pvo[i] + rowoff[DH], 0, dst + i * 1024);
+    for (int i = 0; i < kHeadMoves; ++i) dma16(rs, pvo[i] + rowoff[DH], 0, dst + i * 1024);
   };
   // Window of column tap dw in segment s: rows 16 s + dw + j at chunk g ^ ((row >> 1) & 3);
   // 16 s does not change row bits 1-2, so per lane one base per dw, plus s KB.
@@ -1450,9 +1452,10 @@ __global__ __launch_bounds__(64 * NW, 1) void head_kernel(ConvParams p, int wblo
   };
 
   // Output frame t (accumulator slot S) is complete: add the waves' partial sums through LDS
-  // (two buffers, one barrier per frame), then wave w < kHeadSeg writes segment w; the slot
-  // is cleared for output frame t + 3. Slots of frames before 0 only collect the taps that
-  // reach before the first frame: they are cleared without a store.
+  // (kHeadRed buffers; with one, a barrier before the writes as well as after them), then
+  // wave w < kHeadSeg writes segment w; the slot is cleared for output frame t + 3. Slots of
+  // frames before 0 only collect the taps that reach before the first frame: they are
+  // cleared without a store.
   int rb = 0;
   auto retire = [&](int t, auto S_) __attribute__((always_inline)) {
     constexpr int S = decltype(S_)::value;
@@ -1462,6 +1465,7 @@ __global__ __launch_bounds__(64 * NW, 1) void head_kernel(ConvParams p, int wblo
       return;
     }
     f32x4* rr = red + rb * (NW * kHeadSeg * 64);
+    if (kHeadRed == 1) stage_barrier();              // every wave has read the previous frame's sums
 #pragma unroll
     for (int sg = 0; sg < kHeadSeg; ++sg) {
       rr[(wave * kHeadSeg + sg) * 64 + lane] = acc[S][sg];
@@ -1490,7 +1494,7 @@ __global__ __launch_bounds__(64 * NW, 1) void head_kernel(ConvParams p, int wblo
         *reinterpret_cast<uint32_t*>(p.y + base + (2 * h + 1) * W2) = pack_bf16x2(o[2], o[3]);
       }
     }
-    rb ^= 1;
+    rb = kHeadRed == 1 ? 0 : rb ^ 1;
   };
 
   // Frames in groups of three; without a cache the first group skips the two zero frames
@@ -1512,7 +1516,7 @@ __global__ __launch_bounds__(64 * NW, 1) void head_kernel(ConvParams p, int wblo
       constexpr int K = decltype(K_)::value;
       constexpr int U = K / 3, DH = K % 3;
       constexpr int KN = K + 2, UN = KN / 3, DHN = KN % 3;   // the unit issued after this one
-      wait_vm<4>();                                  // this wave's moves of this unit landed
+      wait_vm<kHeadMoves>();                         // this wave's moves of this unit landed
       if (!SKIP || U == 2) compute_unit(IC<U>{}, IC<DH>{});
       const Rsrc& rn = UN == 0 ? fr0 : UN == 1 ? fr1 : UN == 2 ? fr2 : fr3;
       issue(rn, IC<DHN>{});                          // into the slot this unit's row tap used
@@ -2100,7 +2104,7 @@ extern "C" int head_conv_d2s(const uint16_t* x, sgn_dims d, const uint16_t* cach
     }
     p.nblocks = (int)nb;
     const int nw = p.C / 32;
-    const int lds = nw * kHeadRing * kHeadRows * 64 + 2 * nw * kHeadSeg * 64 * 16 + 64;
+    const int lds = nw * kHeadRing * kHeadRows * 64 + kHeadRed * nw * kHeadSeg * 64 * 16 + 64;
     const void* fn_ptr = nw == 4 ? (const void*)head_kernel<4> : (const void*)head_kernel<8>;
     hipError_t e = hipFuncSetAttribute(fn_ptr, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) {
