@@ -2095,7 +2095,7 @@ extern "C" int head_conv_d2s(const uint16_t* x, sgn_dims d, const uint16_t* cach
   p.mper = d.t * d.h * d.w;
   p.clamp = clamp ? 1 : 0;
   if (!fuse && (p.C == 128 || p.C == 256)) {
-    // The dedicated head kernel: one workgroup per (sample, row, 48 columns).
+    // The dedicated head kernel: one workgroup per (sample, row, 64 columns).
     const int wblocks = (p.W + 16 * kHeadSeg - 1) / (16 * kHeadSeg);
     const int64_t nb = (int64_t)d.n * p.H * wblocks;
     if (nb >= ((int64_t)1 << 31)) {
