@@ -62,6 +62,14 @@ typedef struct {
 const char* sgn_last_error(void);
 
 /*
+ * gn_silu_eligible -- 1 if gn_silu_stats / gn_silu_apply take dims d with `groups`
+ * groups, else 0 (the reason in sgn_last_error()). A predicate apart from the
+ * compute calls, as the group_norm_silu.py page's eligibility check (its
+ * `eligible`: the kernels run only for inputs they support). No device work.
+ */
+int gn_silu_eligible(sgn_dims d, int groups);
+
+/*
  * Bytes of device workspace gn_silu_stats needs for dims d and `groups`
  * (per-block fp64 partial sums). 0 if the arguments are invalid.
  */
@@ -144,6 +152,15 @@ int rms_silu(const uint16_t* x, sgn_dims d, const float* gain, float eps, uint16
 int causal_conv3d(const uint16_t* x, sgn_dims d, const uint16_t* cache_in,
                   const uint16_t* w, int k, const float* bias, const uint16_t* residual,
                   const sgn_gn* fuse, uint16_t* y, uint16_t* cache_out, hipStream_t stream);
+
+/*
+ * causal_conv3d_eligible -- 1 if causal_conv3d takes input dims d and K = k output
+ * channels (fuse_groups > 0: with a fused GroupNorm of that many groups; 0: unfused),
+ * else 0 with the reason in sgn_last_error(). The shape part of causal_conv3d's
+ * checks, as a predicate apart from compute (the group_norm_silu.py page's
+ * `eligible` check). No device work.
+ */
+int causal_conv3d_eligible(sgn_dims d, int k, int fuse_groups);
 
 /*
  * Bytes of device workspace causal_conv3d_next_stats needs for input dims d, K

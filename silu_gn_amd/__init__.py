@@ -35,7 +35,7 @@ class sgn_gn(ctypes.Structure):
                 ("eps", ctypes.c_float), ("groups", ctypes.c_int)]
 
 
-EXPORTS = ["sgn_last_error", "gn_silu_stats_workspace", "gn_silu_stats", "gn_silu_apply", "rms_silu",
+EXPORTS = ["sgn_last_error", "gn_silu_eligible", "causal_conv3d_eligible", "gn_silu_stats_workspace", "gn_silu_stats", "gn_silu_apply", "rms_silu",
            "causal_conv3d", "causal_conv3d_next_stats_workspace", "causal_conv3d_next_stats",
            "upsample2x_prepare_weights", "upsample2x_conv_phases", "upsample2x_conv_phases_shortcut",
            "time_upsample_conv", "head_conv_d2s"]
@@ -55,6 +55,8 @@ def load_library(path: str = LIB_PATH):
     gnp = ctypes.POINTER(sgn_gn)
     sigs = {
         "sgn_last_error": (ctypes.c_char_p, []),
+        "gn_silu_eligible": (i32, [sgn_dims, i32]),
+        "causal_conv3d_eligible": (i32, [sgn_dims, i32, i32]),
         "gn_silu_stats_workspace": (sz, [sgn_dims, i32]),
         "gn_silu_stats": (i32, [vp, sgn_dims, i32, vp, vp, sz, vp]),
         "gn_silu_apply": (i32, [vp, sgn_dims, i32, vp, vp, vp, f32, vp, vp]),
@@ -102,6 +104,14 @@ def _gn(fuse):
     stats, gamma, beta, eps, groups = fuse
     s = sgn_gn(stats.data_ptr(), gamma.data_ptr(), beta.data_ptr(), float(eps), int(groups))
     return ctypes.pointer(s), s
+
+
+def gn_silu_eligible(dims, groups: int) -> bool:
+    return bool(load_library().gn_silu_eligible(sgn_dims(*dims), groups))
+
+
+def causal_conv3d_eligible(dims, k: int, fuse_groups: int = 0) -> bool:
+    return bool(load_library().causal_conv3d_eligible(sgn_dims(*dims), k, fuse_groups))
 
 
 def gn_silu_stats_workspace(dims, groups: int) -> int:

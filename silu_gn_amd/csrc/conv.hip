@@ -1673,13 +1673,9 @@ static bool launch_cache_out(const uint16_t* x, sgn_dims d, const uint16_t* cach
   return launch_ok("cache_out");
 }
 
-static bool conv_common_checks(const uint16_t* x, sgn_dims d, const uint16_t* w, int k,
-                               uint16_t* y, const char* fn) {
+// The shapes the convolution kernels take (no pointers involved).
+static bool conv_shape_ok(sgn_dims d, int k, const char* fn) {
   if (!dims_ok(d, fn)) return false;
-  if (!x || !w || !y) {
-    set_error("%s: x, w and the output are required", fn);
-    return false;
-  }
   if (d.c % 64 != 0 || d.c > kCMax) {
     set_error("%s: C=%lld must be a multiple of 64 and at most %d", fn, (long long)d.c, kCMax);
     return false;
@@ -1704,6 +1700,16 @@ static bool conv_common_checks(const uint16_t* x, sgn_dims d, const uint16_t* w,
   if (4 * d.h * d.w * (int64_t)k * 2 >= ((int64_t)1 << 31)) {
     set_error("%s: an output frame of 4 x H=%lld x W=%lld x K=%d exceeds the 2 GiB frame limit", fn,
               (long long)d.h, (long long)d.w, k);
+    return false;
+  }
+  return true;
+}
+
+static bool conv_common_checks(const uint16_t* x, sgn_dims d, const uint16_t* w, int k,
+                               uint16_t* y, const char* fn) {
+  if (!conv_shape_ok(d, k, fn)) return false;
+  if (!x || !w || !y) {
+    set_error("%s: x, w and the output are required", fn);
     return false;
   }
   return true;
@@ -1832,6 +1838,23 @@ static int causal_conv_impl(const char* fn, const uint16_t* x, sgn_dims d, const
 }
 
 }  // namespace sgn
+
+extern "C" int causal_conv3d_eligible(sgn_dims d, int k, int fuse_groups) {
+  const char* fn = "causal_conv3d_eligible";
+  clear_error();
+  if (!conv_shape_ok(d, k, fn)) return 0;
+  if (fuse_groups != 0) {
+    if (fuse_groups < 0 || d.c % fuse_groups != 0) {
+      set_error("%s: fuse groups=%d must divide C=%lld", fn, fuse_groups, (long long)d.c);
+      return 0;
+    }
+    if (d.c > 2048) {
+      set_error("%s: fused GroupNorm supports C <= 2048", fn);
+      return 0;
+    }
+  }
+  return 1;
+}
 
 extern "C" int causal_conv3d(const uint16_t* x, sgn_dims d, const uint16_t* cache_in,
                              const uint16_t* w, int k, const float* bias, const uint16_t* residual,

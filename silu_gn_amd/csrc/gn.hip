@@ -331,6 +331,11 @@ __global__ __launch_bounds__(kThreads) void rms_silu_kernel(const uint4* __restr
 
 using namespace sgn;
 
+extern "C" int gn_silu_eligible(sgn_dims d, int groups) {
+  clear_error();
+  return gn_shape_ok(d, groups, "gn_silu_eligible") ? 1 : 0;
+}
+
 extern "C" size_t gn_silu_stats_workspace(sgn_dims d, int groups) {
   if (!gn_shape_ok(d, groups, "gn_silu_stats_workspace")) return 0;
   const int64_t positions = d.t * d.h * d.w;

@@ -51,6 +51,31 @@ def _err(rc, code):
     assert msg
 
 
+def test_eligibility_predicates():
+    lib = sga.load_library()
+    # GroupNorm: the shapes gn_silu_stats / gn_silu_apply take
+    assert lib.gn_silu_eligible(D(c=64), 32) == 1
+    assert lib.gn_silu_eligible(D(c=2048), 32) == 1
+    assert lib.gn_silu_eligible(D(c=64), 48) == 0            # groups does not divide C
+    assert lib.gn_silu_eligible(D(c=96), 8) == 0             # 12 channels per group
+    assert lib.gn_silu_eligible(D(c=4096), 32) == 0          # C > 2048
+    assert lib.gn_silu_eligible(D(t=0), 32) == 0
+    assert lib.sgn_last_error().decode()
+    for dims, g in [(D(c=64), 32), (D(c=96), 8), (D(c=4096), 32), (D(c=256), 4)]:
+        assert bool(lib.gn_silu_eligible(dims, g)) == (lib.gn_silu_stats_workspace(dims, g) > 0)
+    # convolution: shape part of causal_conv3d's checks
+    assert lib.causal_conv3d_eligible(D(c=64), 64, 0) == 1
+    assert lib.causal_conv3d_eligible(D(c=4096), 4096, 0) == 1
+    assert lib.causal_conv3d_eligible(D(c=72), 64, 0) == 0    # C % 64
+    assert lib.causal_conv3d_eligible(D(c=64), 6, 0) == 0     # K % 4
+    assert lib.causal_conv3d_eligible(D(c=64), 8192, 0) == 0  # K > 4096
+    assert lib.causal_conv3d_eligible(D(c=2048), 64, 32) == 1
+    assert lib.causal_conv3d_eligible(D(c=4096), 64, 32) == 0  # fused C > 2048
+    assert lib.causal_conv3d_eligible(D(c=64), 64, 48) == 0    # fused groups must divide C
+    assert lib.causal_conv3d_eligible(sga.sgn_dims(1, 1, 20000, 20000, 64), 64, 0) == 0   # frame > 2 GiB
+    assert sga.causal_conv3d_eligible((1, 2, 4, 4, 128), 256) is True
+
+
 def test_stats_workspace_size():
     lib = sga.load_library()
     assert lib.gn_silu_stats_workspace(D(), 32) > 0
