@@ -150,3 +150,30 @@ def test_upsample_shortcut_workload_sampled(ft, first):
     o = o + oup.dup_up3d_at(vals32(src), wl.c, ft, 2, first, pos)
     idx = tuple(torch.from_numpy(pos[:, i]) for i in range(4))
     assert_conv_close(bits(y.cpu()[idx]), o, "upsample+shortcut sampled")
+
+
+def test_up_block_chain():
+    """An up block's tail on a first pass: the temporal x2 of the resnets' output, then the
+    phases with the bias and the DupUp3D shortcut of the block input (ft = 2), against the
+    oracle's own composition (its temporal x2 rounded once to bf16 between the steps, where
+    the library stores the intermediate)."""
+    from oracle import bf16 as obf16
+    n, t, h, w, c = 1, 3, 6, 9, 128
+    seed = 91
+    xin = sg.normal((n, t, h, w, c), seed, sg.X_BLOCK)             # the block's input
+    x = sg.normal((n, t, h, w, c), seed, sg.X)                     # the resnets' output
+    wt = sg.normal((2 * c, 3, c), seed, sg.W_TIME, std=1 / math.sqrt(3 * c))
+    bt = sg.normal((2 * c,), seed, sg.BETA1, std=0.5, dtype=torch.float32)
+    w3 = sg.normal((c, 3, 3, c), seed, sg.W_UP, std=1 / math.sqrt(9 * c))
+    b3 = sg.normal((c,), seed, sg.BETA2, std=0.5, dtype=torch.float32)
+    print("case up block chain", (n, t, h, w, c), flush=True)
+    u = sga.time_upsample_conv(x.to(DEV), wt.to(DEV), True, None, bt.to(DEV))
+    wp = sga.upsample2x_prepare_weights(w3).to(DEV)
+    y = sga.upsample2x_conv_phases_shortcut(u, wp, xin.to(DEV), 2, True, b3.to(DEV))
+    torch.cuda.synchronize()
+    ou, _ = oup.time_upsample(vals(x), vals(wt), None, bt.numpy(), True)
+    assert_conv_close(bits(u)[:, 1:], ou[:, 1:], "chain: temporal x2")
+    our = obf16.decode(obf16.round_rne(ou))                        # stored in bf16 between the steps
+    o = oconv.upsample2x_conv(our, vals(w3), b3.numpy()) + oup.dup_up3d(vals(xin), c, 2, 2, True)
+    assert y.shape == (n, 2 * t - 1, 2 * h, 2 * w, c)
+    assert_conv_close(bits(y), o, "chain: phases + shortcut")
