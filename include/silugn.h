@@ -1,7 +1,8 @@
 /*
- * silugn.h -- C ABI of libsilugn.so: GroupNorm + SiLU and the causal / upsample /
- * head convolutions of a Wan2.2-style video VAE decoder, as gfx950 (MI355X) HIP
- * kernels.
+ * silugn.h -- C ABI of libsilugn.so: GroupNorm + SiLU (and the RMS norm + SiLU),
+ * the causal / upsample / head convolutions and the rest of an up block (temporal
+ * x2, DupUp3D shortcut) of a Wan2.2-style video VAE decoder, as gfx950 (MI355X)
+ * HIP kernels; shape predicates for the GroupNorm and the convolution.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
