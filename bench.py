@@ -182,10 +182,11 @@ def build_step(wl, dev, fused, separate_stats=False):
 
 
 def up_block_extras(wl, dev, iters):
-    """The up block's other steps at this workload's shape, each launched alone (HIP events):
+    """The path's other steps at this workload's shape, each launched alone (HIP events):
     latent: time_upsample_conv (3x1x1 causal conv C -> 2C, halves to frames, steady-state
     pass with a cache); upsample: the phases with the DupUp3D shortcut of a block input of
-    x's shape (ft = 1) against the phases alone."""
+    x's shape (ft = 1) against the phases alone; full-resolution block: the conv with the
+    RMS norm of its output in the epilogue against the conv followed by rms_silu."""
     if wl.kind == "latent":
         x = wl.x(dev)
         wt = sg.normal((2 * wl.c, 3, wl.c), wl.seed, sg.W_TIME, std=1 / math.sqrt(3 * wl.c), device=dev)
@@ -209,6 +210,22 @@ def up_block_extras(wl, dev, iters):
         return {"upsample_shortcut": {"ms": round(with_sc, 4), "ms_without_shortcut": round(plain, 4),
                                       "TFLOP/s": round(fl / (with_sc * 1e-3) / 1e12, 2),
                                       "shortcut": "DupUp3D of a %s block input, ft = 1" % list(wl.shape)}}
+    if wl.kind == "resblock":
+        # the decoder's RMS norm of the conv's output: a separate pass (causal_conv3d, then
+        # rms_silu) against the norm in the conv's epilogue with y not stored
+        x = wl.x(dev)
+        w = wl.conv_weight(1, dev)
+        gain = wl.gamma(2, dev)
+        y = torch.empty_like(x)
+        act = torch.empty_like(x)
+
+        def separate():
+            sga.causal_conv3d(x, w, y=y)
+            sga.rms_silu(y, gain, 1e-6, y=act)
+        sep = time_loop(separate, iters)
+        epi = time_loop(lambda: sga.causal_conv3d_rms(x, w, gain, 1e-6, act=act, store_y=False), iters)
+        return {"conv_rms_epilogue": {"ms": round(epi, 4), "ms_separate": round(sep, 4),
+                                      "form": "causal_conv3d_rms, y not stored (vs causal_conv3d + rms_silu)"}}
     return {}
 
 

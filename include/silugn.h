@@ -155,6 +155,29 @@ int causal_conv3d(const uint16_t* x, sgn_dims d, const uint16_t* cache_in,
                   const sgn_gn* fuse, uint16_t* y, uint16_t* cache_out, hipStream_t stream);
 
 /*
+ * causal_conv3d_rms -- causal_conv3d, plus act = the decoder's RMS norm + SiLU of its
+ * output (the next convolution's input), written by the convolution's epilogue when it
+ * can be.
+ * Defined by: binding.cpp page, Decoder's `prepared` edge (a convolution whose epilogue
+ * already normalised and activated the next convolution's input, with the y store
+ * suppressed when nothing else reads it: Decoder::conv's y_dead) and the decoder's RMS
+ * norm (the comment above Decoder::output_head); the formula is rms_silu's.
+ *
+ *   y   = causal_conv3d(x, cache_in, w, k, bias, residual, fuse)   (bf16)
+ *   act = rms_silu(y, gain, eps)                                   (bf16, N,T,H,W,K)
+ * Unfused with 128 < K <= 256 (one N tile holds every channel of a position) the
+ * epilogue forms each position's mean of squares from the rounded y in fp64 and stores
+ * act beside y; y may then be NULL (not stored). Otherwise y is required and act comes
+ * from rms_silu over y after the convolution. gain fp32 [K] (4-byte aligned); eps > 0;
+ * K % 64 == 0. act must not overlap any input or other output (SGN_EALIAS). Accuracy:
+ * y as causal_conv3d (bitwise the same); act within 1 bf16 ulp of rms_silu(y).
+ */
+int causal_conv3d_rms(const uint16_t* x, sgn_dims d, const uint16_t* cache_in,
+                      const uint16_t* w, int k, const float* bias, const uint16_t* residual,
+                      const sgn_gn* fuse, const float* gain, float eps, uint16_t* y,
+                      uint16_t* act, uint16_t* cache_out, hipStream_t stream);
+
+/*
  * causal_conv3d_eligible -- 1 if causal_conv3d takes input dims d and K = k output
  * channels (fuse_groups > 0: with a fused GroupNorm of that many groups; 0: unfused),
  * else 0 with the reason in sgn_last_error(). The shape part of causal_conv3d's

@@ -36,7 +36,7 @@ class sgn_gn(ctypes.Structure):
 
 
 EXPORTS = ["sgn_last_error", "gn_silu_eligible", "causal_conv3d_eligible", "gn_silu_stats_workspace", "gn_silu_stats", "gn_silu_apply", "rms_silu",
-           "causal_conv3d", "causal_conv3d_next_stats_workspace", "causal_conv3d_next_stats",
+           "causal_conv3d", "causal_conv3d_rms", "causal_conv3d_next_stats_workspace", "causal_conv3d_next_stats",
            "upsample2x_prepare_weights", "upsample2x_conv_phases", "upsample2x_conv_phases_shortcut",
            "time_upsample_conv", "head_conv_d2s"]
 
@@ -62,6 +62,7 @@ def load_library(path: str = LIB_PATH):
         "gn_silu_apply": (i32, [vp, sgn_dims, i32, vp, vp, vp, f32, vp, vp]),
         "rms_silu": (i32, [vp, sgn_dims, vp, f32, vp, vp]),
         "causal_conv3d": (i32, [vp, sgn_dims, vp, vp, i32, vp, vp, gnp, vp, vp, vp]),
+        "causal_conv3d_rms": (i32, [vp, sgn_dims, vp, vp, i32, vp, vp, gnp, vp, f32, vp, vp, vp, vp]),
         "causal_conv3d_next_stats_workspace": (sz, [sgn_dims, i32, i32]),
         "causal_conv3d_next_stats": (i32, [vp, sgn_dims, vp, vp, i32, vp, vp, gnp, vp, vp, i32, vp, vp,
                                            sz, vp]),
@@ -164,6 +165,22 @@ def causal_conv3d(x, w, cache_in=None, bias=None, residual=None, fuse=None, y=No
     _check(lib.causal_conv3d(_ptr(x), _dims(x), _ptr(cache_in), _ptr(w), k, _ptr(bias), _ptr(residual),
                              gp, _ptr(y), _ptr(cache_out), _stream(x)))
     return y
+
+
+def causal_conv3d_rms(x, w, gain, eps: float, cache_in=None, bias=None, residual=None, fuse=None,
+                      y=None, act=None, cache_out=None, store_y=True):
+    """causal_conv3d and act = rms_silu(y); returns (y or None, act). ``store_y=False`` skips y
+    (allowed when the epilogue applies the norm: unfused, 128 < K <= 256)."""
+    lib = load_library()
+    k = w.shape[0]
+    if y is None and store_y:
+        y = torch.empty(x.shape[:4] + (k,), dtype=torch.bfloat16, device=x.device)
+    if act is None:
+        act = torch.empty(x.shape[:4] + (k,), dtype=torch.bfloat16, device=x.device)
+    gp, _keep = _gn(fuse)
+    _check(lib.causal_conv3d_rms(_ptr(x), _dims(x), _ptr(cache_in), _ptr(w), k, _ptr(bias), _ptr(residual), gp,
+                                 _ptr(gain), float(eps), _ptr(y), _ptr(act), _ptr(cache_out), _stream(x)))
+    return y, act
 
 
 def causal_conv3d_next_stats_workspace(dims, k: int, next_groups: int) -> int:

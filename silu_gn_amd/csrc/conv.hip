@@ -70,6 +70,12 @@ struct ConvParams {
   // sc_first = the first ft - 1 output frames are dropped.
   const uint16_t* sc;
   int sc_T, sc_C, sc_ft, sc_first;
+  // The next RMS norm + SiLU written by the causal epilogue, or act == null: act =
+  // silu(y * gain / sqrt(mean_k y^2 + eps)) per position over the K channels of the tile
+  // (one N tile holds all of them); y itself is stored only if y != null.
+  uint16_t* act;
+  const float* rms_gain;
+  double rms_eps;
 };
 
 
@@ -370,6 +376,178 @@ __device__ __forceinline__ Sums store_tile_staged(const f32x16 (&acc)[TN][TM], c
     wait_lgkm0();                                    // reads done before the next rows land
   }
   return Sums{ss, sq};
+}
+
+// Causal epilogue that also applies the next RMS norm + SiLU (the decoder's norm is per
+// position, so a workgroup whose N tile holds all K channels has every value it needs). Per
+// 32-row block: stage fp32 (acc + bias) as store_tile_staged does, form the rounded outputs
+// (+ residual) and each lane's fp64 sum of their exact squares; add the sums of a row's LPR
+// lanes by DPP moves, publish the wave's row sums in LDS (two buffers by block
+// parity, one barrier per block), add the WGN waves' sums in wave order, and activate with
+// gain * rstd in fp64 through activate_packet (the code rms_silu runs). Channels past K
+// add nothing; rows past the frame and channels past K store nothing. Every wave takes
+// the same barriers.
+// v of the lane LPR lanes away in DPP terms: a 32-bit cross-lane move per half of the double.
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  union {
+    double d;
+    int i[2];
+  } u, r;
+  u.d = v;
+  r.i[0] = __builtin_amdgcn_update_dpp(0, u.i[0], CTRL, 0xF, 0xF, false);
+  r.i[1] = __builtin_amdgcn_update_dpp(0, u.i[1], CTRL, 0xF, 0xF, false);
+  return r.d;
+}
+
+// Sum of v over each aligned group of LPR (8 or 16) lanes, in lane 0 of the group: a row
+// mirror (16), a half-row mirror (8), then two quad permutes -- register-to-register moves,
+// a fixed order of additions.
+template <int LPR>
+__device__ __forceinline__ double group_sum_dpp(double v) {
+  static_assert(LPR == 8 || LPR == 16, "lane groups of 8 or 16");
+  if constexpr (LPR == 16) v += dpp_f64<0x140>(v);   // row_mirror: lane i + lane 15 - i
+  v += dpp_f64<0x141>(v);                           // row_half_mirror: lane i + lane 7 - i
+  v += dpp_f64<0x4E>(v);                            // quad_perm [2, 3, 0, 1]
+  v += dpp_f64<0xB1>(v);                            // quad_perm [1, 0, 3, 2]
+  return v;
+}
+
+template <int TN, int TM, int WTM, int WTN, int WGM, int WGN>
+__device__ __forceinline__ void store_tile_rms(const f32x16 (&acc)[TN][TM], const ConvParams& p, int n, int t,
+                                               int pos0, int kbase, int wm, int wn, int lane, const float* lbias,
+                                               char* stage, double* rred, char* opark, float* lgain) {
+  constexpr int ROW = WTN * 4;
+  constexpr int LPR = WTN / 8;
+  constexpr int RPI = 64 / LPR;
+  constexpr int NI = 32 / RPI;
+  static_assert(LPR * RPI == 64 && RPI * NI == 32, "staging shape");
+  constexpr int SWZ = WTN / 4 < 16 ? WTN / 4 - 1 : 15;
+  const int K = p.K, HW = p.H * p.W;
+  const int g = lane % LPR;
+  const int k0 = kbase + 8 * g;
+  const bool kin = k0 < K;
+  const int64_t base = ((int64_t)n * p.T + t) * HW * K;
+  const uint32_t fbytes = (uint32_t)((int64_t)HW * K * 2);
+  const Rsrc as = make_rsrc(p.act + base, fbytes);
+  const Rsrc ys = make_rsrc(p.y ? p.y + base : p.act, p.y ? fbytes : 0u);
+  const bool kfull = kbase + WTN <= K;
+  const Rsrc rs = make_rsrc(p.res ? p.res + base : p.act, p.res ? fbytes : 0u);
+  // The wave's WTN gains, read before any store (a load issued after stores would wait for
+  // them: vmcnt counts both) and kept in LDS.
+  float gload[(WTN + 63) / 64];
+#pragma unroll
+  for (int q = 0; q < (WTN + 63) / 64; ++q) {
+    const int kk = kbase + q * 64 + lane;
+    gload[q] = (q * 64 + lane < WTN && kk < K) ? p.rms_gain[kk] : 0.0f;
+  }
+  stage_barrier();                                   // every wave is done with the operand stages
+#pragma unroll
+  for (int q = 0; q < (WTN + 63) / 64; ++q)
+    if (q * 64 + lane < WTN) lgain[q * 64 + lane] = gload[q];
+#pragma unroll
+  for (int j = 0; j < TM; ++j) {
+    {
+      const int r = lane & 31;
+#pragma unroll
+      for (int i = 0; i < TN; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int kr = i * 32 + 8 * q + 4 * (lane >> 5);
+          const float4 b = *reinterpret_cast<const float4*>(lbias + kr);
+          float4 v;
+          v.x = acc[i][j][4 * q + 0] + b.x;
+          v.y = acc[i][j][4 * q + 1] + b.y;
+          v.z = acc[i][j][4 * q + 2] + b.z;
+          v.w = acc[i][j][4 * q + 3] + b.w;
+          *reinterpret_cast<float4*>(stage + r * ROW + (((kr >> 2) ^ (r & SWZ)) << 4)) = v;
+        }
+    }
+    // this block's residual (one block at a time, after the staging writes: registers are
+    // short here)
+    u32x4 rv[NI];
+    if (p.res) {
+#pragma unroll
+      for (int it = 0; it < NI; ++it) {
+        const int ml = pos0 + wm * WTM + 32 * j + it * RPI + lane / LPR;
+        rv[it] = __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)(((int64_t)ml * K + k0) * 2), 0, 0);
+      }
+    }
+    wait_lgkm0();
+    double* rb = rred + (j & 1) * (WGN * WGM * 32);
+#pragma unroll
+    for (int it = 0; it < NI; ++it) {
+      const int r = it * RPI + lane / LPR;
+      const float4 lo = *reinterpret_cast<const float4*>(stage + r * ROW + (((2 * g) ^ (r & SWZ)) << 4));
+      const float4 hi = *reinterpret_cast<const float4*>(stage + r * ROW + (((2 * g + 1) ^ (r & SWZ)) << 4));
+      float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      if (p.res) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[2 * e] += bf16_lo(rv[it][e]);
+          v[2 * e + 1] += bf16_hi(rv[it][e]);
+        }
+      }
+      double ss = 0.0;
+      u32x4 o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        o[e] = pack_bf16x2(v[2 * e], v[2 * e + 1]);
+        const double a = bf16_lo(o[e]), b = bf16_hi(o[e]);
+        ss = fma(a, a, ss);
+        ss = fma(b, b, ss);
+      }
+      // the rounded outputs wait in this wave's LDS area across the barrier below
+      *reinterpret_cast<u32x4*>(opark + (it * 64 + lane) * 16) = o;
+      // this wave's sum for the row: its LPR lanes, by DPP moves (in lane g == 0)
+      if (!kin) ss = 0.0;
+      ss = group_sum_dpp<LPR>(ss);
+      if (g == 0) rb[(wn * WGM + wm) * 32 + it * RPI + lane / LPR] = ss;
+    }
+    wait_lgkm0();                                    // staging reads and row sums done
+    stage_barrier();                                 // every wave's row sums of this block
+#pragma unroll
+    for (int it = 0; it < NI; ++it) {
+      const int r = it * RPI + lane / LPR;
+      double tot = rb[wm * 32 + r];
+#pragma unroll
+      for (int q = 1; q < WGN; ++q) tot += rb[(q * WGM + wm) * 32 + r];
+      const double rstd = 1.0 / sqrt(tot / (double)K + p.rms_eps);
+      // the lane's 8 gains from LDS (not held across the block: registers are short)
+      const float4 g0 = *reinterpret_cast<const float4*>(lgain + 8 * g);
+      const float4 g1 = *reinterpret_cast<const float4*>(lgain + 8 * g + 4);
+      const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+      Affine a[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        a[i].s = (double)gv[i] * rstd;
+        a[i].b = 0.0;
+      }
+      const u32x4 ovv = *reinterpret_cast<const u32x4*>(opark + (it * 64 + lane) * 16);
+      const uint4 o4 = make_uint4(ovv[0], ovv[1], ovv[2], ovv[3]);
+      const uint4 act = activate_packet(o4, a);
+      const int ml = pos0 + wm * WTM + 32 * j + r;
+      const uint32_t off = (uint32_t)(((int64_t)ml * K + k0) * 2);
+      if (kfull) {                                   // past the frame: dropped
+        u32x4 av;
+        av[0] = act.x;
+        av[1] = act.y;
+        av[2] = act.z;
+        av[3] = act.w;
+        __builtin_amdgcn_raw_buffer_store_b128(av, as, off, 0, 0);
+        if (p.y) __builtin_amdgcn_raw_buffer_store_b128(ovv, ys, off, 0, 0);
+      } else if (kin && ml < HW) {
+        const int64_t e0 = base + (int64_t)ml * K + k0;
+        if (k0 + 8 <= K) {
+          *reinterpret_cast<uint4*>(p.act + e0) = act;
+          if (p.y) *reinterpret_cast<uint4*>(p.y + e0) = o4;
+        } else {
+          *reinterpret_cast<uint2*>(p.act + e0) = make_uint2(act.x, act.y);
+          if (p.y) *reinterpret_cast<uint2*>(p.y + e0) = make_uint2(o4.x, o4.y);
+        }
+      }
+    }
+  }
 }
 
 // Statistics for the next GroupNorm, per workgroup: every lane's (S, Q) of the rounded
@@ -1284,7 +1462,25 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_slab_kernel(ConvParams
 
   static_assert(NW * 32 * WTN * 4 <= SLABS, "epilogue staging fits the weight stages");
   const float* lb = reinterpret_cast<const float*>(smem + LBIAS) + wn * WTN;
-  if (K % 8 == 0) {                                  // rows of y 16-byte aligned
+  // The next RMS norm in the epilogue (LDS: the waves' staging areas, the row sums, then
+  // each wave's parked outputs, NI x 64 lanes x 16 bytes).
+  bool rms_done = false;
+  if constexpr (MODE == kCausal) {
+    if (p.act) {
+      constexpr int RSUM = NW * 32 * WTN * 4, PARK = RSUM + 2 * NW * 32 * 8;
+      constexpr int NIP = 32 / (64 / (WTN / 8));
+      constexpr int GAIN = PARK + NW * NIP * 64 * 16;
+      static_assert(GAIN + NW * WTN * 4 <= SLABS + NSL * SLAB, "epilogue LDS");
+      store_tile_rms<TN, TM, WTM, WTN, WGM, WGN>(acc, p, n, t, pos0, ntile * BN + wn * WTN, wm, wn, lane, lb,
+                                                 smem + wave * (32 * WTN * 4),
+                                                 reinterpret_cast<double*>(smem + RSUM),
+                                                 smem + PARK + wave * (NIP * 64 * 16),
+                                                 reinterpret_cast<float*>(smem + GAIN) + wave * WTN);
+      rms_done = true;
+    }
+  }
+  if (rms_done) {
+  } else if (K % 8 == 0) {                           // rows of y 16-byte aligned
     const Sums sums = store_tile_staged<MODE, TN, TM, WTM, WTN>(
         acc, p, n, t, pos0, ntile * BN + wn * WTN, wm, lane, phase, lb, smem + wave * (32 * WTN * 4));
     static_assert(NW * 32 * WTN * 4 + NW * 64 * 16 <= SLABS + NSL * SLAB, "statistics area");
@@ -1551,6 +1747,7 @@ struct TileCfg {
   ConvFn fn;
   int lds;
   int threads;
+  bool rms_epilogue;   // the kernel applies the next RMS norm in its epilogue when p.act is set
 };
 
 template <int BM, int BN, int WGM, int WGN, int NS, int MODE, bool FUSE>
@@ -1561,6 +1758,7 @@ static TileCfg make_cfg(int c) {
   t.fn = conv_kernel<BM, BN, WGM, WGN, NS, MODE, FUSE>;
   t.lds = NS * (BM + BN) * kPK * 2 + (FUSE ? c * 16 : 0) + BN * 4;
   t.threads = 64 * WGM * WGN;
+  t.rms_epilogue = false;
   return t;
 }
 
@@ -1572,6 +1770,7 @@ static TileCfg make_slab_cfg() {
   t.fn = conv_slab_kernel<BM, BN, WGM, WGN, kSlabStages, MODE>;
   t.lds = slab_lds_bytes<BM, BN, kSlabStages, MODE>();
   t.threads = 64 * WGM * WGN;
+  t.rms_epilogue = MODE == kCausal;
   return t;
 }
 
@@ -1765,11 +1964,24 @@ static size_t next_stats_bytes(sgn_dims d, int k, int groups) {
   return fused > plain ? fused : plain;
 }
 
+// The RMS norm + SiLU of y requested by causal_conv3d_rms.
+struct RmsOut {
+  const float* gain;
+  float eps;
+  uint16_t* act;
+};
+
+// causal_conv3d_rms computes act in the epilogue for an unfused convolution whose one N
+// tile holds all K channels (128 < K <= 256, the 224-row slab tile); y may then be NULL.
+static bool rms_in_epilogue(int k, const sgn_gn* fuse) { return !fuse && k > 128 && k <= 256 && k % 8 == 0; }
+
 static int causal_conv_impl(const char* fn, const uint16_t* x, sgn_dims d, const uint16_t* cache_in,
                             const uint16_t* w, int k, const float* bias, const uint16_t* residual,
                             const sgn_gn* fuse, uint16_t* y, uint16_t* cache_out, const NextStats* ns,
-                            hipStream_t stream) {
-  if (!conv_common_checks(x, d, w, k, y, fn)) return SGN_EINVAL;
+                            hipStream_t stream, const RmsOut* ro = nullptr) {
+  const bool rms_epi = ro && rms_in_epilogue(k, fuse);
+  uint16_t* yo = y ? y : (rms_epi ? ro->act : nullptr);   // the conv's primary output
+  if (!conv_common_checks(x, d, w, k, yo, fn)) return SGN_EINVAL;
   int rc = check_fuse(fuse, d, fn);
   if (rc) return rc;
   if (!aligned16(x) || !aligned16(w) || !aligned16(y) || (cache_in && !aligned16(cache_in)) ||
@@ -1782,13 +1994,20 @@ static int causal_conv_impl(const char* fn, const uint16_t* x, sgn_dims d, const
   const size_t yb = (size_t)(d.n * d.t * d.h * d.w) * k * 2;
   const size_t cb = (size_t)(d.n * 2 * d.h * d.w * d.c) * 2;
   const size_t wb = (size_t)k * 27 * d.c * 2;
-  if (overlap(y, yb, x, xb) || overlap(y, yb, w, wb) || (cache_in && overlap(y, yb, cache_in, cb)) ||
-      (residual && overlap(y, yb, residual, yb)) ||
-      (cache_out && (overlap(cache_out, cb, x, xb) || overlap(cache_out, cb, y, yb) ||
+  if (overlap(yo, yb, x, xb) || overlap(yo, yb, w, wb) || (cache_in && overlap(yo, yb, cache_in, cb)) ||
+      (residual && overlap(yo, yb, residual, yb)) ||
+      (cache_out && (overlap(cache_out, cb, x, xb) || overlap(cache_out, cb, yo, yb) ||
                      overlap(cache_out, cb, w, wb) ||
                      (cache_in && overlap(cache_out, cb, cache_in, cb)) ||
                      (residual && overlap(cache_out, cb, residual, yb))))) {
     set_error("%s: an output overlaps an input or the other output", fn);
+    return SGN_EALIAS;
+  }
+  if (ro && ro->act != yo &&
+      (overlap(ro->act, yb, x, xb) || overlap(ro->act, yb, w, wb) || overlap(ro->act, yb, yo, yb) ||
+       (cache_in && overlap(ro->act, yb, cache_in, cb)) || (residual && overlap(ro->act, yb, residual, yb)) ||
+       (cache_out && overlap(ro->act, yb, cache_out, cb)))) {
+    set_error("%s: act overlaps an input or another output", fn);
     return SGN_EALIAS;
   }
   ConvParams p = {};
@@ -1813,6 +2032,17 @@ static int causal_conv_impl(const char* fn, const uint16_t* x, sgn_dims d, const
   p.mper = d.t * d.h * d.w;
   const TileCfg cfg = fuse ? choose_tile<kCausal, true>(d.h * d.w, d.t, k, p.C, d.n)
                            : choose_tile<kCausal, false>(d.h * d.w, d.t, k, p.C, d.n);
+  if (rms_epi) {
+    // y may be NULL here: only a kernel with the RMS epilogue (which never stores a NULL y)
+    // may take this call.
+    if (!cfg.rms_epilogue || cfg.bn < k) {
+      set_error("%s: internal: the chosen tile cannot apply the RMS norm in its epilogue", fn);
+      return SGN_EINVAL;
+    }
+    p.act = ro->act;
+    p.rms_gain = ro->gain;
+    p.rms_eps = (double)ro->eps;
+  }
   // Statistics of y from the epilogue when its lanes hold whole 8-channel slices of one group
   // inside one N tile; otherwise from gn_silu_stats over y after the convolution.
   const int ncg = ns ? k / ns->groups : 0;
@@ -1824,6 +2054,12 @@ static int causal_conv_impl(const char* fn, const uint16_t* x, sgn_dims d, const
   }
   if (!launch_conv(cfg, p, d.n, 1, stream, fn)) return SGN_ELAUNCH;
   if (cache_out && !launch_cache_out(x, d, cache_in, fuse, cache_out, stream)) return SGN_ELAUNCH;
+  if (ro && !rms_epi) {                              // act from y by the RMS norm kernel
+    sgn_dims yd = d;
+    yd.c = k;
+    const int rc = rms_silu(y, yd, ro->gain, ro->eps, ro->act, stream);
+    if (rc != SGN_OK) return rc;
+  }
   if (in_epilogue) {
     const double length = (double)ncg * (double)(d.t * d.h * d.w);
     if (!launch_gn_finalize(p.nws, (int)(d.t * p.tiles_f), ns->groups, d.n, length, ns->stats, stream))
@@ -1863,6 +2099,36 @@ extern "C" int causal_conv3d(const uint16_t* x, sgn_dims d, const uint16_t* cach
   clear_error();
   return causal_conv_impl("causal_conv3d", x, d, cache_in, w, k, bias, residual, fuse, y, cache_out,
                           nullptr, stream);
+}
+
+extern "C" int causal_conv3d_rms(const uint16_t* x, sgn_dims d, const uint16_t* cache_in, const uint16_t* w,
+                                 int k, const float* bias, const uint16_t* residual, const sgn_gn* fuse,
+                                 const float* gain, float eps, uint16_t* y, uint16_t* act, uint16_t* cache_out,
+                                 hipStream_t stream) {
+  const char* fn = "causal_conv3d_rms";
+  clear_error();
+  if (!gain || !act) {
+    set_error("%s: gain and act are required", fn);
+    return SGN_EINVAL;
+  }
+  if (!(eps > 0.0f) || !isfinite(eps)) {
+    set_error("%s: eps must be a positive finite number", fn);
+    return SGN_EINVAL;
+  }
+  if (k % 64 != 0) {
+    set_error("%s: K=%d must be a multiple of 64 (the RMS norm's channels)", fn, k);
+    return SGN_EINVAL;
+  }
+  if (!y && !rms_in_epilogue(k, fuse)) {
+    set_error("%s: y may be NULL only when the epilogue applies the norm (unfused, 128 < K <= 256)", fn);
+    return SGN_EINVAL;
+  }
+  if (((uintptr_t)gain & 3) || !aligned16(act)) {
+    set_error("%s: act must be 16-byte and gain 4-byte aligned", fn);
+    return SGN_EALIGN;
+  }
+  const RmsOut ro = {gain, eps, act};
+  return causal_conv_impl(fn, x, d, cache_in, w, k, bias, residual, fuse, y, cache_out, nullptr, stream, &ro);
 }
 
 extern "C" size_t causal_conv3d_next_stats_workspace(sgn_dims d, int k, int next_groups) {

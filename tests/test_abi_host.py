@@ -134,6 +134,26 @@ def test_conv_rejects():
          EINVAL)
 
 
+def test_conv_rms_rejects():
+    lib = sga.load_library()
+    far = FAKE + (1 << 32)
+    w = FAKE + (1 << 30)
+    act = FAKE + (1 << 34)
+
+    def call(k=256, gain=FAKE + (1 << 35), eps=1e-6, y=far, a=act, fuse=None):
+        return lib.causal_conv3d_rms(FAKE, D(), None, w, k, None, None, fuse, gain, eps, y, a, None, None)
+    _err(call(gain=None), EINVAL)
+    _err(call(a=None), EINVAL)
+    _err(call(eps=0.0), EINVAL)
+    _err(call(k=200), EINVAL)                           # K % 64
+    _err(call(k=512, y=None), EINVAL)                   # y may be NULL only in the epilogue form
+    _err(call(k=128, y=None), EINVAL)
+    _err(call(gain=FAKE + (1 << 35) + 2), EALIGN)
+    _err(call(a=act + 8), EALIGN)
+    _err(call(a=far + 64), EALIAS)                      # act inside y
+    _err(call(a=FAKE + 64), EALIAS)                     # act inside x
+
+
 def test_next_stats_workspace_size():
     lib = sga.load_library()
     ws = lib.causal_conv3d_next_stats_workspace(D(), 256, 32)

@@ -270,3 +270,84 @@ def test_conv_next_stats_fullres_workload():
     ref = sga.gn_silu_stats(y, wl.groups)
     torch.cuda.synchronize()
     np.testing.assert_allclose(st.cpu().numpy(), ref.cpu().numpy(), rtol=1e-12, atol=1e-14)
+
+
+@pytest.mark.parametrize("shape,k,res,store_y,fused", [
+    ((1, 2, 5, 7, 64), 256, False, True, False),     # the epilogue applies the norm (one N tile)
+    ((1, 3, 17, 19, 128), 256, True, False, False),  # ... y not stored, residual
+    ((2, 2, 9, 30, 64), 192, True, True, False),     # ... K = 192: the last wave's channels all past K
+    ((1, 2, 3, 5, 64), 128, False, True, False),     # K <= 128: the conv, then rms_silu over y
+    ((1, 2, 3, 5, 64), 512, True, True, False),      # two N tiles: the conv, then rms_silu
+    ((1, 2, 5, 6, 256), 256, False, True, True),     # GroupNorm fused in: the conv, then rms_silu
+])
+def test_conv_rms(shape, k, res, store_y, fused):
+    """causal_conv3d_rms: y bitwise as causal_conv3d; act within 1 ulp of rms_silu(y) and close
+    to the oracle's composition (its conv rounded once, then its RMS norm)."""
+    from oracle import rmsnorm as orms
+    from oracle import bf16 as obf16
+    print("case conv rms", shape, k, res, store_y, fused, flush=True)
+    n, t, h, w, c = shape
+    seed = n + t + h + w + c + k + 5
+    x = sg.normal(shape, seed, sg.X)
+    wt = _w(k, c, seed)
+    ci = sg.normal((n, 2, h, w, c), seed, sg.X_PREV)
+    b = sg.normal((k,), seed, sg.BETA2, std=0.5, dtype=torch.float32)
+    r = sg.normal((n, t, h, w, k), seed, sg.GAMMA2) if res else None
+    gain = sg.normal((k,), seed, sg.GAMMA1, std=0.2, mean=1.0, dtype=torch.float32)
+    xd, wd, cd, bd, gd = (v.to(DEV) for v in (x, wt, ci, b, gain))
+    rd = r.to(DEV) if res else None
+    fuse = None
+    if fused:
+        gamma, beta = _gn_params(c, seed)
+        fuse = (sga.gn_silu_stats(xd, 32), gamma.to(DEV), beta.to(DEV), 1e-5, 32)
+    y, act = sga.causal_conv3d_rms(xd, wd, gd, 1e-6, cd, bd, rd, fuse=fuse, store_y=store_y)
+    y_ref = sga.causal_conv3d(xd, wd, cd, bd, rd, fuse=fuse)
+    act_ref = sga.rms_silu(y_ref, gd, 1e-6)
+    torch.cuda.synchronize()
+    if store_y:
+        assert torch.equal(y.view(torch.int16), y_ref.view(torch.int16))
+    d = obf16.ulp_distance(bits(act), bits(act_ref))
+    print("  act vs rms_silu(y): max ulp %d, exact %.5f" % (d.max(), (d == 0).mean()), flush=True)
+    assert d.max() <= 1
+    if not fused:
+        o, _ = oconv.causal_conv3d(vals(x), vals(wt), vals(ci), b.numpy(), vals(r) if res else None)
+        oa = orms.rms_silu(obf16.decode(obf16.round_rne(o)), gain.numpy(), 1e-6)
+        assert_conv_close(bits(act), oa, "act vs oracle")
+
+
+def test_conv_rms_large_tile():
+    """[1,16,64,64,64] -> K = 256: 256 tiles of 256 rows fill one wave of the chip, so the
+    256 x 256 tile (not the 224-row one) runs the RMS epilogue; y bitwise as causal_conv3d,
+    act within 1 ulp of rms_silu(y), with a residual and y stored."""
+    shape, k = (1, 16, 64, 64, 64), 256
+    seed = 123
+    x = sg.normal(shape, seed, sg.X).to(DEV)
+    wt = _w(k, 64, seed).to(DEV)
+    r = sg.normal(shape[:4] + (k,), seed, sg.GAMMA2).to(DEV)
+    gain = sg.normal((k,), seed, sg.GAMMA1, std=0.2, mean=1.0, dtype=torch.float32).to(DEV)
+    print("case conv rms large tile", flush=True)
+    y, act = sga.causal_conv3d_rms(x, wt, gain, 1e-6, residual=r)
+    y_ref = sga.causal_conv3d(x, wt, residual=r)
+    act_ref = sga.rms_silu(y_ref, gain, 1e-6)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y_ref.view(torch.int16))
+    d = (act.view(torch.int16).int() - act_ref.view(torch.int16).int()).abs()
+    assert int(d.max()) <= 1
+
+
+@pytest.mark.slow
+def test_conv_rms_fullres():
+    """The full-resolution conv (C = K = 256 at [1,16,352,624]) with the RMS norm in its
+    epilogue and y not stored: act within 1 ulp of rms_silu over causal_conv3d's y."""
+    wl = WORKLOADS[4]
+    x = wl.x(device=DEV)
+    wt = wl.conv_weight(1, DEV)
+    gain = wl.gamma(2, DEV)
+    print("case conv rms fullres", flush=True)
+    _, act = sga.causal_conv3d_rms(x, wt, gain, 1e-6, store_y=False)
+    y_ref = sga.causal_conv3d(x, wt)
+    act_ref = sga.rms_silu(y_ref, gain, 1e-6)
+    torch.cuda.synchronize()
+    d = (act.view(torch.int16).int() - act_ref.view(torch.int16).int()).abs()
+    print("  max |bit difference| %d, differing %d" % (int(d.max()), int((d > 0).sum())), flush=True)
+    assert int(d.max()) <= 1
