@@ -1122,7 +1122,9 @@ __device__ __forceinline__ void wait_vm_n(int n) {
   }
 }
 
-template <int BM, int BN, int WGM, int WGN, int NS, int MODE>
+// RMS: the instantiation that can apply the next RMS norm in its epilogue (a separate one,
+// so that the plain convolution keeps its spill-free register allocation).
+template <int BM, int BN, int WGM, int WGN, int NS, int MODE, bool RMS = false>
 __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_slab_kernel(ConvParams p) {
   static_assert(MODE == kCausal || MODE == kPhase || MODE == kTime, "slab modes");
   constexpr int INNER = slab_inner(MODE);            // column taps per group
@@ -1465,7 +1467,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_slab_kernel(ConvParams
   // The next RMS norm in the epilogue (LDS: the waves' staging areas, the row sums, then
   // each wave's parked outputs, NI x 64 lanes x 16 bytes).
   bool rms_done = false;
-  if constexpr (MODE == kCausal) {
+  if constexpr (MODE == kCausal && RMS) {
     if (p.act) {
       constexpr int RSUM = NW * 32 * WTN * 4, PARK = RSUM + 2 * NW * 32 * 8;
       constexpr int NIP = 32 / (64 / (WTN / 8));
@@ -1762,15 +1764,15 @@ static TileCfg make_cfg(int c) {
   return t;
 }
 
-template <int BM, int BN, int WGM, int WGN, int MODE>
+template <int BM, int BN, int WGM, int WGN, int MODE, bool RMS = false>
 static TileCfg make_slab_cfg() {
   TileCfg t;
   t.bm = BM;
   t.bn = BN;
-  t.fn = conv_slab_kernel<BM, BN, WGM, WGN, kSlabStages, MODE>;
+  t.fn = conv_slab_kernel<BM, BN, WGM, WGN, kSlabStages, MODE, RMS>;
   t.lds = slab_lds_bytes<BM, BN, kSlabStages, MODE>();
   t.threads = 64 * WGM * WGN;
-  t.rms_epilogue = MODE == kCausal;
+  t.rms_epilogue = MODE == kCausal && RMS;
   return t;
 }
 
@@ -2030,8 +2032,10 @@ static int causal_conv_impl(const char* fn, const uint16_t* x, sgn_dims d, const
   p.C = (int)d.c;
   p.K = k;
   p.mper = d.t * d.h * d.w;
-  const TileCfg cfg = fuse ? choose_tile<kCausal, true>(d.h * d.w, d.t, k, p.C, d.n)
-                           : choose_tile<kCausal, false>(d.h * d.w, d.t, k, p.C, d.n);
+  TileCfg cfg = fuse ? choose_tile<kCausal, true>(d.h * d.w, d.t, k, p.C, d.n)
+                     : choose_tile<kCausal, false>(d.h * d.w, d.t, k, p.C, d.n);
+  if (rms_epi)      // the same tile, in its instantiation with the RMS epilogue
+    cfg = cfg.bm == 256 ? make_slab_cfg<256, 256, 2, 2, kCausal, true>() : make_slab_cfg<224, 256, 1, 4, kCausal, true>();
   if (rms_epi) {
     // y may be NULL here: only a kernel with the RMS epilogue (which never stores a NULL y)
     // may take this call.
