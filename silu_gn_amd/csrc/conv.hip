@@ -1,6 +1,8 @@
 // Implicit-GEMM convolutions on bf16 MFMA (gfx950): the causal 3x3x3 convolution with
-// its 2-frame cache, the nearest-x2 upsample as four 2x2 phase convolutions, and the
-// output head with its 2x2 depth-to-space.
+// its 2-frame cache, the nearest-x2 upsample as four 2x2 phase convolutions (optionally
+// with an up block's DupUp3D shortcut), an up block's causal 3x1x1 temporal x2, and the
+// output head with its 2x2 depth-to-space. Epilogues can also emit the next GroupNorm's
+// statistics or apply the next RMS norm + SiLU.
 //
 // GEMM view (per sample, per upsample phase):
 //   D[k][m] = sum_{tap, c} W[k][tap][c] * P[src(m, tap)][c]
@@ -17,7 +19,9 @@
 // 2 frames of the padded input, bias and residual in the epilogue), prepare() and
 // Decoder::up (the four 2x2 phase convolutions of nearest-x2 + 3x3, interleaved with the
 // bias), Decoder::output_head (the head convolution to 12 = 3 x 2 x 2 channels, bias,
-// clamp) and decode_video's write of the 2x2-unfolded RGB video.
+// clamp) and decode_video's write of the 2x2-unfolded RGB video; Decoder::up_block (the
+// temporal x2 after the resnets, the DupUp3D shortcut in the resampler's last pass) and
+// Decoder's `prepared` edge (the next norm applied by the producing convolution).
 #include <math.h>
 #include <stdio.h>
 

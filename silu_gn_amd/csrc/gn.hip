@@ -11,6 +11,9 @@
 // Apply (gn_silu_apply): one read and one write; each thread forms the fp64 affine of
 // its 8 channels once and then streams packets through activate_packet().
 //
+// RMS norm + SiLU (rms_silu): the decoder's per-position norm, one read and one write,
+// the same activate_packet() with the affine gain * rstd.
+//
 // Pages: WanGP group_norm_silu.py (module docstring: exact partial sums reduced in
 // fp64 in a fixed order, one rounding to the output dtype; its apply kernel: biased
 // variance, rstd = 1/sqrt(var + eps), y * sigmoid(y)). The pages' second, centred pass
