@@ -87,7 +87,8 @@ size_t gn_silu_stats_workspace(sgn_dims d, int groups);
  *   stats[(n*G + g)*2 + 0] = mean,  stats[(n*G + g)*2 + 1] = biased variance,
  * both fp64. x: bf16 (N,T,H,W,C). ws: device workspace of at least
  * gn_silu_stats_workspace(d, groups) bytes, overwritten. C % groups == 0 and
- * C/groups must be 1, 2, 4 or a multiple of 8; C <= 2048.
+ * C/groups must be 1, 2, 4 or a multiple of 8; C <= 2048. x, stats and ws must not
+ * overlap (SGN_EALIAS).
  */
 int gn_silu_stats(const uint16_t* x, sgn_dims d, int groups, double* stats,
                   void* ws, size_t ws_bytes, hipStream_t stream);
@@ -187,6 +188,29 @@ int causal_conv3d_rms(const uint16_t* x, sgn_dims d, const uint16_t* cache_in,
 int causal_conv3d_eligible(sgn_dims d, int k, int fuse_groups);
 
 /*
+ * sgn_conv_plan -- which kernel and tile a convolution call would run, without running
+ * it (a predicate-style query beside causal_conv3d_eligible, as the group_norm_silu.py
+ * page separates its eligibility check from compute). No device work.
+ *   op     SGN_OP_CAUSAL (causal_conv3d / causal_conv3d_next_stats / causal_conv3d_rms;
+ *          fused != 0 for a fused GroupNorm), SGN_OP_PHASES (upsample2x_conv_phases[_shortcut]:
+ *          d = the low-resolution input), SGN_OP_TIME (time_upsample_conv: d.t = the frames
+ *          convolved, T - first; k is ignored, K = 2C)
+ *   plan   receives the kernel (SGN_KERNEL_SLAB: the slab kernel whose three column taps
+ *          share one staged slab; SGN_KERNEL_GENERIC: the per-tap kernel), the tile
+ *          (output positions x output channels per workgroup) and the workgroup count.
+ * Returns SGN_OK, or SGN_EINVAL for a shape the call would reject. The dedicated output
+ * head kernel is not covered (head_conv_d2s picks it for unfused C = 128 or 256).
+ */
+enum { SGN_OP_CAUSAL = 0, SGN_OP_PHASES = 1, SGN_OP_TIME = 2 };
+enum { SGN_KERNEL_SLAB = 1, SGN_KERNEL_GENERIC = 2 };
+typedef struct {
+  int kernel;
+  int tile_m, tile_n;
+  int64_t workgroups;
+} sgn_plan;
+int sgn_conv_plan(int op, sgn_dims d, int k, int fused, sgn_plan* plan);
+
+/*
  * Bytes of device workspace causal_conv3d_next_stats needs for input dims d, K
  * output channels and next_groups groups (0 if the arguments are invalid).
  */
@@ -213,8 +237,8 @@ size_t causal_conv3d_next_stats_workspace(sgn_dims d, int k, int next_groups);
  * multiple of 8 dividing the kernel's N tile; otherwise gn_silu_stats runs over y.
  * Errors: next_groups must divide K and y's GroupNorm must be one gn_silu_stats
  * accepts (K % 8 == 0; K/G = 1, 2, 4 or a multiple of 8), else SGN_EINVAL; a
- * missing or short workspace is SGN_EWORKSPACE; ws, next_stats and y must not
- * overlap (SGN_EALIAS).
+ * missing or short workspace is SGN_EWORKSPACE; ws and next_stats must not overlap
+ * each other, y or any input (SGN_EALIAS).
  */
 int causal_conv3d_next_stats(const uint16_t* x, sgn_dims d, const uint16_t* cache_in,
                              const uint16_t* w, int k, const float* bias,

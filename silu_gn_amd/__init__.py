@@ -1,10 +1,12 @@
 """Python binding of libsilugn.so (argument marshalling only).
 
 Every function here has the name of the C entry point it calls (see
-include/silugn.h) and takes torch tensors for the buffers; the tensors' device
-pointers and the current HIP stream are handed to the library, which does all
-of the work in its gfx950 kernels. There is no fallback: if the library is not
-built, or a call fails, an exception is raised.
+include/silugn.h) and takes torch tensors for the buffers. Each tensor is
+checked first (dtype, shape against x and the weights, contiguity, device),
+because the C side sees only pointers; then the tensors' device pointers and the
+current HIP stream are handed to the library, which does all of the work in
+its gfx950 kernels. There is no fallback: if the library is not built, or a
+call fails, an exception is raised.
 """
 from __future__ import annotations
 
@@ -35,7 +37,15 @@ class sgn_gn(ctypes.Structure):
                 ("eps", ctypes.c_float), ("groups", ctypes.c_int)]
 
 
-EXPORTS = ["sgn_last_error", "gn_silu_eligible", "causal_conv3d_eligible", "gn_silu_stats_workspace", "gn_silu_stats", "gn_silu_apply", "rms_silu",
+class sgn_plan(ctypes.Structure):
+    _fields_ = [("kernel", ctypes.c_int), ("tile_m", ctypes.c_int), ("tile_n", ctypes.c_int),
+                ("workgroups", ctypes.c_int64)]
+
+
+SGN_OP_CAUSAL, SGN_OP_PHASES, SGN_OP_TIME = 0, 1, 2
+SGN_KERNELS = {1: "slab", 2: "generic"}
+
+EXPORTS = ["sgn_last_error", "gn_silu_eligible", "causal_conv3d_eligible", "sgn_conv_plan", "gn_silu_stats_workspace", "gn_silu_stats", "gn_silu_apply", "rms_silu",
            "causal_conv3d", "causal_conv3d_rms", "causal_conv3d_next_stats_workspace", "causal_conv3d_next_stats",
            "upsample2x_prepare_weights", "upsample2x_conv_phases", "upsample2x_conv_phases_shortcut",
            "time_upsample_conv", "head_conv_d2s"]
@@ -57,6 +67,7 @@ def load_library(path: str = LIB_PATH):
         "sgn_last_error": (ctypes.c_char_p, []),
         "gn_silu_eligible": (i32, [sgn_dims, i32]),
         "causal_conv3d_eligible": (i32, [sgn_dims, i32, i32]),
+        "sgn_conv_plan": (i32, [i32, sgn_dims, i32, i32, ctypes.POINTER(sgn_plan)]),
         "gn_silu_stats_workspace": (sz, [sgn_dims, i32]),
         "gn_silu_stats": (i32, [vp, sgn_dims, i32, vp, vp, sz, vp]),
         "gn_silu_apply": (i32, [vp, sgn_dims, i32, vp, vp, vp, f32, vp, vp]),
@@ -95,15 +106,61 @@ def _dims(x):
 
 
 def _stream(x):
+    """torch's current stream on x's device (the last check before a call: x is on a GPU)."""
+    if x.device.type != "cuda":
+        raise ValueError("x must be a GPU tensor, got one on %s" % x.device)
     return torch.cuda.current_stream(x.device).cuda_stream
 
 
-def _gn(fuse):
-    """(stats, gamma, beta, eps, groups) -> sgn_gn pointer, or None."""
+def _arg(t, name, dtype, shape=None, device=None, ndim=None):
+    """Check one tensor argument before its pointer reaches the library: the C side sees
+    only a pointer, so a wrong dtype, a strided view, a wrong shape or a tensor on another
+    device would make it read or write the wrong bytes. ``shape`` entries of None are not
+    checked. Raises TypeError (not a tensor, wrong dtype) or ValueError (anything else)."""
+    if not torch.is_tensor(t):
+        raise TypeError("%s must be a torch tensor, got %s" % (name, type(t).__name__))
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError("%s must have %d dimensions, got shape %s" % (name, ndim, tuple(t.shape)))
+    if shape is not None:
+        if t.dim() != len(shape) or any(s is not None and s != d for s, d in zip(shape, t.shape)):
+            want = "(" + ", ".join("*" if s is None else str(s) for s in shape) + ")"
+            raise ValueError("%s must have shape %s, got %s" % (name, want, tuple(t.shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous (the library reads dense row-major memory)" % name)
+    if device is not None and t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+    return t
+
+
+def _act(x, name="x"):
+    """A bf16 channels-last activation (N, T, H, W, C): the argument the others follow (their
+    device must be x's; that x is on a GPU is checked last, by _stream)."""
+    return _arg(x, name, torch.bfloat16, ndim=5)
+
+
+def _opt(t, name, dtype, shape, device):
+    return None if t is None else _arg(t, name, dtype, shape, device)
+
+
+def _workspace(ws, need, device):
+    _arg(ws, "ws", ws.dtype, None, device)
+    if ws.numel() * ws.element_size() < need:
+        raise ValueError("ws holds %d bytes, %d are needed" % (ws.numel() * ws.element_size(), need))
+    return ws
+
+
+def _gn(fuse, n, c, device):
+    """(stats, gamma, beta, eps, groups) -> (sgn_gn pointer, keep-alive), or (None, None)."""
     if fuse is None:
         return None, None
     stats, gamma, beta, eps, groups = fuse
-    s = sgn_gn(stats.data_ptr(), gamma.data_ptr(), beta.data_ptr(), float(eps), int(groups))
+    groups = int(groups)
+    _arg(stats, "fuse stats", torch.float64, (n, groups, 2), device)
+    _arg(gamma, "fuse gamma", torch.float32, (c,), device)
+    _arg(beta, "fuse beta", torch.float32, (c,), device)
+    s = sgn_gn(stats.data_ptr(), gamma.data_ptr(), beta.data_ptr(), float(eps), groups)
     return ctypes.pointer(s), s
 
 
@@ -115,6 +172,13 @@ def causal_conv3d_eligible(dims, k: int, fuse_groups: int = 0) -> bool:
     return bool(load_library().causal_conv3d_eligible(sgn_dims(*dims), k, fuse_groups))
 
 
+def sgn_conv_plan(op: int, dims, k: int, fused: bool = False) -> dict:
+    """The kernel ("slab" / "generic"), tile and workgroup count a convolution call would run."""
+    p = sgn_plan()
+    _check(load_library().sgn_conv_plan(int(op), sgn_dims(*dims), int(k), int(bool(fused)), ctypes.byref(p)))
+    return {"kernel": SGN_KERNELS[p.kernel], "tile_m": p.tile_m, "tile_n": p.tile_n, "workgroups": p.workgroups}
+
+
 def gn_silu_stats_workspace(dims, groups: int) -> int:
     return int(load_library().gn_silu_stats_workspace(sgn_dims(*dims), groups))
 
@@ -122,12 +186,15 @@ def gn_silu_stats_workspace(dims, groups: int) -> int:
 def gn_silu_stats(x, groups: int, stats=None, ws=None):
     """fp64 [N, G, 2] (mean, biased variance) of bf16 NDHWC ``x``."""
     lib = load_library()
-    d = _dims(x)
-    if stats is None:
-        stats = torch.empty((x.shape[0], groups, 2), dtype=torch.float64, device=x.device)
+    _act(x)
+    d, dev, groups = _dims(x), x.device, int(groups)
     need = lib.gn_silu_stats_workspace(d, groups)
+    if stats is None:
+        stats = torch.empty((x.shape[0], groups, 2), dtype=torch.float64, device=dev)
+    _arg(stats, "stats", torch.float64, (x.shape[0], groups, 2), dev)
     if ws is None:
-        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    _workspace(ws, need, dev)
     _check(lib.gn_silu_stats(_ptr(x), d, groups, _ptr(stats), _ptr(ws), ws.numel() * ws.element_size(),
                              _stream(x)))
     return stats
@@ -136,8 +203,14 @@ def gn_silu_stats(x, groups: int, stats=None, ws=None):
 def gn_silu_apply(x, groups: int, stats, gamma, beta, eps: float, y=None):
     """bf16 silu(group_norm(x)); ``y`` may be ``x`` (in place)."""
     lib = load_library()
+    _act(x)
+    dev, (n, c), groups = x.device, (x.shape[0], x.shape[4]), int(groups)
+    _arg(stats, "stats", torch.float64, (n, groups, 2), dev)
+    _arg(gamma, "gamma", torch.float32, (c,), dev)
+    _arg(beta, "beta", torch.float32, (c,), dev)
     if y is None:
         y = torch.empty_like(x)
+    _arg(y, "y", torch.bfloat16, tuple(x.shape), dev)
     _check(lib.gn_silu_apply(_ptr(x), _dims(x), groups, _ptr(stats), _ptr(gamma), _ptr(beta),
                              float(eps), _ptr(y), _stream(x)))
     return y
@@ -146,10 +219,28 @@ def gn_silu_apply(x, groups: int, stats, gamma, beta, eps: float, y=None):
 def rms_silu(x, gain, eps: float, y=None):
     """bf16 silu(rms_norm(x)) per position over the channels; ``y`` may be ``x`` (in place)."""
     lib = load_library()
+    _act(x)
+    _arg(gain, "gain", torch.float32, (x.shape[4],), x.device)
     if y is None:
         y = torch.empty_like(x)
+    _arg(y, "y", torch.bfloat16, tuple(x.shape), x.device)
     _check(lib.rms_silu(_ptr(x), _dims(x), _ptr(gain), float(eps), _ptr(y), _stream(x)))
     return y
+
+
+def _conv_args(x, w, cache_in, bias, residual, y, cache_out, k=None):
+    """Checks shared by the causal convolutions; returns (K, y)."""
+    _act(x)
+    n, t, h, wd, c = x.shape
+    dev = x.device
+    _arg(w, "w", torch.bfloat16, (k, 3, 3, 3, c), dev)
+    k = w.shape[0]
+    _opt(cache_in, "cache_in", torch.bfloat16, (n, 2, h, wd, c), dev)
+    _opt(bias, "bias", torch.float32, (k,), dev)
+    _opt(residual, "residual", torch.bfloat16, (n, t, h, wd, k), dev)
+    _opt(cache_out, "cache_out", torch.bfloat16, (n, 2, h, wd, c), dev)
+    _opt(y, "y", torch.bfloat16, (n, t, h, wd, k), dev)
+    return k
 
 
 def causal_conv3d(x, w, cache_in=None, bias=None, residual=None, fuse=None, y=None, cache_out=None):
@@ -158,10 +249,10 @@ def causal_conv3d(x, w, cache_in=None, bias=None, residual=None, fuse=None, y=No
     Returns y (bf16 N,T,H,W,K); ``cache_out`` (if given) receives the last 2 frames of the padded input.
     """
     lib = load_library()
-    k = w.shape[0]
+    k = _conv_args(x, w, cache_in, bias, residual, y, cache_out)
+    gp, _keep = _gn(fuse, x.shape[0], x.shape[4], x.device)
     if y is None:
         y = torch.empty(x.shape[:4] + (k,), dtype=torch.bfloat16, device=x.device)
-    gp, _keep = _gn(fuse)
     _check(lib.causal_conv3d(_ptr(x), _dims(x), _ptr(cache_in), _ptr(w), k, _ptr(bias), _ptr(residual),
                              gp, _ptr(y), _ptr(cache_out), _stream(x)))
     return y
@@ -172,12 +263,14 @@ def causal_conv3d_rms(x, w, gain, eps: float, cache_in=None, bias=None, residual
     """causal_conv3d and act = rms_silu(y); returns (y or None, act). ``store_y=False`` skips y
     (allowed when the epilogue applies the norm: unfused, 128 < K <= 256)."""
     lib = load_library()
-    k = w.shape[0]
+    k = _conv_args(x, w, cache_in, bias, residual, y, cache_out)
+    _arg(gain, "gain", torch.float32, (k,), x.device)
+    _opt(act, "act", torch.bfloat16, tuple(x.shape[:4]) + (k,), x.device)
+    gp, _keep = _gn(fuse, x.shape[0], x.shape[4], x.device)
     if y is None and store_y:
         y = torch.empty(x.shape[:4] + (k,), dtype=torch.bfloat16, device=x.device)
     if act is None:
         act = torch.empty(x.shape[:4] + (k,), dtype=torch.bfloat16, device=x.device)
-    gp, _keep = _gn(fuse)
     _check(lib.causal_conv3d_rms(_ptr(x), _dims(x), _ptr(cache_in), _ptr(w), k, _ptr(bias), _ptr(residual), gp,
                                  _ptr(gain), float(eps), _ptr(y), _ptr(act), _ptr(cache_out), _stream(x)))
     return y, act
@@ -191,16 +284,19 @@ def causal_conv3d_next_stats(x, w, next_groups: int, cache_in=None, bias=None, r
                              y=None, cache_out=None, stats=None, ws=None):
     """causal_conv3d, plus the GroupNorm statistics (fp64 [N, G, 2]) of its output; returns (y, stats)."""
     lib = load_library()
-    k = w.shape[0]
-    if y is None:
-        y = torch.empty(x.shape[:4] + (k,), dtype=torch.bfloat16, device=x.device)
-    if stats is None:
-        stats = torch.empty((x.shape[0], next_groups, 2), dtype=torch.float64, device=x.device)
-    d = _dims(x)
+    k = _conv_args(x, w, cache_in, bias, residual, y, cache_out)
+    gp, _keep = _gn(fuse, x.shape[0], x.shape[4], x.device)
+    next_groups = int(next_groups)
+    d, dev = _dims(x), x.device
     need = lib.causal_conv3d_next_stats_workspace(d, k, next_groups)
+    if y is None:
+        y = torch.empty(x.shape[:4] + (k,), dtype=torch.bfloat16, device=dev)
+    if stats is None:
+        stats = torch.empty((x.shape[0], next_groups, 2), dtype=torch.float64, device=dev)
+    _arg(stats, "stats", torch.float64, (x.shape[0], next_groups, 2), dev)
     if ws is None:
-        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
-    gp, _keep = _gn(fuse)
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    _workspace(ws, need, dev)
     _check(lib.causal_conv3d_next_stats(_ptr(x), d, _ptr(cache_in), _ptr(w), k, _ptr(bias), _ptr(residual), gp,
                                         _ptr(y), _ptr(cache_out), next_groups, _ptr(stats), _ptr(ws),
                                         ws.numel() * ws.element_size(), _stream(x)))
@@ -211,16 +307,27 @@ def upsample2x_prepare_weights(w3x3):
     """Host: bf16 (K,3,3,C) -> bf16 phase weights (2,2,K,2,2,C) (CPU tensors)."""
     lib = load_library()
     w = w3x3.detach().to("cpu").contiguous()
+    _arg(w, "w3x3", torch.bfloat16, (None, 3, 3, None))
     k, _, _, c = w.shape
     out = torch.empty((2, 2, k, 2, 2, c), dtype=torch.bfloat16)
     _check(lib.upsample2x_prepare_weights(w.data_ptr(), k, c, out.data_ptr()))
     return out
 
 
+def _phase_args(x, w_phase, bias, y):
+    _act(x)
+    n, t, h, wd, c = x.shape
+    _arg(w_phase, "w_phase", torch.bfloat16, (2, 2, None, 2, 2, c), x.device)
+    k = w_phase.shape[2]
+    _opt(bias, "bias", torch.float32, (k,), x.device)
+    _opt(y, "y", torch.bfloat16, (n, t, 2 * h, 2 * wd, k), x.device)
+    return k
+
+
 def upsample2x_conv_phases(x, w_phase, bias=None, y=None):
     """Nearest-x2 + 3x3 conv via four 2x2 phases; y bf16 (N,T,2H,2W,K)."""
     lib = load_library()
-    k = w_phase.shape[2]
+    k = _phase_args(x, w_phase, bias, y)
     n, t, h, wd, _ = x.shape
     if y is None:
         y = torch.empty((n, t, 2 * h, 2 * wd, k), dtype=torch.bfloat16, device=x.device)
@@ -231,8 +338,9 @@ def upsample2x_conv_phases(x, w_phase, bias=None, y=None):
 def upsample2x_conv_phases_shortcut(x, w_phase, shortcut, ft: int, first: bool, bias=None, y=None):
     """upsample2x_conv_phases plus the DupUp3D shortcut of ``shortcut`` (the block input)."""
     lib = load_library()
-    k = w_phase.shape[2]
+    k = _phase_args(x, w_phase, bias, y)
     n, t, h, wd, _ = x.shape
+    _arg(shortcut, "shortcut", torch.bfloat16, (n, None, h, wd, None), x.device)
     if y is None:
         y = torch.empty((n, t, 2 * h, 2 * wd, k), dtype=torch.bfloat16, device=x.device)
     _check(lib.upsample2x_conv_phases_shortcut(_ptr(x), _dims(x), _ptr(w_phase), k, _ptr(bias), _ptr(shortcut),
@@ -243,10 +351,18 @@ def upsample2x_conv_phases_shortcut(x, w_phase, shortcut, ft: int, first: bool, 
 def time_upsample_conv(x, w, first: bool, cache_in=None, bias=None, y=None, cache_out=None):
     """Temporal x2: causal 3x1x1 conv to 2C channels, halves to frames; y (N, first + 2 (T - first), H, W, C)."""
     lib = load_library()
+    _act(x)
     n, t, h, wd, c = x.shape
+    dev = x.device
     first = int(bool(first))
+    _arg(w, "w", torch.bfloat16, (2 * c, 3, c), dev)
+    _opt(cache_in, "cache_in", torch.bfloat16, (n, 2, h, wd, c), dev)
+    _opt(bias, "bias", torch.float32, (2 * c,), dev)
+    _opt(cache_out, "cache_out", torch.bfloat16, (n, 2, h, wd, c), dev)
+    to = first + 2 * (t - first)
     if y is None:
-        y = torch.empty((n, first + 2 * (t - first), h, wd, c), dtype=torch.bfloat16, device=x.device)
+        y = torch.empty((n, to, h, wd, c), dtype=torch.bfloat16, device=dev)
+    _arg(y, "y", torch.bfloat16, (n, to, h, wd, c), dev)
     _check(lib.time_upsample_conv(_ptr(x), _dims(x), _ptr(cache_in), _ptr(w), _ptr(bias), first, _ptr(y),
                                   _ptr(cache_out), _stream(x)))
     return y
@@ -255,10 +371,12 @@ def time_upsample_conv(x, w, first: bool, cache_in=None, bias=None, y=None, cach
 def head_conv_d2s(x, w, cache_in=None, bias=None, fuse=None, clamp=False, video=None, cache_out=None):
     """Output head: causal conv to 12 channels + 2x2 depth-to-space; video bf16 (N,3,T,2H,2W)."""
     lib = load_library()
+    _conv_args(x, w, cache_in, bias, None, None, cache_out, k=12)
     n, t, h, wd, _ = x.shape
+    gp, _keep = _gn(fuse, n, x.shape[4], x.device)
     if video is None:
         video = torch.empty((n, 3, t, 2 * h, 2 * wd), dtype=torch.bfloat16, device=x.device)
-    gp, _keep = _gn(fuse)
+    _arg(video, "video", torch.bfloat16, (n, 3, t, 2 * h, 2 * wd), x.device)
     _check(lib.head_conv_d2s(_ptr(x), _dims(x), _ptr(cache_in), _ptr(w), _ptr(bias), gp, int(bool(clamp)),
                              _ptr(video), _ptr(cache_out), _stream(x)))
     return video

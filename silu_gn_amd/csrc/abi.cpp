@@ -2,6 +2,7 @@
 // (host-side) preparation of the nearest-x2 phase weights.
 #include <hip/hip_runtime.h>
 #include <math.h>
+#include <new>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -99,7 +100,11 @@ extern "C" int upsample2x_prepare_weights(const uint16_t* w3x3, int k, int c, ui
       const int fl = num < 0 ? -1 : num / 2;
       tap_of[a][r] = fl - a + 1;
     }
-  float* acc = new float[(size_t)c];
+  float* acc = new (std::nothrow) float[(size_t)c];
+  if (!acc) {
+    set_error("upsample2x_prepare_weights: cannot allocate %d floats of host memory", c);
+    return SGN_EINVAL;
+  }
   for (int a = 0; a < 2; ++a)
     for (int b = 0; b < 2; ++b)
       for (int kk = 0; kk < k; ++kk)

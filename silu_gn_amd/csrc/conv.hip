@@ -1754,6 +1754,7 @@ struct TileCfg {
   int lds;
   int threads;
   bool rms_epilogue;   // the kernel applies the next RMS norm in its epilogue when p.act is set
+  bool slab;           // conv_slab_kernel (else conv_kernel)
 };
 
 template <int BM, int BN, int WGM, int WGN, int NS, int MODE, bool FUSE>
@@ -1765,6 +1766,7 @@ static TileCfg make_cfg(int c) {
   t.lds = NS * (BM + BN) * kPK * 2 + (FUSE ? c * 16 : 0) + BN * 4;
   t.threads = 64 * WGM * WGN;
   t.rms_epilogue = false;
+  t.slab = false;
   return t;
 }
 
@@ -1777,6 +1779,7 @@ static TileCfg make_slab_cfg() {
   t.lds = slab_lds_bytes<BM, BN, kSlabStages, MODE>();
   t.threads = 64 * WGM * WGN;
   t.rms_epilogue = MODE == kCausal && RMS;
+  t.slab = true;
   return t;
 }
 
@@ -2100,6 +2103,57 @@ extern "C" int causal_conv3d_eligible(sgn_dims d, int k, int fuse_groups) {
   return 1;
 }
 
+extern "C" int sgn_conv_plan(int op, sgn_dims d, int k, int fused, sgn_plan* plan) {
+  const char* fn = "sgn_conv_plan";
+  clear_error();
+  if (!plan) {
+    set_error("%s: plan is required", fn);
+    return SGN_EINVAL;
+  }
+  if (fused && op != SGN_OP_CAUSAL) {
+    set_error("%s: only the causal convolution takes a fused GroupNorm", fn);
+    return SGN_EINVAL;
+  }
+  TileCfg cfg;
+  int64_t units = d.n;     // (sample, phase) pairs sharing the tile grid
+  int kk = k;
+  switch (op) {
+    case SGN_OP_CAUSAL:
+      if (!conv_shape_ok(d, k, fn)) return SGN_EINVAL;
+      if (fused && d.c > 2048) {
+        set_error("%s: fused GroupNorm supports C <= 2048", fn);
+        return SGN_EINVAL;
+      }
+      cfg = fused ? choose_tile<kCausal, true>(d.h * d.w, d.t, k, (int)d.c, d.n)
+                  : choose_tile<kCausal, false>(d.h * d.w, d.t, k, (int)d.c, d.n);
+      break;
+    case SGN_OP_PHASES:
+      if (!conv_shape_ok(d, k, fn)) return SGN_EINVAL;
+      units = d.n * 4;
+      cfg = choose_tile<kPhase, false>(d.h * d.w, d.t, k, (int)d.c, units);
+      break;
+    case SGN_OP_TIME:
+      if (!dims_ok(d, fn)) return SGN_EINVAL;
+      if (d.c > 2048) {
+        set_error("%s: the temporal x2 takes C <= 2048", fn);
+        return SGN_EINVAL;
+      }
+      kk = 2 * (int)d.c;
+      if (!conv_shape_ok(d, kk, fn)) return SGN_EINVAL;
+      cfg = choose_tile<kTime, false>(d.h * d.w, d.t, kk, (int)d.c, d.n);
+      break;
+    default:
+      set_error("%s: unknown op %d", fn, op);
+      return SGN_EINVAL;
+  }
+  plan->kernel = cfg.slab ? SGN_KERNEL_SLAB : SGN_KERNEL_GENERIC;
+  plan->tile_m = cfg.bm;
+  plan->tile_n = cfg.bn;
+  const int64_t tiles_f = (d.h * d.w + cfg.bm - 1) / cfg.bm;
+  plan->workgroups = tiles_f * d.t * ((kk + cfg.bn - 1) / cfg.bn) * units;
+  return SGN_OK;
+}
+
 extern "C" int causal_conv3d(const uint16_t* x, sgn_dims d, const uint16_t* cache_in,
                              const uint16_t* w, int k, const float* bias, const uint16_t* residual,
                              const sgn_gn* fuse, uint16_t* y, uint16_t* cache_out,
@@ -2181,8 +2235,21 @@ extern "C" int causal_conv3d_next_stats(const uint16_t* x, sgn_dims d, const uin
   }
   const size_t yb = (size_t)(d.n * d.t * d.h * d.w) * k * 2;
   const size_t sb = (size_t)d.n * next_groups * 2 * sizeof(double);
-  if (overlap(ws, ws_bytes, y, yb) || overlap(next_stats, sb, y, yb) || overlap(ws, ws_bytes, next_stats, sb)) {
-    set_error("%s: the workspace, next_stats and y must not overlap", fn);
+  const size_t xb = (size_t)(d.n * d.t * d.h * d.w * d.c) * 2;
+  const size_t cb = (size_t)(d.n * 2 * d.h * d.w * d.c) * 2;
+  const size_t wb = (size_t)k * 27 * d.c * 2;
+  // The workspace and next_stats are written: they may overlap no input and no other output.
+  const struct {
+    const void* p;
+    size_t n;
+  } others[] = {{y, yb}, {x, xb}, {w, wb}, {cache_in, cb}, {cache_out, cb}, {residual, yb},
+                {bias, (size_t)k * 4}, {fuse ? fuse->stats : nullptr, fuse && fuse->groups > 0 ? (size_t)d.n * fuse->groups * 16 : 0},
+                {fuse ? fuse->gamma : nullptr, (size_t)d.c * 4}, {fuse ? fuse->beta : nullptr, (size_t)d.c * 4}};
+  bool alias = overlap(ws, ws_bytes, next_stats, sb);
+  for (const auto& o : others)
+    if (o.p) alias = alias || overlap(ws, ws_bytes, o.p, o.n) || overlap(next_stats, sb, o.p, o.n);
+  if (alias) {
+    set_error("%s: the workspace and next_stats must not overlap each other, an input or y", fn);
     return SGN_EALIAS;
   }
   const NextStats ns = {next_groups, next_stats, ws, ws_bytes};

@@ -375,6 +375,11 @@ extern "C" int gn_silu_stats(const uint16_t* x, sgn_dims d, int groups, double* 
     set_error("gn_silu_stats: workspace must be 16-byte aligned");
     return SGN_EALIGN;
   }
+  const size_t xb = (size_t)(d.n * positions * d.c) * 2, sb = (size_t)d.n * groups * 2 * sizeof(double);
+  if (overlap(ws, need, x, xb) || overlap(stats, sb, x, xb) || overlap(ws, need, stats, sb)) {
+    set_error("gn_silu_stats: x, stats and the workspace must not overlap");
+    return SGN_EALIAS;
+  }
   dim3 grid(g.blocks, (unsigned)d.n);
   const uint4* xp = reinterpret_cast<const uint4*>(x);
   double* w = static_cast<double*>(ws);

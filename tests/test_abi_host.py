@@ -243,3 +243,92 @@ def test_prepare_phase_weights_rejects():
     _err(lib.upsample2x_prepare_weights(None, 4, 8, FAKE), EINVAL)
     buf = (ctypes.c_uint16 * (16 * 4 * 8))()
     _err(lib.upsample2x_prepare_weights(ctypes.addressof(buf), 4, 8, ctypes.addressof(buf) + 16), EALIAS)
+
+
+def _bf(*shape):
+    return torch.zeros(shape, dtype=torch.bfloat16)
+
+
+def test_binding_rejects_bad_tensors():
+    """The binding checks every tensor before its pointer reaches the library (the C side
+    cannot see dtype, strides or shape): wrong dtype, strided views, mis-shaped outputs and
+    weights, and tensors on another device raise before any call."""
+    x, w = _bf(1, 2, 4, 4, 64), _bf(64, 3, 3, 3, 64)
+    with pytest.raises(TypeError, match="x must be torch.bfloat16"):
+        sga.causal_conv3d(x.float(), w)
+    with pytest.raises(ValueError, match="x must be contiguous"):
+        sga.causal_conv3d(_bf(1, 2, 4, 8, 64)[:, :, :, ::2], w)
+    with pytest.raises(ValueError, match="y must have shape"):
+        sga.causal_conv3d(x, w, y=_bf(1, 2, 4, 4, 32))
+    with pytest.raises(ValueError, match="w must have shape"):
+        sga.causal_conv3d(x, _bf(64, 3, 3, 3, 32))
+    with pytest.raises(TypeError, match="bias must be torch.float32"):
+        sga.causal_conv3d(x, w, bias=torch.zeros(64, dtype=torch.float64))
+    with pytest.raises(ValueError, match="cache_in must have shape"):
+        sga.causal_conv3d(x, w, cache_in=_bf(1, 1, 4, 4, 64))
+    with pytest.raises(ValueError, match="residual must be contiguous"):
+        sga.causal_conv3d(x, w, residual=_bf(1, 2, 4, 4, 128)[..., ::2])
+    with pytest.raises(ValueError, match="fuse stats must have shape"):
+        sga.causal_conv3d(x, w, fuse=(torch.zeros(1, 16, 2, dtype=torch.float64), torch.ones(64),
+                                      torch.zeros(64), 1e-5, 32))
+    with pytest.raises(ValueError, match="x must be a GPU tensor"):
+        sga.causal_conv3d(x, w)                                   # every check passed but the device
+    with pytest.raises(ValueError, match="stats must have shape"):
+        sga.gn_silu_apply(x, 32, torch.zeros(1, 32, 3, dtype=torch.float64), torch.ones(64), torch.zeros(64), 1e-5)
+    with pytest.raises(TypeError, match="gamma must be torch.float32"):
+        sga.gn_silu_apply(x, 32, torch.zeros(1, 32, 2, dtype=torch.float64), torch.ones(64, dtype=torch.bfloat16),
+                          torch.zeros(64), 1e-5)
+    with pytest.raises(ValueError, match="y must have shape"):
+        sga.rms_silu(x, torch.ones(64), 1e-6, y=_bf(1, 2, 4, 4, 128))
+    with pytest.raises(ValueError, match="ws holds"):
+        sga.gn_silu_stats(x, 32, ws=torch.empty(8, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="video must have shape"):
+        sga.head_conv_d2s(x, _bf(12, 3, 3, 3, 64), video=_bf(1, 3, 2, 4, 4))
+    with pytest.raises(ValueError, match="w_phase must have shape"):
+        sga.upsample2x_conv_phases(x, _bf(2, 2, 64, 3, 3, 64))
+    with pytest.raises(ValueError, match="shortcut must have shape"):
+        sga.upsample2x_conv_phases_shortcut(x, _bf(2, 2, 64, 2, 2, 64), _bf(1, 2, 4, 5, 64), 1, False)
+    with pytest.raises(ValueError, match="y must have shape"):
+        sga.time_upsample_conv(x, _bf(128, 3, 64), True, y=_bf(1, 4, 4, 4, 64))
+    with pytest.raises(ValueError, match="act must have shape"):
+        sga.causal_conv3d_rms(x, w, torch.ones(64), 1e-6, act=_bf(1, 2, 4, 4, 32))
+    with pytest.raises(ValueError, match="stats must have shape"):
+        sga.causal_conv3d_next_stats(x, w, 32, stats=torch.zeros(1, 16, 2, dtype=torch.float64))
+    with pytest.raises(ValueError, match="w3x3 must have shape"):
+        sga.upsample2x_prepare_weights(_bf(64, 3, 2, 64))
+
+
+def test_conv_plan():
+    """sgn_conv_plan names the kernel and tile a call would run, and rejects what the call would."""
+    p = sga.sgn_conv_plan(sga.SGN_OP_CAUSAL, (1, 16, 352, 624, 256), 256)
+    assert p == {"kernel": "slab", "tile_m": 256, "tile_n": 256, "workgroups": 13728}
+    assert sga.sgn_conv_plan(sga.SGN_OP_CAUSAL, (1, 4, 44, 78, 1024), 1024)["tile_m"] == 224
+    assert sga.sgn_conv_plan(sga.SGN_OP_CAUSAL, (1, 3, 16, 16, 64), 64)["kernel"] == "generic"
+    assert sga.sgn_conv_plan(sga.SGN_OP_CAUSAL, (1, 3, 16, 16, 256), 256, fused=True)["kernel"] == "generic"
+    assert sga.sgn_conv_plan(sga.SGN_OP_PHASES, (1, 8, 88, 156, 512), 512)["workgroups"] == 3456
+    assert sga.sgn_conv_plan(sga.SGN_OP_TIME, (1, 4, 44, 78, 1024), 0)["tile_n"] == 256
+    lib = sga.load_library()
+    p = sga.sgn_plan()
+    _err(lib.sgn_conv_plan(0, D(c=72), 64, 0, ctypes.byref(p)), EINVAL)          # C % 64
+    _err(lib.sgn_conv_plan(1, D(), 64, 1, ctypes.byref(p)), EINVAL)               # fused phases
+    _err(lib.sgn_conv_plan(7, D(), 64, 0, ctypes.byref(p)), EINVAL)               # unknown op
+    _err(lib.sgn_conv_plan(0, D(), 64, 0, None), EINVAL)
+
+
+def test_stats_and_next_stats_alias_rejects():
+    lib = sga.load_library()
+    d = D()
+    need = lib.gn_silu_stats_workspace(d, 32)
+    # the workspace over x, stats over x, stats inside the workspace
+    _err(lib.gn_silu_stats(FAKE, d, 32, FAKE + (1 << 24), FAKE + 64, need, None), EALIAS)
+    _err(lib.gn_silu_stats(FAKE, d, 32, FAKE + 64, FAKE + (1 << 24), need, None), EALIAS)
+    _err(lib.gn_silu_stats(FAKE, d, 32, FAKE + (1 << 24) + 64, FAKE + (1 << 24), need, None), EALIAS)
+    nneed = lib.causal_conv3d_next_stats_workspace(d, 64, 32)
+    far = FAKE + (1 << 32)
+    # ws over x; next_stats over the weights; ws over cache_in (y, next_stats elsewhere)
+    _err(lib.causal_conv3d_next_stats(FAKE, d, None, far, 64, None, None, None, far + (1 << 24), None, 32,
+                                      far + (2 << 24), FAKE + 1024, nneed, None), EALIAS)
+    _err(lib.causal_conv3d_next_stats(FAKE, d, None, far, 64, None, None, None, far + (1 << 24), None, 32,
+                                      far + 1024, far + (3 << 24), nneed, None), EALIAS)
+    _err(lib.causal_conv3d_next_stats(FAKE, d, far + (4 << 24), far, 64, None, None, None, far + (1 << 24), None,
+                                      32, far + (2 << 24), far + (4 << 24) + 512, nneed, None), EALIAS)

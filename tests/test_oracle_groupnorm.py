@@ -32,6 +32,37 @@ def test_stats_exact_rational_tiny():
         assert abs(var[0, gi] - float(v)) <= 1e-15 * float(v)
 
 
+def test_stats_multi_chunk_exact_rational(monkeypatch):
+    """More positions than one chunk (8 chunks of 5 positions, the last ragged, two samples):
+    the per-chunk sums are combined by the compensated step, the variance pass runs chunk by
+    chunk; against exact rational arithmetic."""
+    monkeypatch.setattr(groupnorm, "_CHUNK_POSITIONS", 5)
+    x = _tiny(seed=5, shape=(2, 3, 4, 3, 16), offset=300.0)        # 36 positions per sample
+    g = 4
+    mean, var = groupnorm.group_stats(x, g)
+    xv = x.reshape(2, -1, g, 4)
+    for n in range(2):
+        for gi in range(g):
+            vals = [Fraction(float(v)) for v in xv[n, :, gi, :].ravel()]
+            m = sum(vals) / len(vals)
+            v = sum((u - m) ** 2 for u in vals) / len(vals)
+            assert abs(mean[n, gi] - float(m)) <= 1e-15 * abs(float(m))
+            assert abs(var[n, gi] - float(v)) <= 1e-13 * float(v)
+
+
+def test_stats_chunk_sums_compensated(monkeypatch):
+    """One position per chunk, so that every chunk sum is one exact value: the group's values
+    2^60, 1, -2^60, 1 have mean 1/2 exactly. A plain running fp64 sum loses the first 1 against
+    2^60 and gives 1/4; the compensated combination must keep it."""
+    monkeypatch.setattr(groupnorm, "_CHUNK_POSITIONS", 1)
+    x = np.array([2.0 ** 60, 1.0, -2.0 ** 60, 1.0]).reshape(1, 4, 1, 1, 1) * np.ones((1, 1, 1, 1, 8))
+    mean, var = groupnorm.group_stats(x, 8)
+    assert np.all(mean == 0.5)
+    half = Fraction(1, 2)
+    exact = ((2 ** 60 - half) ** 2 + (-(2 ** 60) - half) ** 2 + 2 * half ** 2) / 4
+    assert np.allclose(var, float(exact), rtol=1e-15, atol=0)
+
+
 def test_stats_large_mean_no_cancellation():
     # A group offset by 1000 with unit spread: the two-pass variance is still ~1.
     x = _tiny(offset=1000.0)
