@@ -1,21 +1,25 @@
 """Throughput of the silu(group_norm(x)) -> causal conv3d hot path on one MI355X.
 
 A step is one pass of the path over one batch of synthetic input, inputs resident
-in HBM. Default workload: the latent-resolution block -- GroupNorm(32)+SiLU fused
-into the causal 3x3x3 conv 1024->1024 over [1,4,44,78,1024] bf16 NDHWC with 2
-cached frames from a previous pass (gn_silu_stats, then causal_conv3d with the
-GroupNorm applied in its operand load, writing y and the new cache).
-Other workloads: --config 1..5 (see synthgen/workloads.py).
+in HBM. Default workload: the full-resolution residual block over [1,16,352,624,256]
+bf16 NDHWC (per-channel mean offsets U(-4,4)), each conv with a 2-frame cache from a
+previous pass: gn_silu_stats + gn_silu_apply of x, conv1 (causal_conv3d_next_stats: the
+conv, plus norm2's statistics from its epilogue), gn_silu_apply of conv1's output, then
+conv2 (causal_conv3d) with the residual x. The convolutions run unfused on the slab
+kernel's 256 x 256 tile. Other workloads: --config 1..5 (see synthgen/workloads.py).
 
 Prints ONE JSON line. ``value`` = algorithmic conv FLOPs of a step / step time
 (TFLOP/s). ``roofline`` is the conv kernel alone (HIP events on the stream it runs
-on) against the bf16 dense MFMA peak; ``gn_silu`` is gn_silu_stats + gn_silu_apply on
-the same tensor at 6 bytes/element against HBM peak; ``rms_silu`` is the output head's
-RMS norm + SiLU on that tensor at 4 bytes/element; ``box_ceilings`` is what this GPU
-sustains for those two resources (libsgnprobe.so: bf16 MFMA with random and with
-constant operand bits, HBM streaming read and copy), with each fraction repeated
-against it; ``cpu_baseline`` is the fp64 oracle on the host over a bounded sample
-(rank 0, N=1 only).
+on) against the bf16 dense MFMA peak, with the HBM traffic and MFMA busy fraction of
+the committed rocprofv3 counter summaries when the kernel's sources are unchanged since
+they were taken; ``gn_silu`` is gn_silu_stats + gn_silu_apply on the same tensor at 6
+bytes/element against HBM peak; ``rms_silu`` is the output head's RMS norm + SiLU on
+that tensor at 4 bytes/element; ``other_configs`` is the dominant kernel of every
+other workload, launched alone; ``box_ceilings`` is what this GPU sustains for those
+two resources (libsgnprobe.so: bf16 MFMA with random and with constant operand bits,
+HBM streaming read and copy), with each fraction repeated against it;
+``cpu_baseline`` is the fp64 oracle on the host over a bounded sample (rank 0, N=1
+only).
 """
 from __future__ import annotations
 
@@ -255,40 +259,122 @@ def _oracle_cores():
         return os.cpu_count() or 1
 
 
-def cpu_baseline(wl, budget_s=12.0, max_reps=8):
-    """The fp64 oracle on the host cores, on the same step as the GPU: GroupNorm statistics
-    and activation of all of x, then the causal conv of every output frame with the cache
-    (latent / tiny block). The step is repeated until ``budget_s`` seconds have passed
-    (at most ``max_reps`` times); value = conv FLOPs of a step / mean step time."""
+def _oracle_step(wl, frames):
+    """One pass of the workload's step through the fp64 oracle, over the first ``frames``
+    frames of its input (the whole input when frames == T); returns a callable."""
     import numpy as np
     from oracle import bf16 as obf16
     from oracle import conv as oconv
     from oracle import groupnorm as ogn
-    if wl.kind not in ("block", "latent"):
-        return None
-    xv = wl.x().float().numpy().astype(np.float64)
+
+    def f64(t):
+        return t.float().numpy().astype(np.float64)
+
+    def rnd(v):
+        return obf16.decode(obf16.round_rne(v))
+
+    g, eps = wl.groups, wl.eps
+    x = f64(wl.x(frames=frames))
     gamma, beta = wl.gamma().numpy(), wl.beta().numpy()
-    wv = wl.conv_weight().float().numpy().astype(np.float64)
-    cache = None
-    if wl.cache_from_prev:                       # previous pass, untimed (as on the GPU): its cache
-        xp = wl.x_prev().float().numpy().astype(np.float64)      # is its last 2 activated frames
-        act, _ = ogn.gn_silu(xp, wl.groups, gamma, beta, wl.eps)
-        cache = obf16.decode(obf16.round_rne(act))[:, -2:]
+    if wl.kind in ("block", "latent"):
+        w = f64(wl.conv_weight())
+        cache = None
+        if wl.cache_from_prev:                   # previous pass, untimed (as on the GPU): its cache
+            act, _ = ogn.gn_silu(f64(wl.x_prev()), g, gamma, beta, eps)      # is its last 2
+            cache = rnd(act)[:, -2:]                                          # activated frames
+
+        def step():
+            act, _ = ogn.gn_silu(x, g, gamma, beta, eps)
+            oconv.causal_conv3d(rnd(act), w, cache)
+        return step
+    if wl.kind == "upsample":
+        wup = f64(wl.up_weight())
+        w = f64(sg.normal((wl.c, 3, 3, 3, wl.c), wl.seed, sg.W1, std=1 / math.sqrt(27 * wl.c)))
+
+        def step():
+            u = rnd(oconv.upsample2x_conv(x, wup))
+            act, _ = ogn.gn_silu(u, g, gamma, beta, eps)
+            oconv.causal_conv3d(rnd(act), w, None)
+        return step
+    if wl.kind == "resblock":
+        (g1, b1, w1), (g2, b2, w2) = [(wl.gamma(i).numpy(), wl.beta(i).numpy(), f64(wl.conv_weight(i)))
+                                      for i in (1, 2)]
+
+        def step():
+            a1, _ = ogn.gn_silu(x, g, g1, b1, eps)
+            h, _ = oconv.causal_conv3d(rnd(a1), w1, None)
+            a2, _ = ogn.gn_silu(rnd(h), g, g2, b2, eps)
+            oconv.causal_conv3d(rnd(a2), w2, None, residual=x)
+        return step
+    w = f64(wl.conv_weight())
+
+    def step():
+        act, _ = ogn.gn_silu(x, g, gamma, beta, eps)
+        oconv.head_conv_d2s(rnd(act), w, None)
+    return step
+
+
+# Frames of each workload's input the CPU baseline runs (about 5-30 s of fp64 work on 16
+# host cores); the result is extrapolated linearly to all T frames.
+ORACLE_FRAMES = {"tiny_block": 3, "latent_block": 4, "upsample_block": 1, "fullres_resblock": 1,
+                 "output_head": 2}
+
+
+def cpu_baseline(wl, flops, budget_s=12.0, max_reps=8):
+    """The fp64 oracle on the host cores, on the workload's step: the whole step for the tiny
+    and latent blocks, else the step over its first ORACLE_FRAMES frames, extrapolated
+    linearly in the frame count (every stage's work is proportional to the frames it covers).
+    The sample is repeated until ``budget_s`` seconds have passed (at most ``max_reps``
+    times); value = conv FLOPs of a whole step / extrapolated step time."""
+    frames = min(ORACLE_FRAMES[wl.name], wl.t)
+    step = _oracle_step(wl, frames)
     reps, t0 = 0, time.perf_counter()
     while True:
-        act, _ = ogn.gn_silu(xv, wl.groups, gamma, beta, wl.eps)
-        oconv.causal_conv3d(obf16.decode(obf16.round_rne(act)), wv, cache)
+        step()
         reps += 1
         dt = time.perf_counter() - t0
         if dt >= budget_s or reps >= max_reps:
             break
-    step_s = dt / reps
-    flops = conv_flops(wl.n, wl.t, wl.h, wl.w, wl.k, wl.c)
+    sample_s = dt / reps
+    step_s = sample_s * wl.t / frames
+    what = ("the whole %s step" % wl.name if frames == wl.t else
+            "the %s step over %d of its %d frames (every stage: GroupNorm+SiLU, the convolutions), "
+            "extrapolated x%g to all frames" % (wl.name, frames, wl.t, wl.t / frames))
     return {"value": round(flops / step_s / 1e12, 6), "unit": "TFLOP/s", "cores": int(_oracle_cores()),
             "kind": "oracle",
-            "sample": "the whole %s step (GroupNorm+SiLU of all of x, then the causal conv of all %d "
-                      "frames with the 2-frame cache), fp64, repeated %d times in %.1f s (%.2f s/step)" %
-                      (wl.name, wl.t, reps, dt, step_s)}
+            "sample": "%s, fp64, repeated %d times in %.1f s (%.2f s per sample, %.2f s per step)" %
+                      (what, reps, dt, sample_s, step_s)}
+
+
+def other_configs(index, dev, iters):
+    """The dominant kernel of every other workload's step, launched alone after one step
+    (HIP events): the conv (unfused, the library's dispatch), the head, and for the upsample
+    block also the phases."""
+    out = {}
+    for i, wl in sorted(WORKLOADS.items()):
+        if i == index or wl.kind == "block":
+            continue
+        step, conv_only, _, _, launch_flops, _, name = build_step(wl, dev, False)
+        step()
+        ms = time_loop(conv_only, iters)
+        tf = launch_flops / (ms * 1e-3) / 1e12
+        rec = {"kernel": name, "ms": round(ms, 4), "TFLOP/s": round(tf, 2),
+               "frac": round(tf / PEAK_BF16_TFLOPS, 4), "flop_per_launch": launch_flops}
+        if wl.kind == "upsample":
+            x = wl.x(dev)
+            wp = sga.upsample2x_prepare_weights(wl.up_weight()).to(dev)
+            u = torch.empty((wl.n, wl.t, 2 * wl.h, 2 * wl.w, wl.c), dtype=torch.bfloat16, device=dev)
+            pms = time_loop(lambda: sga.upsample2x_conv_phases(x, wp, y=u), iters)
+            pfl = conv_flops(wl.n, wl.t, wl.h, wl.w, wl.c, wl.c, taps=16)
+            ptf = pfl / (pms * 1e-3) / 1e12
+            rec["phases"] = {"ms": round(pms, 4), "TFLOP/s": round(ptf, 2), "frac": round(ptf / PEAK_BF16_TFLOPS, 4),
+                             "flop_per_launch": pfl}
+            del x, u
+        out[wl.name] = rec
+        del step, conv_only
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    return out
 
 
 def box_ceilings(dev):
@@ -352,6 +438,28 @@ def read_traffic(kernel_tag):
         return None
 
 
+def read_mfma(kernel_tag):
+    """MFMA busy fraction and clock per launch of the dominant kernel from the committed counter
+    summary (SQ_VALU_MFMA_BUSY_CYCLES, SQ_BUSY_CYCLES, GRBM_GUI_ACTIVE), if the kernel's sources
+    are unchanged since the counters were taken (else None)."""
+    path = os.path.join(ROOT, "profiles", "%s_mfma.txt" % kernel_tag)
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith(" "):
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+    srcs = fields.get("sources", "").split()
+    if not srcs or sources_sha256(srcs) != fields.get("sources_sha256"):
+        return None
+    try:
+        return {"mfma_busy": float(fields["mfma_busy"]), "clock_GHz": float(fields["clock_GHz"])}
+    except (KeyError, ValueError):
+        return None
+
+
 def sources_sha256(paths):
     import hashlib
     h = hashlib.sha256()
@@ -366,9 +474,12 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=2, choices=sorted(WORKLOADS))
+    ap.add_argument("--config", type=int, default=4, choices=sorted(WORKLOADS),
+                    help="workload (default 4: the full-resolution residual block, the largest)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceilings", action="store_true", help="skip the box-ceiling probes")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="skip timing the other workloads' dominant kernels")
     ap.add_argument("--fused", action="store_true",
                     help="apply GroupNorm+SiLU inside the conv's operand load instead of gn_silu_apply")
     ap.add_argument("--separate-stats", action="store_true",
@@ -520,8 +631,13 @@ def main():
         out["gn_silu"]["frac_of_box"] = round(gn_gbps / (gn_bytes / box_s / 1e9), 4)
         if rms_ms:
             out["rms_silu"]["frac_of_box"] = round(rms_gbps / ceilings["hbm_copy_GB/s"], 4)
+    mf = read_mfma(kernel_tag)
+    if mf:
+        out["roofline"].update(mf)
+    if not args.no_other_configs:
+        out["other_configs"] = other_configs(args.config, dev, iters)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl)
+        out["cpu_baseline"] = cpu_baseline(wl, flops)
     print(json.dumps(out), flush=True)
 
 

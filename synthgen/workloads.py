@@ -49,9 +49,15 @@ class Workload:
     def numel(self):
         return math.prod(self.shape)
 
-    def x(self, device="cpu"):
+    def x(self, device="cpu", frames=None):
+        """The input; ``frames``: only its first frames (drawn alone: the generator is
+        counter-based, so they equal the whole tensor's first frames; N = 1 only)."""
         mean = self.offsets(device) if self.channel_offsets else 0.0
-        return sg.normal(self.shape, self.seed, sg.X, mean=mean, device=device)
+        shape = self.shape
+        if frames is not None:
+            assert self.n == 1 and 1 <= frames <= self.t
+            shape = (1, frames) + shape[2:]
+        return sg.normal(shape, self.seed, sg.X, mean=mean, device=device)
 
     def x_prev(self, device="cpu"):
         mean = self.offsets(device) if self.channel_offsets else 0.0
