@@ -94,6 +94,20 @@ int gn_silu_stats(const uint16_t* x, sgn_dims d, int groups, double* stats,
                   void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * gn_silu_stats_noalloc -- gn_silu_stats without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). It allocates nothing: the per-block partial sums go
+ * to a static 4 MiB device array inside the library, one per GPU, held until the process
+ * ends. Same x, d, groups, stats and result as gn_silu_stats (bitwise the same for up to
+ * 128 groups; with more, fewer partial blocks are used, so the sums are taken in another
+ * fixed order). Requires N x groups <= 262144 (else SGN_EINVAL); stats must not overlap
+ * x (SGN_EALIAS). All calls on one GPU share the array: calls that overlap in time on one
+ * GPU (different streams, or host threads without ordering) race and must not be made.
+ */
+int gn_silu_stats_noalloc(const uint16_t* x, sgn_dims d, int groups, double* stats,
+                          hipStream_t stream);
+
+/*
  * gn_silu_apply -- y = silu(group_norm(x)), one rounding to bf16.
  * Defined by: WanGP group_norm_silu.py page, module docstring ("GroupNorm and
  * SiLU in FP32, one rounding to the output dtype") and its third pass.

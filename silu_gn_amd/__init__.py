@@ -45,7 +45,7 @@ class sgn_plan(ctypes.Structure):
 SGN_OP_CAUSAL, SGN_OP_PHASES, SGN_OP_TIME = 0, 1, 2
 SGN_KERNELS = {1: "slab", 2: "generic"}
 
-EXPORTS = ["sgn_last_error", "gn_silu_eligible", "causal_conv3d_eligible", "sgn_conv_plan", "gn_silu_stats_workspace", "gn_silu_stats", "gn_silu_apply", "rms_silu",
+EXPORTS = ["sgn_last_error", "gn_silu_eligible", "causal_conv3d_eligible", "sgn_conv_plan", "gn_silu_stats_workspace", "gn_silu_stats", "gn_silu_stats_noalloc", "gn_silu_apply", "rms_silu",
            "causal_conv3d", "causal_conv3d_rms", "causal_conv3d_next_stats_workspace", "causal_conv3d_next_stats",
            "upsample2x_prepare_weights", "upsample2x_conv_phases", "upsample2x_conv_phases_shortcut",
            "time_upsample_conv", "head_conv_d2s"]
@@ -70,6 +70,7 @@ def load_library(path: str = LIB_PATH):
         "sgn_conv_plan": (i32, [i32, sgn_dims, i32, i32, ctypes.POINTER(sgn_plan)]),
         "gn_silu_stats_workspace": (sz, [sgn_dims, i32]),
         "gn_silu_stats": (i32, [vp, sgn_dims, i32, vp, vp, sz, vp]),
+        "gn_silu_stats_noalloc": (i32, [vp, sgn_dims, i32, vp, vp]),
         "gn_silu_apply": (i32, [vp, sgn_dims, i32, vp, vp, vp, f32, vp, vp]),
         "rms_silu": (i32, [vp, sgn_dims, vp, f32, vp, vp]),
         "causal_conv3d": (i32, [vp, sgn_dims, vp, vp, i32, vp, vp, gnp, vp, vp, vp]),
@@ -197,6 +198,15 @@ def gn_silu_stats(x, groups: int, stats=None, ws=None):
     _workspace(ws, need, dev)
     _check(lib.gn_silu_stats(_ptr(x), d, groups, _ptr(stats), _ptr(ws), ws.numel() * ws.element_size(),
                              _stream(x)))
+    return stats
+
+
+def gn_silu_stats_noalloc(x, groups: int, stats):
+    """gn_silu_stats with no workspace: the library's static scratch holds the partial sums."""
+    lib = load_library()
+    _act(x)
+    _arg(stats, "stats", torch.float64, (x.shape[0], int(groups), 2), x.device)
+    _check(lib.gn_silu_stats_noalloc(_ptr(x), _dims(x), int(groups), _ptr(stats), _stream(x)))
     return stats
 
 

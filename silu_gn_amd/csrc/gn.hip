@@ -23,6 +23,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "common.hpp"
 #include "silugn.h"
 #include "host.hpp"
@@ -393,6 +395,94 @@ extern "C" int gn_silu_stats(const uint16_t* x, sgn_dims d, int groups, double* 
   const double length = (double)positions * cg;
   gn_stats_finalize<<<dim3(groups, (unsigned)d.n), kThreads, 0, stream>>>(w, g.blocks, groups, length, stats);
   if (!launch_ok("gn_silu_stats (finalize)")) return SGN_ELAUNCH;
+  return SGN_OK;
+}
+
+// ---------------------------------------------------------------- statistics without a workspace
+// The per-block partial sums of gn_silu_stats_noalloc live in this file-scope array (one copy
+// per GPU, held until the process ends). Host code never passes the array's name to a kernel:
+// it is a host-side stand-in, not the device address. The address comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+constexpr int64_t kScratchDoubles = 1 << 19;      // 4 MiB
+static __device__ __align__(256) double scratch[kScratchDoubles];
+
+namespace sgn {
+
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[64];       // per device ordinal, null until first looked up
+
+static double* scratch_for_current_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    g_scratch_ptr[dev] = p;
+  }
+  return static_cast<double*>(g_scratch_ptr[dev]);
+}
+
+}  // namespace sgn
+
+extern "C" int gn_silu_stats_noalloc(const uint16_t* x, sgn_dims d, int groups, double* stats,
+                                     hipStream_t stream) {
+  const char* fn = "gn_silu_stats_noalloc";
+  clear_error();
+  if (!gn_shape_ok(d, groups, fn)) return SGN_EINVAL;
+  if (!x || !stats) {
+    set_error("%s: x and stats are required", fn);
+    return SGN_EINVAL;
+  }
+  if (!aligned16(x) || ((uintptr_t)stats & 7)) {
+    set_error("%s: x must be 16-byte and stats 8-byte aligned", fn);
+    return SGN_EALIGN;
+  }
+  // Every (sample, group) needs at least one partial (S, Q) pair in the scratch array.
+  if ((double)d.n * groups * 2 > (double)kScratchDoubles) {
+    set_error("%s: N x groups = %lld exceeds the %lld (sample, group) pairs the scratch holds", fn,
+              (long long)(d.n * groups), (long long)(kScratchDoubles / 2));
+    return SGN_EINVAL;
+  }
+  const int64_t positions = d.t * d.h * d.w;
+  const size_t xb = (size_t)(d.n * positions * d.c) * 2, sb = (size_t)d.n * groups * 2 * sizeof(double);
+  if (overlap(stats, sb, x, xb)) {
+    set_error("%s: stats must not overlap x", fn);
+    return SGN_EALIAS;
+  }
+  double* ws = scratch_for_current_device();
+  if (!ws) {
+    set_error("%s: cannot look up the scratch array's device address", fn);
+    return SGN_ELAUNCH;
+  }
+  const int cg = (int)(d.c / groups);
+  const int gpp = cg >= 8 ? 1 : 8 / cg;
+  const void* partial = gpp == 1   ? (const void*)gn_stats_partial<1>
+                        : gpp == 2 ? (const void*)gn_stats_partial<2>
+                        : gpp == 4 ? (const void*)gn_stats_partial<4>
+                                   : (const void*)gn_stats_partial<8>;
+  // As gn_silu_stats, with the partial-sum blocks capped so that they fit the scratch array
+  // (with 32 groups the cap is above the resident grid: the same blocks, the same bits).
+  int max_blocks = resident_blocks(partial);
+  const int64_t fit = kScratchDoubles / ((int64_t)groups * 2);
+  if (max_blocks > fit) max_blocks = (int)fit;
+  PacketGrid g = packet_grid(positions, (int)d.c, (int)d.n, 8, max_blocks);
+  if ((int64_t)d.n * groups * 2 * g.blocks > kScratchDoubles) {
+    set_error("%s: internal: %d partial blocks per sample do not fit the scratch", fn, g.blocks);
+    return SGN_EINVAL;
+  }
+  dim3 grid(g.blocks, (unsigned)d.n);
+  const uint4* xp = reinterpret_cast<const uint4*>(x);
+  switch (gpp) {
+    case 1: gn_stats_partial<1><<<grid, kThreads, 0, stream>>>(xp, positions, g.cp, g.rstep, g.rows_per_block, cg, groups, ws); break;
+    case 2: gn_stats_partial<2><<<grid, kThreads, 0, stream>>>(xp, positions, g.cp, g.rstep, g.rows_per_block, cg, groups, ws); break;
+    case 4: gn_stats_partial<4><<<grid, kThreads, 0, stream>>>(xp, positions, g.cp, g.rstep, g.rows_per_block, cg, groups, ws); break;
+    default: gn_stats_partial<8><<<grid, kThreads, 0, stream>>>(xp, positions, g.cp, g.rstep, g.rows_per_block, cg, groups, ws); break;
+  }
+  if (!launch_ok("gn_silu_stats_noalloc (partial)")) return SGN_ELAUNCH;
+  gn_stats_finalize<<<dim3(groups, (unsigned)d.n), kThreads, 0, stream>>>(ws, g.blocks, groups,
+                                                                          (double)positions * cg, stats);
+  if (!launch_ok("gn_silu_stats_noalloc (finalize)")) return SGN_ELAUNCH;
   return SGN_OK;
 }
 

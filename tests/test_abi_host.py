@@ -332,3 +332,13 @@ def test_stats_and_next_stats_alias_rejects():
                                       far + 1024, far + (3 << 24), nneed, None), EALIAS)
     _err(lib.causal_conv3d_next_stats(FAKE, d, far + (4 << 24), far, 64, None, None, None, far + (1 << 24), None,
                                       32, far + (2 << 24), far + (4 << 24) + 512, nneed, None), EALIAS)
+
+
+def test_noalloc_stats_rejects():
+    lib = sga.load_library()
+    far = FAKE + (1 << 32)
+    _err(lib.gn_silu_stats_noalloc(FAKE, D(c=64), 48, far, None), EINVAL)              # groups
+    _err(lib.gn_silu_stats_noalloc(None, D(), 32, far, None), EINVAL)
+    _err(lib.gn_silu_stats_noalloc(FAKE + 2, D(), 32, far, None), EALIGN)
+    _err(lib.gn_silu_stats_noalloc(FAKE, D(n=200, c=2048), 2048, far, None), EINVAL)   # beyond the scratch
+    _err(lib.gn_silu_stats_noalloc(FAKE, D(), 32, FAKE + 64, None), EALIAS)            # stats inside x
