@@ -31,9 +31,16 @@ FastVideo ``wan22_vae_decode/solution/binding.cpp``):
                     unfold to ft x fs x fs). Neither formula is printed on the pages; the
                     module docstring states the readings.
 
+* ``winograd``   -- the causal 3x3x3 convolution through F(4x4,3x3) (binding.cpp,
+                    prepare(): the 6x3 weight transform G, each of the 36 components
+                    keeping the causal 3-tap temporal convolution; Decoder::conv: input
+                    transform, per-component temporal products, output transform). The
+                    input and output transforms are those of the same interpolation points
+                    (the pages print G only); pinned by the identity with ``conv``.
+
 Every function is pinned by ``tests/test_oracle_*.py`` against brute force,
 closed forms, invariants or an independent library routine. Parity unpinned:
 agreement with the real Wan2.2 decoder (trained weights, real latents, the
 head's channel order), which needs data this repository does not have.
 """
-from . import bf16, groupnorm, conv, rmsnorm, upblock  # noqa: F401
+from . import bf16, groupnorm, conv, rmsnorm, upblock, winograd  # noqa: F401
