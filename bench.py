@@ -228,8 +228,26 @@ def up_block_extras(wl, dev, iters):
             sga.rms_silu(y, gain, 1e-6, y=act)
         sep = time_loop(separate, iters)
         epi = time_loop(lambda: sga.causal_conv3d_rms(x, w, gain, 1e-6, act=act, store_y=False), iters)
-        return {"conv_rms_epilogue": {"ms": round(epi, 4), "ms_separate": round(sep, 4),
-                                      "form": "causal_conv3d_rms, y not stored (vs causal_conv3d + rms_silu)"}}
+        out = {"conv_rms_epilogue": {"ms": round(epi, 4), "ms_separate": round(sep, 4),
+                                     "form": "causal_conv3d_rms, y not stored (vs causal_conv3d + rms_silu)"}}
+        # the same conv through Winograd F(4x4,3x3) (input transform, 36 component products,
+        # output transform) against the direct conv, both on the GroupNorm+SiLU output of x
+        st = sga.gn_silu_stats(x, wl.groups)
+        sga.gn_silu_apply(x, wl.groups, st, wl.gamma(1, dev), wl.beta(1, dev), wl.eps, y=act)
+        u = sga.winograd_prepare_weights(wl.conv_weight(1)).to(dev)
+        ws = torch.empty(sga.causal_conv3d_winograd_workspace(wl.shape, wl.c), dtype=torch.uint8, device=dev)
+        wino = time_loop(lambda: sga.causal_conv3d_winograd(act, u, y=y, ws=ws), iters)
+        direct = time_loop(lambda: sga.causal_conv3d(act, w, y=y), iters)
+        fl = conv_flops(wl.n, wl.t, wl.h, wl.w, wl.c, wl.c)
+        tiles = ((wl.h + 3) // 4) * ((wl.w + 3) // 4)
+        mfl = 36 * 2.0 * wl.n * wl.t * tiles * wl.c * 3 * wl.c
+        out["winograd"] = {"ms": round(wino, 4), "ms_direct": round(direct, 4),
+                           "TFLOP/s_direct_equivalent": round(fl / (wino * 1e-3) / 1e12, 2),
+                           "mfma_flop_per_launch": mfl, "workspace_bytes": ws.numel(),
+                           "form": "causal_conv3d_winograd (F(4x4,3x3), bf16 U and V) vs causal_conv3d"}
+        del ws
+        torch.cuda.empty_cache()
+        return out
     return {}
 
 

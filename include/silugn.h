@@ -261,6 +261,56 @@ int causal_conv3d_next_stats(const uint16_t* x, sgn_dims d, const uint16_t* cach
                              void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * winograd_prepare_weights -- HOST function: the F(4x4,3x3) Winograd weights of a causal
+ * 3x3x3 convolution for causal_conv3d_winograd.
+ * Defined by: binding.cpp page, prepare() ("F(4x4,3x3) Winograd weights": the 6x3 matrix G
+ * below; each of the 36 components keeps the 3-tap temporal convolution; the sums are formed
+ * in fp32 and stored in bf16).
+ *
+ *   G = [1/4 0 0; -1/6 -1/6 -1/6; -1/6 1/6 -1/6; 1/24 1/12 1/6; 1/24 -1/12 1/6; 0 0 1]
+ *   u[a*6 + b][k][dt][c] = RNE_bf16( sum over (r, s) with G[a][r] G[b][s] != 0 of
+ *                                    w[k][dt][r][s][c] * (G[a][r] G[b][s]) ), summed in fp32
+ * w: host bf16 (K,3,3,3,C); u: host bf16 (36,K,3,C), i.e. 108*K*C values; u must not
+ * overlap w (SGN_EALIAS).
+ */
+int winograd_prepare_weights(const uint16_t* w, int k, int c, uint16_t* u);
+
+/*
+ * Bytes of device workspace causal_conv3d_winograd needs for input dims d and K output
+ * channels (0, with the reason in sgn_last_error(), for a shape it rejects).
+ */
+size_t causal_conv3d_winograd_workspace(sgn_dims d, int k);
+
+/*
+ * causal_conv3d_winograd -- causal_conv3d (unfused) through Winograd F(4x4,3x3): the spatial
+ * 3x3 taps in 6x6-point transforms, each of the 36 components a causal 3-tap temporal
+ * product.
+ * Defined by: binding.cpp page, Decoder::conv (only the expensive spatial 3x3 convolutions
+ * go through Winograd: the padded input is transformed, one 3-tap temporal convolution runs
+ * per component, and an epilogue forms the output with the bias and the residual) and
+ * prepare() (the weights: winograd_prepare_weights). The input and output transforms are
+ * those of G's interpolation points 0, 1, -1, 2, -2 and infinity:
+ *   V = B^T d B of each 4x4 output tile's 6x6 input patch (rows and columns 4i-1 .. 4i+4,
+ *       zero outside the frame) in every frame of P = cat(cache_in, x), fp32 from the bf16
+ *       input, rounded once to bf16;
+ *   M[ab][n,t,tile,k] = sum_{dt,c} u[ab][k][dt][c] V[ab][n, t+dt, tile, c]   (fp32)
+ *   y = RNE_bf16( A^T M A + bias + residual )   (fp32), the pixels inside the frame.
+ * Arguments as causal_conv3d with u (device, from winograd_prepare_weights) for w, no fused
+ * GroupNorm, and a device workspace ws of causal_conv3d_winograd_workspace(d, k) bytes,
+ * 16-byte aligned, overwritten: V, bf16 [36][N][T+2][ceil(H/4)][ceil(W/4)][C], at offset 0,
+ * then M, fp32 [36][N][T][ceil(H/4)][ceil(W/4)][K], at the next 256-byte boundary.
+ * Accuracy: the same result as causal_conv3d up to the bf16 rounding of u and V, which the
+ * output transform amplifies (by up to about 10x at a tile's far corner): about 2.5e-2
+ * relative L2 error on unit-scale data against 1.7e-3 for causal_conv3d.
+ * Requires C % 64 == 0 with C <= 4096 and 128 < K <= 4096 with K % 8 == 0; the outputs and
+ * the workspace must not overlap any input or each other (SGN_EALIAS).
+ */
+int causal_conv3d_winograd(const uint16_t* x, sgn_dims d, const uint16_t* cache_in,
+                           const uint16_t* u, int k, const float* bias, const uint16_t* residual,
+                           uint16_t* y, uint16_t* cache_out, void* ws, size_t ws_bytes,
+                           hipStream_t stream);
+
+/*
  * upsample2x_prepare_weights -- HOST function: the four 2x2 phase kernels of a
  * nearest-x2 + 3x3 convolution.
  * Defined by: binding.cpp page, prepare() ("Nearest-x2 + 3x3 convolution equals

@@ -47,6 +47,7 @@ SGN_KERNELS = {1: "slab", 2: "generic"}
 
 EXPORTS = ["sgn_last_error", "gn_silu_eligible", "causal_conv3d_eligible", "sgn_conv_plan", "gn_silu_stats_workspace", "gn_silu_stats", "gn_silu_stats_noalloc", "gn_silu_apply", "rms_silu",
            "causal_conv3d", "causal_conv3d_rms", "causal_conv3d_next_stats_workspace", "causal_conv3d_next_stats",
+           "winograd_prepare_weights", "causal_conv3d_winograd_workspace", "causal_conv3d_winograd",
            "upsample2x_prepare_weights", "upsample2x_conv_phases", "upsample2x_conv_phases_shortcut",
            "time_upsample_conv", "head_conv_d2s"]
 
@@ -79,6 +80,9 @@ def load_library(path: str = LIB_PATH):
         "causal_conv3d_next_stats": (i32, [vp, sgn_dims, vp, vp, i32, vp, vp, gnp, vp, vp, i32, vp, vp,
                                            sz, vp]),
         "upsample2x_prepare_weights": (i32, [vp, i32, i32, vp]),
+        "winograd_prepare_weights": (i32, [vp, i32, i32, vp]),
+        "causal_conv3d_winograd_workspace": (sz, [sgn_dims, i32]),
+        "causal_conv3d_winograd": (i32, [vp, sgn_dims, vp, vp, i32, vp, vp, vp, vp, vp, sz, vp]),
         "upsample2x_conv_phases": (i32, [vp, sgn_dims, vp, i32, vp, vp, vp]),
         "upsample2x_conv_phases_shortcut": (i32, [vp, sgn_dims, vp, i32, vp, vp, sgn_dims, i32, i32, vp, vp]),
         "time_upsample_conv": (i32, [vp, sgn_dims, vp, vp, vp, i32, vp, vp, vp]),
@@ -322,6 +326,50 @@ def upsample2x_prepare_weights(w3x3):
     out = torch.empty((2, 2, k, 2, 2, c), dtype=torch.bfloat16)
     _check(lib.upsample2x_prepare_weights(w.data_ptr(), k, c, out.data_ptr()))
     return out
+
+
+def winograd_prepare_weights(w):
+    """Host: bf16 (K,3,3,3,C) -> bf16 F(4x4,3x3) weights (36,K,3,C) (CPU tensors)."""
+    lib = load_library()
+    w = w.detach().to("cpu").contiguous()
+    _arg(w, "w", torch.bfloat16, (None, 3, 3, 3, None))
+    k, c = w.shape[0], w.shape[4]
+    out = torch.empty((36, k, 3, c), dtype=torch.bfloat16)
+    _check(lib.winograd_prepare_weights(w.data_ptr(), k, c, out.data_ptr()))
+    return out
+
+
+def causal_conv3d_winograd_workspace(dims, k: int) -> int:
+    return int(load_library().causal_conv3d_winograd_workspace(sgn_dims(*dims), int(k)))
+
+
+def causal_conv3d_winograd(x, u, cache_in=None, bias=None, residual=None, y=None, cache_out=None, ws=None):
+    """causal_conv3d through Winograd F(4x4,3x3) with the weights of winograd_prepare_weights (on the
+    device); returns y. ``ws`` receives the transformed input and the products (see the header)."""
+    lib = load_library()
+    _act(x)
+    n, t, h, wd, c = x.shape
+    dev = x.device
+    _arg(u, "u", torch.bfloat16, (36, None, 3, c), dev)
+    k = u.shape[1]
+    _opt(cache_in, "cache_in", torch.bfloat16, (n, 2, h, wd, c), dev)
+    _opt(bias, "bias", torch.float32, (k,), dev)
+    _opt(residual, "residual", torch.bfloat16, (n, t, h, wd, k), dev)
+    _opt(cache_out, "cache_out", torch.bfloat16, (n, 2, h, wd, c), dev)
+    d = _dims(x)
+    need = lib.causal_conv3d_winograd_workspace(d, k)
+    if need == 0:
+        _check(-1)
+    if y is None:
+        y = torch.empty((n, t, h, wd, k), dtype=torch.bfloat16, device=dev)
+    _arg(y, "y", torch.bfloat16, (n, t, h, wd, k), dev)
+    if ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    _workspace(ws, need, dev)
+    _check(lib.causal_conv3d_winograd(_ptr(x), d, _ptr(cache_in), _ptr(u), k, _ptr(bias), _ptr(residual),
+                                      _ptr(y), _ptr(cache_out), _ptr(ws), ws.numel() * ws.element_size(),
+                                      _stream(x)))
+    return y
 
 
 def _phase_args(x, w_phase, bias, y):

@@ -125,3 +125,48 @@ extern "C" int upsample2x_prepare_weights(const uint16_t* w3x3, int k, int c, ui
   delete[] acc;
   return SGN_OK;
 }
+
+// Winograd F(4x4,3x3) weights (binding.cpp page, prepare(): the 6x3 matrix G; each of the 36
+// components keeps the 3 frame taps; sums formed in fp32, stored in bf16):
+//   u[a * 6 + b][k][dt][c] = RNE_bf16( fp32 sum over the taps (r, s) with G[a][r] G[b][s] != 0
+//                                      of w[k][dt][r][s][c] * (G[a][r] G[b][s]) ).
+extern "C" int winograd_prepare_weights(const uint16_t* w, int k, int c, uint16_t* u) {
+  clear_error();
+  if (!w || !u || k <= 0 || c <= 0) {
+    set_error("winograd_prepare_weights: w, u and positive k, c are required");
+    return SGN_EINVAL;
+  }
+  const size_t in_bytes = (size_t)k * 27 * c * 2, out_bytes = (size_t)36 * k * 3 * c * 2;
+  if (overlap(w, in_bytes, u, out_bytes)) {
+    set_error("winograd_prepare_weights: u overlaps w");
+    return SGN_EALIAS;
+  }
+  static const float G[6][3] = {{0.25f, 0.0f, 0.0f},
+                                {-1.0f / 6, -1.0f / 6, -1.0f / 6},
+                                {-1.0f / 6, 1.0f / 6, -1.0f / 6},
+                                {1.0f / 24, 1.0f / 12, 1.0f / 6},
+                                {1.0f / 24, -1.0f / 12, 1.0f / 6},
+                                {0.0f, 0.0f, 1.0f}};
+  float* acc = new (std::nothrow) float[(size_t)c];
+  if (!acc) {
+    set_error("winograd_prepare_weights: cannot allocate %d floats of host memory", c);
+    return SGN_EINVAL;
+  }
+  for (int a = 0; a < 6; ++a)
+    for (int b = 0; b < 6; ++b)
+      for (int kk = 0; kk < k; ++kk)
+        for (int dt = 0; dt < 3; ++dt) {
+          for (int ci = 0; ci < c; ++ci) acc[ci] = 0.0f;
+          for (int r = 0; r < 3; ++r)
+            for (int s = 0; s < 3; ++s) {
+              const float coef = G[a][r] * G[b][s];
+              if (coef == 0.0f) continue;
+              const uint16_t* src = w + ((((size_t)kk * 3 + dt) * 3 + r) * 3 + s) * c;
+              for (int ci = 0; ci < c; ++ci) acc[ci] += bf16_to_f32(src[ci]) * coef;
+            }
+          uint16_t* dst = u + (((size_t)(a * 6 + b) * k + kk) * 3 + dt) * c;
+          for (int ci = 0; ci < c; ++ci) dst[ci] = f32_to_bf16(acc[ci]);
+        }
+  delete[] acc;
+  return SGN_OK;
+}

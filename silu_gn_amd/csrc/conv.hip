@@ -42,7 +42,7 @@ struct IC {
   static constexpr int value = V;
 };
 
-enum Mode { kCausal = 0, kPhase = 1, kHead = 2, kTime = 3 };
+enum Mode { kCausal = 0, kPhase = 1, kHead = 2, kTime = 3, kWino = 4 };
 
 struct ConvParams {
   const uint16_t* x;
@@ -80,6 +80,11 @@ struct ConvParams {
   uint16_t* act;
   const float* rms_gain;
   double rms_eps;
+  // Winograd products (kWino): sample n of the launch is component n / wino_n (of 36) of
+  // sample n % wino_n; its weights start at w + component * K * 3 * C, and the fp32 products
+  // go to yf (N x T frames of H x W positions -- the tiles -- by K channels).
+  int wino_n;
+  float* yf;
 };
 
 
@@ -380,6 +385,60 @@ __device__ __forceinline__ Sums store_tile_staged(const f32x16 (&acc)[TN][TM], c
     wait_lgkm0();                                    // reads done before the next rows land
   }
   return Sums{ss, sq};
+}
+
+// Epilogue of the Winograd products: fp32 acc of 32 positions x WTN channels per wave staged
+// in LDS as store_tile_staged does, read back as 4 channels (16 bytes) per lane and stored,
+// unrounded, to yf: frame n * T + t of H x W positions (the tiles), K channels each, through a
+// descriptor over that frame (rows past it are dropped). K % 4 == 0.
+template <int TN, int TM, int WTM, int WTN>
+__device__ __forceinline__ void store_tile_f32(const f32x16 (&acc)[TN][TM], const ConvParams& p, int n, int t,
+                                               int pos0, int kbase, int wm, int lane, char* stage) {
+  constexpr int ROW = WTN * 4;                       // staging row bytes
+  constexpr int LPR = WTN / 4;                       // lanes per row on the way out
+  constexpr int RPI = 64 / LPR;                      // rows per instruction
+  constexpr int NI = 32 / RPI;                       // instructions per 32 rows
+  static_assert(LPR * RPI == 64 && RPI * NI == 32, "staging shape");
+  constexpr int SWZ = WTN / 4 < 16 ? WTN / 4 - 1 : 15;
+  const int K = p.K, HW = p.H * p.W;
+  const int g = lane % LPR;                          // 4-channel group of this lane
+  const int k0 = kbase + 4 * g;
+  const int64_t base = ((int64_t)n * p.T + t) * HW * K;
+  const Rsrc ms = make_rsrc(p.yf + base, (uint32_t)((int64_t)HW * K * 4));
+  const bool kfull = kbase + WTN <= K;
+  stage_barrier();                                   // every wave is done with the operand stages
+#pragma unroll
+  for (int j = 0; j < TM; ++j) {
+    {
+      const int r = lane & 31;
+#pragma unroll
+      for (int i = 0; i < TN; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int kr = i * 32 + 8 * q + 4 * (lane >> 5);
+          float4 v;
+          v.x = acc[i][j][4 * q + 0];
+          v.y = acc[i][j][4 * q + 1];
+          v.z = acc[i][j][4 * q + 2];
+          v.w = acc[i][j][4 * q + 3];
+          *reinterpret_cast<float4*>(stage + r * ROW + (((kr >> 2) ^ (r & SWZ)) << 4)) = v;
+        }
+    }
+    wait_lgkm0();                                    // this wave's rows are in its area
+#pragma unroll
+    for (int it = 0; it < NI; ++it) {
+      const int r = it * RPI + lane / LPR;
+      const float4 v = *reinterpret_cast<const float4*>(stage + r * ROW + ((g ^ (r & SWZ)) << 4));
+      const int ml = pos0 + wm * WTM + 32 * j + r;
+      if (kfull) {
+        const u32x4 o = {__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z), __float_as_uint(v.w)};
+        __builtin_amdgcn_raw_buffer_store_b128(o, ms, (uint32_t)(((int64_t)ml * K + k0) * 4), 0, 0);
+      } else if (k0 < K && ml < HW) {
+        *reinterpret_cast<float4*>(p.yf + base + (int64_t)ml * K + k0) = v;
+      }
+    }
+    wait_lgkm0();                                    // reads done before the next rows land
+  }
 }
 
 // Causal epilogue that also applies the next RMS norm + SiLU (the decoder's norm is per
@@ -1073,7 +1132,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_kernel(ConvParams p) {
 //   distinct 16-byte bank groups, whatever the window offset.
 constexpr int kSlabStages = 4;           // weight stage buffers of the slab kernel
 
-__host__ __device__ constexpr int slab_inner(int mode) { return mode == kPhase ? 2 : mode == kTime ? 1 : 3; }
+__host__ __device__ constexpr int slab_inner(int mode) { return mode == kPhase ? 2 : (mode == kTime || mode == kWino) ? 1 : 3; }
 
 // Slab buffers: slab G starts moving L + INNER stages before stage INNER G and its buffer
 // must have been retired (after stage INNER (G - NSL) + INNER - 1): INNER NSL >= L + 2 INNER.
@@ -1130,9 +1189,10 @@ __device__ __forceinline__ void wait_vm_n(int n) {
 // so that the plain convolution keeps its spill-free register allocation).
 template <int BM, int BN, int WGM, int WGN, int NS, int MODE, bool RMS = false>
 __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_slab_kernel(ConvParams p) {
-  static_assert(MODE == kCausal || MODE == kPhase || MODE == kTime, "slab modes");
+  static_assert(MODE == kCausal || MODE == kPhase || MODE == kTime || MODE == kWino, "slab modes");
+  constexpr bool TEMPORAL = MODE == kTime || MODE == kWino;   // 3 frame taps, one row, no column taps
   constexpr int INNER = slab_inner(MODE);            // column taps per group
-  constexpr int TAPS = MODE == kPhase ? 4 : MODE == kTime ? 3 : 27;
+  constexpr int TAPS = MODE == kPhase ? 4 : TEMPORAL ? 3 : 27;
   constexpr int NW = WGM * WGN, L = NS - 1, NSL = slab_bufs(NS, INNER);
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
   constexpr int TM = WTM / 32, TN = WTN / 32;
@@ -1190,12 +1250,13 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_slab_kernel(ConvParams
   const int NG = (TAPS / INNER) * kpt;               // groups, INNER stages each
   const int KS = INNER * NG;
   const int pos0 = mt * BM;
-  const int c0 = MODE == kPhase ? pb - 1 : MODE == kTime ? 0 : -1;   // column offset of slab row 0
+  const int c0 = MODE == kPhase ? pb - 1 : TEMPORAL ? 0 : -1;   // column offset of slab row 0
   // This lane moves logical chunk lc of row (16 qi + (lane >> 2)); (row & 15) = lane >> 2.
   const int lc = (lane & 3) ^ ((lane >> 3) & 3) ^ ((lane >> 5) & 1);
 
-  const Rsrc wr = make_rsrc(p.w + (MODE == kPhase ? (int64_t)phase * K * 4 * C : 0),
-                            (uint32_t)K * TAPS * C * 2);
+  const int64_t wsel = MODE == kPhase ? (int64_t)phase * K * 4 * C
+                       : MODE == kWino ? (int64_t)(n / p.wino_n) * K * 3 * C : 0;
+  const Rsrc wr = make_rsrc(p.w + wsel, (uint32_t)K * TAPS * C * 2);
   uint32_t wvo[DW];
 #pragma unroll
   for (int j = 0; j < DW; ++j) {
@@ -1235,18 +1296,19 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_slab_kernel(ConvParams
   };
   // Descriptors of the source frames of frame taps dt = 0, 1, 2: frame t + dt - 2 of x, a
   // cache frame, or (no cache) zeros. The phases read frame t only. The temporal x2 reads
-  // x from frame x0 on, Tx frames per sample.
-  const int64_t xf0 = MODE == kTime ? (int64_t)n * p.Tx + p.x0 : (int64_t)n * T;
+  // x from frame x0 on, Tx frames per sample; the Winograd products read frames t .. t + 2
+  // of the Tx = T + 2 transformed frames of P (x0 = 2), which always exist.
+  const int64_t xf0 = TEMPORAL ? (int64_t)n * p.Tx + p.x0 : (int64_t)n * T;
   const Rsrc frs2 = make_rsrc(p.x + (xf0 + t) * HW * C, frame_bytes);
   Rsrc frs0 = frs2, frs1 = frs2;
-  if (MODE == kCausal || MODE == kTime) {
-    if (t >= 2)
+  if (MODE == kCausal || TEMPORAL) {
+    if (t >= 2 || MODE == kWino)
       frs0 = make_rsrc(p.x + (xf0 + t - 2) * HW * C, frame_bytes);
     else if (p.cache)
       frs0 = make_rsrc(p.cache + ((int64_t)n * 2 + t) * HW * C, frame_bytes);
     else
       frs0 = make_rsrc(p.x, 0);
-    if (t >= 1)
+    if (t >= 1 || MODE == kWino)
       frs1 = make_rsrc(p.x + (xf0 + t - 1) * HW * C, frame_bytes);
     else if (p.cache)
       frs1 = make_rsrc(p.cache + ((int64_t)n * 2 + t + 1) * HW * C, frame_bytes);
@@ -1259,8 +1321,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_slab_kernel(ConvParams
     constexpr int PART = decltype(part_c)::value;
     if (PART == 0) {
       // dh: the row tap, stored + 1 (causal dh; phase u + a; the temporal x2's one row).
-      const int dt = MODE == kPhase ? 2 : MODE == kTime ? go : go / 3;
-      const int dh = MODE == kPhase ? go + pa : MODE == kTime ? 1 : go - 3 * dt;
+      const int dt = MODE == kPhase ? 2 : TEMPORAL ? go : go / 3;
+      const int dh = MODE == kPhase ? go + pa : TEMPORAL ? 1 : go - 3 * dt;
       const Rsrc r0 = frs0, r1 = frs1, r2 = frs2;     // values: a select of lvalues would
       srs = dt == 0 ? r0 : dt == 1 ? r1 : r2;        // select their addresses
       sdelta = ((dh - 1) * W * C + gch * kPK) * 2;
@@ -1486,6 +1548,9 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_slab_kernel(ConvParams
     }
   }
   if (rms_done) {
+  } else if constexpr (MODE == kWino) {
+    store_tile_f32<TN, TM, WTM, WTN>(acc, p, n, t, pos0, ntile * BN + wn * WTN, wm, lane,
+                                     smem + wave * (32 * WTN * 4));
   } else if (K % 8 == 0) {                           // rows of y 16-byte aligned
     const Sums sums = store_tile_staged<MODE, TN, TM, WTM, WTN>(
         acc, p, n, t, pos0, ntile * BN + wn * WTN, wm, lane, phase, lb, smem + wave * (32 * WTN * 4));
@@ -1493,7 +1558,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_slab_kernel(ConvParams
     if (MODE == kCausal && p.nws)
       next_stats_partials<NW, WGM, WTN, BN>(p, n, t, mt, ntile, wave, lane, sums,
                                             reinterpret_cast<double*>(smem + NW * 32 * WTN * 4));
-  } else if constexpr (MODE != kTime) {               // the temporal x2 needs K % 16 == 0
+  } else if constexpr (MODE != kTime && MODE != kWino) {   // the temporal x2 needs K % 16 == 0
     store_tile<MODE, TN, TM, WTM, WTN>(acc, p, n, (int64_t)t * HW + pos0, (int64_t)(t + 1) * HW,
                                        ntile * BN + wn * WTN, wm, lane, phase, lb);
   }
@@ -1744,6 +1809,176 @@ __global__ __launch_bounds__(64 * NW, 1) void head_kernel(ConvParams p, int wblo
   wait_vm<0>();
 }
 
+// ---------------------------------------------------------------- Winograd F(4x4, 3x3)
+//
+// The causal 3x3x3 convolution as 36 per-component causal 3-tap temporal products (binding.cpp
+// page: prepare()'s F(4x4,3x3) weight transform, whose 36 components each keep the 3 frame
+// taps; Decoder::conv: input transform, the per-component products, an epilogue forming the
+// output with bias and residual). Three launches:
+//  1. wino_input_kernel: V = B^T d B of every tile's 6 x 6 patch in every frame of
+//     P = cat(cache, x), in fp32 from the bf16 input, rounded once to bf16, component-major:
+//     V[36][N][T + 2][TH x TW tiles][C].
+//  2. conv_slab_kernel<.., kWino>: per component, M[t][tile][k] = sum_{dt, c} U[k][dt][c] V[t +
+//     dt][tile][c] -- the slab kernel's temporal mode over the 36 N "samples", fp32 out.
+//  3. wino_output_kernel: Y = A^T M A per tile and channel in fp32, + bias + residual, one
+//     rounding to bf16, the pixels inside the frame stored NDHWC.
+// The transforms use the interpolation points 0, 1, -1, 2, -2 and infinity of the page's G.
+
+// Input transform of 6 values (one row or column of a patch): B^T d.
+__device__ __forceinline__ void wino_bt(const float d[6], float o[6]) {
+  o[0] = 4.0f * d[0] - 5.0f * d[2] + d[4];
+  o[1] = -4.0f * d[1] - 4.0f * d[2] + d[3] + d[4];
+  o[2] = 4.0f * d[1] - 4.0f * d[2] - d[3] + d[4];
+  o[3] = -2.0f * d[1] - d[2] + 2.0f * d[3] + d[4];
+  o[4] = 2.0f * d[1] - d[2] - 2.0f * d[3] + d[4];
+  o[5] = 4.0f * d[1] - 5.0f * d[3] + d[5];
+}
+
+// One thread: channels 2 c2, 2 c2 + 1 of one tile of frame f (blockIdx.y) of sample n
+// (blockIdx.z); grid-stride over tiles x channel pairs, channel pairs fastest (coalesced).
+__global__ __launch_bounds__(256) void wino_input_kernel(const uint32_t* __restrict__ x,
+                                                         const uint32_t* __restrict__ cache,
+                                                         uint32_t* __restrict__ v, int N, int T, int H,
+                                                         int W, int cp, int TW, int64_t TP) {
+  const int f = blockIdx.y, n = blockIdx.z;
+  const int64_t fsz = (int64_t)H * W * cp;           // dwords per frame
+  const uint32_t* src = f >= 2 ? x + ((int64_t)n * T + f - 2) * fsz
+                               : (cache ? cache + ((int64_t)n * 2 + f) * fsz : nullptr);
+  const int64_t cstride = (int64_t)N * (T + 2) * TP * cp;   // dwords between components
+  uint32_t* dst = v + ((int64_t)n * (T + 2) + f) * TP * cp;
+  const int64_t items = TP * cp;
+  for (int64_t it = (int64_t)blockIdx.x * 256 + threadIdx.x; it < items; it += (int64_t)gridDim.x * 256) {
+    const int c2 = (int)(it % cp);
+    const int64_t tile = it / cp;
+    const int ti = (int)(tile / TW), tj = (int)(tile - (int64_t)ti * TW);
+    float d0[6][6], d1[6][6];
+#pragma unroll
+    for (int r = 0; r < 6; ++r) {
+      const int yy = 4 * ti - 1 + r;
+#pragma unroll
+      for (int q = 0; q < 6; ++q) {
+        const int xx = 4 * tj - 1 + q;
+        uint32_t u = 0;
+        if (src && yy >= 0 && yy < H && xx >= 0 && xx < W) u = src[((int64_t)yy * W + xx) * cp + c2];
+        d0[r][q] = bf16_lo(u);
+        d1[r][q] = bf16_hi(u);
+      }
+    }
+    // rows: e[r][b] = (B^T d[r][:])[b]; then columns: V[a][b] = (B^T e[:][b])[a]
+    float e0[6][6], e1[6][6];
+#pragma unroll
+    for (int r = 0; r < 6; ++r) {
+      wino_bt(d0[r], e0[r]);
+      wino_bt(d1[r], e1[r]);
+    }
+#pragma unroll
+    for (int b = 0; b < 6; ++b) {
+      float c0v[6], c1v[6], o0[6], o1[6];
+#pragma unroll
+      for (int r = 0; r < 6; ++r) {
+        c0v[r] = e0[r][b];
+        c1v[r] = e1[r][b];
+      }
+      wino_bt(c0v, o0);
+      wino_bt(c1v, o1);
+#pragma unroll
+      for (int a = 0; a < 6; ++a) dst[(int64_t)(a * 6 + b) * cstride + tile * cp + c2] = pack_bf16x2(o0[a], o1[a]);
+    }
+  }
+}
+
+// One thread: channels 4 k4 .. 4 k4 + 3 of one tile of output frame t (blockIdx.y) of sample
+// n (blockIdx.z). Rows of A^T M A first along the component's column index b, then along a.
+__global__ __launch_bounds__(256) void wino_output_kernel(const float* __restrict__ m, const float* __restrict__ bias,
+                                                          const uint16_t* __restrict__ res, uint16_t* __restrict__ y,
+                                                          int N, int T, int H, int W, int K, int TW, int64_t TP) {
+  const int t = blockIdx.y, n = blockIdx.z;
+  const int kq = K / 4;
+  const int64_t cstride = (int64_t)N * T * TP * K;   // floats between components
+  const float* src = m + ((int64_t)n * T + t) * TP * K;
+  const int64_t fbase = ((int64_t)n * T + t) * H * W;
+  const int64_t items = TP * kq;
+  for (int64_t it = (int64_t)blockIdx.x * 256 + threadIdx.x; it < items; it += (int64_t)gridDim.x * 256) {
+    const int k4 = (int)(it % kq);
+    const int64_t tile = it / kq;
+    const int ti = (int)(tile / TW), tj = (int)(tile - (int64_t)ti * TW);
+    float o[4][4][4];                                // [row][column][channel]
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[a][b][e] = 0.0f;
+#pragma unroll
+    for (int a = 0; a < 6; ++a) {
+      float4 mm[6];
+#pragma unroll
+      for (int b = 0; b < 6; ++b)
+        mm[b] = *reinterpret_cast<const float4*>(src + (int64_t)(a * 6 + b) * cstride + tile * K + 4 * k4);
+      // s[x] = (A^T row x) . mm, per channel
+      float sx[4][4];
+      const float* q0 = &mm[0].x;
+      const float* q1 = &mm[1].x;
+      const float* q2 = &mm[2].x;
+      const float* q3 = &mm[3].x;
+      const float* q4 = &mm[4].x;
+      const float* q5 = &mm[5].x;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sx[0][e] = q0[e] + q1[e] + q2[e] + q3[e] + q4[e];
+        sx[1][e] = q1[e] - q2[e] + 2.0f * q3[e] - 2.0f * q4[e];
+        sx[2][e] = q1[e] + q2[e] + 4.0f * q3[e] + 4.0f * q4[e];
+        sx[3][e] = q1[e] - q2[e] + 8.0f * q3[e] - 8.0f * q4[e] + q5[e];
+      }
+      // o[row][x] += A^T[row][a] s[x]; A^T column a: (1,0,0,0), (1,1,1,1), (1,-1,1,-1),
+      // (1,2,4,8), (1,-2,4,-8), (0,0,0,1)
+      const float c1 = a == 0 ? 0.0f : a == 1 ? 1.0f : a == 2 ? -1.0f : a == 3 ? 2.0f : a == 4 ? -2.0f : 0.0f;
+      const float c2 = a == 0 ? 0.0f : a == 1 ? 1.0f : a == 2 ? 1.0f : a == 3 ? 4.0f : a == 4 ? 4.0f : 0.0f;
+      const float c3 = a == 0 ? 0.0f : a == 1 ? 1.0f : a == 2 ? -1.0f : a == 3 ? 8.0f : a == 4 ? -8.0f : 1.0f;
+      const float c0 = a == 5 ? 0.0f : 1.0f;
+#pragma unroll
+      for (int xx = 0; xx < 4; ++xx)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          o[0][xx][e] += c0 * sx[xx][e];
+          o[1][xx][e] += c1 * sx[xx][e];
+          o[2][xx][e] += c2 * sx[xx][e];
+          o[3][xx][e] += c3 * sx[xx][e];
+        }
+    }
+    float bv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (bias) {
+      const float4 b4 = *reinterpret_cast<const float4*>(bias + 4 * k4);
+      bv[0] = b4.x;
+      bv[1] = b4.y;
+      bv[2] = b4.z;
+      bv[3] = b4.w;
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int yy = 4 * ti + r;
+#pragma unroll
+      for (int xx = 0; xx < 4; ++xx) {
+        const int xc = 4 * tj + xx;
+        if (yy < H && xc < W) {
+          const int64_t off = (fbase + (int64_t)yy * W + xc) * K + 4 * k4;
+          float vv[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) vv[e] = o[r][xx][e] + bv[e];
+          if (res) {
+            const uint2 rr = *reinterpret_cast<const uint2*>(res + off);
+            vv[0] += bf16_lo(rr.x);
+            vv[1] += bf16_hi(rr.x);
+            vv[2] += bf16_lo(rr.y);
+            vv[3] += bf16_hi(rr.y);
+          }
+          *reinterpret_cast<uint2*>(y + off) = make_uint2(pack_bf16x2(vv[0], vv[1]), pack_bf16x2(vv[2], vv[3]));
+        }
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------- host side
 
 typedef void (*ConvFn)(ConvParams);
@@ -1787,29 +2022,34 @@ static TileCfg make_slab_cfg() {
 template <int MODE, bool FUSE>
 static int candidates(int bn, int c, TileCfg* out) {
   int n = 0;
-  switch (bn) {
-    case 256:
-      // conv_kernel: 8 waves, two per SIMD: one wave's barrier and LDS waits hide under the
-      // other's MFMAs (measured faster than 4-wave 224/192-row tiles, latent block 0.74 vs
-      // 0.81 ms). The slab kernel: 4 waves of 128 x 128 (accumulators in AGPRs), a third
-      // fewer fragment reads per MFMA; its moves are scheduled between MFMAs, so one wave
-      // per SIMD keeps the matrix pipe fed (latent block 0.600 vs 0.632 ms with 8 waves).
-      if constexpr ((MODE == kCausal || MODE == kPhase || MODE == kTime) && !FUSE) {
-        out[n++] = make_slab_cfg<256, 256, 2, 2, MODE>();
-        out[n++] = make_slab_cfg<224, 256, 1, 4, MODE>();
-      } else {
-        out[n++] = make_cfg<256, 256, 2, 4, kStages, MODE, FUSE>(c);
-      }
-      break;
-    case 128:
-      out[n++] = make_cfg<256, 128, 2, 2, kStages, MODE, FUSE>(c);
-      break;
-    case 64:
-      out[n++] = make_cfg<256, 64, 4, 1, kStages, MODE, FUSE>(c);
-      break;
-    default:
-      out[n++] = make_cfg<256, 32, 4, 1, kStages, MODE, FUSE>(c);
-      break;
+  if constexpr (MODE == kWino) {                    // K > 128 only: the slab tiles
+    out[n++] = make_slab_cfg<256, 256, 2, 2, MODE>();
+    out[n++] = make_slab_cfg<224, 256, 1, 4, MODE>();
+  } else {
+    switch (bn) {
+      case 256:
+        // conv_kernel: 8 waves, two per SIMD: one wave's barrier and LDS waits hide under the
+        // other's MFMAs (measured faster than 4-wave 224/192-row tiles, latent block 0.74 vs
+        // 0.81 ms). The slab kernel: 4 waves of 128 x 128 (accumulators in AGPRs), a third
+        // fewer fragment reads per MFMA; its moves are scheduled between MFMAs, so one wave
+        // per SIMD keeps the matrix pipe fed (latent block 0.600 vs 0.632 ms with 8 waves).
+        if constexpr ((MODE == kCausal || MODE == kPhase || MODE == kTime) && !FUSE) {
+          out[n++] = make_slab_cfg<256, 256, 2, 2, MODE>();
+          out[n++] = make_slab_cfg<224, 256, 1, 4, MODE>();
+        } else {
+          out[n++] = make_cfg<256, 256, 2, 4, kStages, MODE, FUSE>(c);
+        }
+        break;
+      case 128:
+        out[n++] = make_cfg<256, 128, 2, 2, kStages, MODE, FUSE>(c);
+        break;
+      case 64:
+        out[n++] = make_cfg<256, 64, 4, 1, kStages, MODE, FUSE>(c);
+        break;
+      default:
+        out[n++] = make_cfg<256, 32, 4, 1, kStages, MODE, FUSE>(c);
+        break;
+    }
   }
   return n;
 }
@@ -2486,5 +2726,126 @@ extern "C" int head_conv_d2s(const uint16_t* x, sgn_dims d, const uint16_t* cach
     if (!launch_conv(cfg, p, d.n, 1, stream, fn)) return SGN_ELAUNCH;
   }
   if (cache_out && !launch_cache_out(x, d, cache_in, fuse, cache_out, stream)) return SGN_ELAUNCH;
+  return SGN_OK;
+}
+
+namespace sgn {
+
+// Workspace of causal_conv3d_winograd: the transformed input V (bf16 [36][N][T + 2][TP][C])
+// at offset 0, the products M (fp32 [36][N][T][TP][K]) at offset *m_off (256-byte aligned).
+static size_t wino_workspace(sgn_dims d, int k, size_t* m_off) {
+  const int64_t tp = ((d.h + 3) / 4) * ((d.w + 3) / 4);
+  const size_t vb = (size_t)36 * d.n * (d.t + 2) * tp * d.c * 2;
+  const size_t off = (vb + 255) / 256 * 256;
+  if (m_off) *m_off = off;
+  return off + (size_t)36 * d.n * d.t * tp * k * 4;
+}
+
+static bool wino_shape_ok(sgn_dims d, int k, const char* fn) {
+  if (!conv_shape_ok(d, k, fn)) return false;
+  if (k <= 128 || k % 8 != 0) {
+    set_error("%s: K=%d must be a multiple of 8 above 128 (the slab kernel's tiles)", fn, k);
+    return false;
+  }
+  const int64_t tp = ((d.h + 3) / 4) * ((d.w + 3) / 4);
+  if ((tp + 256) * (int64_t)k * 4 >= ((int64_t)1 << 31) || (tp + 256) * d.c * 2 >= ((int64_t)1 << 31)) {
+    set_error("%s: a frame of %lld tiles exceeds the 2 GiB frame limit of the products", fn, (long long)tp);
+    return false;
+  }
+  return true;
+}
+
+}  // namespace sgn
+
+extern "C" size_t causal_conv3d_winograd_workspace(sgn_dims d, int k) {
+  clear_error();
+  if (!wino_shape_ok(d, k, "causal_conv3d_winograd_workspace")) return 0;
+  return wino_workspace(d, k, nullptr);
+}
+
+extern "C" int causal_conv3d_winograd(const uint16_t* x, sgn_dims d, const uint16_t* cache_in, const uint16_t* u,
+                                      int k, const float* bias, const uint16_t* residual, uint16_t* y,
+                                      uint16_t* cache_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  const char* fn = "causal_conv3d_winograd";
+  clear_error();
+  if (!wino_shape_ok(d, k, fn)) return SGN_EINVAL;
+  if (!x || !u || !y) {
+    set_error("%s: x, u and y are required", fn);
+    return SGN_EINVAL;
+  }
+  if (!aligned16(x) || !aligned16(u) || !aligned16(y) || (cache_in && !aligned16(cache_in)) ||
+      (residual && !aligned16(residual)) || (cache_out && !aligned16(cache_out)) || (bias && !aligned16(bias))) {
+    set_error("%s: tensors (and bias) must be 16-byte aligned", fn);
+    return SGN_EALIGN;
+  }
+  size_t m_off = 0;
+  const size_t need = wino_workspace(d, k, &m_off);
+  if (!ws || ws_bytes < need) {
+    set_error("%s: workspace of %zu bytes required, got %zu", fn, need, ws ? ws_bytes : 0);
+    return SGN_EWORKSPACE;
+  }
+  if (!aligned16(ws)) {
+    set_error("%s: workspace must be 16-byte aligned", fn);
+    return SGN_EALIGN;
+  }
+  const size_t xb = (size_t)(d.n * d.t * d.h * d.w * d.c) * 2;
+  const size_t yb = (size_t)(d.n * d.t * d.h * d.w) * k * 2;
+  const size_t cb = (size_t)(d.n * 2 * d.h * d.w * d.c) * 2;
+  const size_t ub = (size_t)36 * k * 3 * d.c * 2;
+  if (overlap(y, yb, x, xb) || overlap(y, yb, u, ub) || (cache_in && overlap(y, yb, cache_in, cb)) ||
+      (residual && overlap(y, yb, residual, yb)) ||
+      (cache_out && (overlap(cache_out, cb, x, xb) || overlap(cache_out, cb, y, yb) ||
+                     overlap(cache_out, cb, u, ub) || (cache_in && overlap(cache_out, cb, cache_in, cb)) ||
+                     (residual && overlap(cache_out, cb, residual, yb))))) {
+    set_error("%s: an output overlaps an input or the other output", fn);
+    return SGN_EALIAS;
+  }
+  const struct {
+    const void* p;
+    size_t n;
+  } others[] = {{x, xb}, {u, ub}, {y, yb}, {cache_in, cb}, {cache_out, cb}, {residual, yb}, {bias, (size_t)k * 4}};
+  for (const auto& o : others)
+    if (o.p && overlap(ws, need, o.p, o.n)) {
+      set_error("%s: the workspace overlaps an input or an output", fn);
+      return SGN_EALIAS;
+    }
+  const int th = (int)((d.h + 3) / 4), tw = (int)((d.w + 3) / 4);
+  const int64_t tp = (int64_t)th * tw;
+  uint16_t* v = static_cast<uint16_t*>(ws);
+  float* m = reinterpret_cast<float*>(static_cast<char*>(ws) + m_off);
+  {
+    const int cp = (int)(d.c / 2);
+    int64_t blocks = (tp * cp + 255) / 256;
+    if (blocks > 1024) blocks = 1024;
+    wino_input_kernel<<<dim3((unsigned)blocks, (unsigned)(d.t + 2), (unsigned)d.n), 256, 0, stream>>>(
+        reinterpret_cast<const uint32_t*>(x), reinterpret_cast<const uint32_t*>(cache_in),
+        reinterpret_cast<uint32_t*>(v), (int)d.n, (int)d.t, (int)d.h, (int)d.w, cp, tw, tp);
+    if (!launch_ok("causal_conv3d_winograd (input transform)")) return SGN_ELAUNCH;
+  }
+  {
+    ConvParams p = {};
+    p.x = v;
+    p.w = u;
+    p.yf = m;
+    p.T = (int)d.t;
+    p.H = th;
+    p.W = tw;
+    p.C = (int)d.c;
+    p.K = k;
+    p.mper = d.t * tp;
+    p.Tx = (int)d.t + 2;
+    p.x0 = 2;
+    p.wino_n = (int)d.n;
+    const TileCfg cfg = choose_tile<kWino, false>(tp, d.t, k, p.C, 36 * d.n);
+    if (!launch_conv(cfg, p, 36 * d.n, 1, stream, fn)) return SGN_ELAUNCH;
+  }
+  {
+    int64_t blocks = (tp * (k / 4) + 255) / 256;
+    if (blocks > 1024) blocks = 1024;
+    wino_output_kernel<<<dim3((unsigned)blocks, (unsigned)d.t, (unsigned)d.n), 256, 0, stream>>>(
+        m, bias, residual, y, (int)d.n, (int)d.t, (int)d.h, (int)d.w, k, tw, tp);
+    if (!launch_ok("causal_conv3d_winograd (output transform)")) return SGN_ELAUNCH;
+  }
+  if (cache_out && !launch_cache_out(x, d, cache_in, nullptr, cache_out, stream)) return SGN_ELAUNCH;
   return SGN_OK;
 }

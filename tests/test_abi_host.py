@@ -342,3 +342,44 @@ def test_noalloc_stats_rejects():
     _err(lib.gn_silu_stats_noalloc(FAKE + 2, D(), 32, far, None), EALIGN)
     _err(lib.gn_silu_stats_noalloc(FAKE, D(n=200, c=2048), 2048, far, None), EINVAL)   # beyond the scratch
     _err(lib.gn_silu_stats_noalloc(FAKE, D(), 32, FAKE + 64, None), EALIAS)            # stats inside x
+
+
+@pytest.mark.parametrize("k,c", [(8, 16), (3, 64)])
+def test_winograd_weights_match_oracle(k, c):
+    """The host F(4x4,3x3) weight prep (fp32 sums, one rounding to bf16) within one bf16 ulp of
+    the oracle's fp64 transform rounded once (the fp32 sum may round before the bf16 rounding)."""
+    from oracle import winograd as ow
+    import synthgen as sg
+    w = sg.normal((k, 3, 3, 3, c), k + c, sg.W1, std=0.2)
+    u = sga.winograd_prepare_weights(w)
+    assert u.shape == (36, k, 3, c)
+    ref = ow.weight_transform(w.float().numpy().astype(np.float64))      # (6, 6, K, 3, C)
+    ref = obf16.round_rne(ref.reshape(36, k, 3, c))
+    got = u.view(torch.int16).numpy().view(np.uint16)
+    d = obf16.ulp_distance(got, ref)
+    assert d.max() <= 1 and (d == 0).mean() > 0.95
+
+
+def test_winograd_rejects():
+    lib = sga.load_library()
+    far = FAKE + (1 << 33)
+    ws = far + (1 << 32)
+    need = lib.causal_conv3d_winograd_workspace(D(c=64), 256)
+    assert need > 0
+    assert lib.causal_conv3d_winograd_workspace(D(c=64), 128) == 0                 # K <= 128
+    assert lib.causal_conv3d_winograd_workspace(D(c=72), 256) == 0                 # C % 64
+    _err(lib.causal_conv3d_winograd(FAKE, D(), None, far, 120, None, None, far + (1 << 30), None, ws, need, None),
+         EINVAL)                                                                      # K % 8, K <= 128
+    _err(lib.causal_conv3d_winograd(None, D(), None, far, 256, None, None, far + (1 << 30), None, ws, need, None),
+         EINVAL)
+    _err(lib.causal_conv3d_winograd(FAKE, D(), None, far, 256, None, None, far + (1 << 30), None, ws, 16, None),
+         EWORKSPACE)
+    _err(lib.causal_conv3d_winograd(FAKE + 8, D(), None, far, 256, None, None, far + (1 << 30), None, ws, need, None),
+         EALIGN)
+    _err(lib.causal_conv3d_winograd(FAKE, D(), None, far, 256, None, None, FAKE + 64, None, ws, need, None),
+         EALIAS)                                                                      # y inside x
+    _err(lib.causal_conv3d_winograd(FAKE, D(), None, far, 256, None, None, far + (1 << 30), None, FAKE + 256, need,
+                                    None), EALIAS)                                    # workspace over x
+    _err(lib.winograd_prepare_weights(None, 4, 64, FAKE), EINVAL)
+    buf = np.zeros(36 * 4 * 3 * 64, dtype=np.uint16)
+    _err(lib.winograd_prepare_weights(buf.ctypes.data, 4, 64, buf.ctypes.data + 64), EALIAS)
