@@ -399,7 +399,7 @@ def box_ceilings(dev):
     """Sustained bf16 MFMA (random / constant operands) and HBM read / copy rates of this GPU,
     from the probe kernels in libsgnprobe.so (about a second in all)."""
     import ctypes
-    path = os.path.join(ROOT, "silu_gn_amd", "libsgnprobe.so")
+    path = os.path.join(ROOT, "bench_probe", "libsgnprobe.so")
     if not os.path.exists(path):
         return None
     lib = ctypes.CDLL(path)

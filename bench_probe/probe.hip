@@ -5,6 +5,7 @@
 //   constant operand bits. The rate with random bits is the one real data sees: MFMA power
 //   grows with operand toggling and the clock drops to hold the board's power limit.
 // - HBM: a streaming read (16-byte non-temporal loads, xor-reduced) and a streaming copy.
+// Built by silu_gn_amd/build.py into bench_probe/libsgnprobe.so; only bench.py loads it.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -88,18 +89,26 @@ __global__ __launch_bounds__(256) void read_probe(const u32x4* src, size_t n, u3
   out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = acc;
 }
 
+// The copy sweeps grid-wide (pass k of workgroup b covers packets (k * grid + b) * 1024 ..
+// + 1023, 4 in flight per thread), as the GroupNorm apply does: with whole slices per
+// workgroup the copy ran at about 4.9 TB/s, swept at about 5.7.
+constexpr int kCopyU = 4;
+constexpr int kCopyBlocks = 8192;
 __global__ __launch_bounds__(256) void copy_probe(const u32x4* src, u32x4* dst, size_t n) {
-  const size_t per = (n + gridDim.x - 1) / gridDim.x;
-  const size_t beg = (size_t)blockIdx.x * per, end = beg + per < n ? beg + per : n;
-  size_t i = beg + threadIdx.x;
-  for (; i + (kU - 1) * 256 < end; i += kU * 256) {
-    u32x4 v[kU];
+  const size_t step = (size_t)gridDim.x * 256 * kCopyU;
+  for (size_t base = (size_t)blockIdx.x * 256 * kCopyU; base < n; base += step) {
+    u32x4 v[kCopyU];
 #pragma unroll
-    for (int u = 0; u < kU; ++u) v[u] = __builtin_nontemporal_load(src + i + u * 256);
+    for (int u = 0; u < kCopyU; ++u) {
+      const size_t i = base + u * 256 + threadIdx.x;
+      if (i < n) v[u] = __builtin_nontemporal_load(src + i);
+    }
 #pragma unroll
-    for (int u = 0; u < kU; ++u) __builtin_nontemporal_store(v[u], dst + i + u * 256);
+    for (int u = 0; u < kCopyU; ++u) {
+      const size_t i = base + u * 256 + threadIdx.x;
+      if (i < n) __builtin_nontemporal_store(v[u], dst + i);
+    }
   }
-  for (; i < end; i += 256) __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
 }
 
 constexpr int kProbeBlocks = 1792;   // 7 per CU on 256 CUs: one round
@@ -127,6 +136,6 @@ extern "C" int sgn_probe_read(const void* src, size_t bytes, void* out, hipStrea
 // Streaming copy of `bytes` (a multiple of 16) from src to dst (non-overlapping).
 extern "C" int sgn_probe_copy(const void* src, void* dst, size_t bytes, hipStream_t s) {
   if (!src || !dst || bytes % 16) return -1;
-  copy_probe<<<kProbeBlocks, 256, 0, s>>>(static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), bytes / 16);
+  copy_probe<<<kCopyBlocks, 256, 0, s>>>(static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), bytes / 16);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }

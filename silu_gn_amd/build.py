@@ -17,9 +17,11 @@ CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libsilugn.so")
 SOURCES = ["abi.cpp", "gn.hip", "conv.hip"]
-# Ceiling probes used by bench.py only (not part of the C ABI): a library of their own.
-PROBE_LIB = os.path.join(HERE, "libsgnprobe.so")
-PROBE_SOURCES = ["probe.hip"]
+# Ceiling probes used by bench.py only (not part of the C ABI): a library of their own,
+# built from bench_probe/ beside bench.py.
+PROBE_DIR = os.path.join(ROOT, "bench_probe")
+PROBE_LIB = os.path.join(PROBE_DIR, "libsgnprobe.so")
+PROBE_SOURCES = [os.path.join(PROBE_DIR, "probe.hip")]
 
 # -packed-fp32-ops: no packed fp32 instructions are generated (hipcc's host pass warns
 # that it does not know the feature; harmless). -ffp-contract=off: the compensated
@@ -40,7 +42,7 @@ def _hipcc():
 
 
 def _compile(src: str) -> str:
-    obj = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
+    obj = os.path.join(OBJ, os.path.splitext(os.path.basename(src))[0] + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
     cmd = [_hipcc(), *HIPFLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
