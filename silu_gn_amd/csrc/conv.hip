@@ -1574,22 +1574,25 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_slab_kernel(ConvParams
 //   output channels x 32 input channels, rows 12-15 zero). The waves' partial sums are
 //   added through LDS when an output frame is complete. Eight waves (two per SIMD) cover
 //   C = 256, four cover C = 128.
-// - A workgroup owns one output row h and 64 columns (4 segments of 16) for every frame,
-//   and streams the input frames of P = cat(cache, x) once: frame p feeds output frames
-//   p - dt, dt = 0..2, held in a ring of 3 accumulators per segment. Output frame t is
-//   complete after input frame t + 2.
-// - A unit of work is (input frame, input row h + dh - 1, the wave's chunk). Its 66 input
-//   columns w0 - 1 .. w0 + 64 (64-byte rows) move global -> LDS with buffer_load ... lds
-//   into the wave's own ring of 3 units, two units ahead; each wave waits only for its own
-//   moves (counted vmcnt), so the ring needs no barrier.
-// - With two waves per SIMD and one instruction per wave per issue cycle, the kernel is
-//   bound by instruction issue as much as by the matrix pipe: the loop over a group of 3
-//   frames is unrolled so that a unit's ring slot, row tap and accumulator slots are
-//   constants, every LDS read is a per-lane base (one per column tap) plus an immediate,
-//   and the frame descriptors are built once per group.
+// - A workgroup owns two output rows h0, h0 + 1 and 48 columns (3 segments of 16) for every
+//   frame, and streams the input frames of P = cat(cache, x) once: frame p feeds output
+//   frames p - dt, dt = 0..2, held in a ring of 3 accumulators per (output row, segment).
+//   Output frame t is complete after input frame t + 2.
+// - A unit of work is (input frame, input row h0 - 1 + r, r = 0..3, the wave's chunk): input
+//   row h0 - 1 + r feeds output row h0 through row tap r and row h0 + 1 through row tap
+//   r - 1. Its 50 input columns w0 - 1 .. w0 + 48 (64-byte rows) move global -> LDS with
+//   buffer_load ... lds into the wave's own ring of 3 units, two units ahead; each wave waits
+//   only for its own moves (counted vmcnt), so the ring needs no barrier.
+// - The kernel is bound by these moves, not by the matrix pipe: with every MFMA removed it
+//   runs as long. Two output rows per workgroup stage 4 input rows per frame for 2 output
+//   rows, where one row per workgroup staged 3 for each; the moves per output pixel drop by
+//   about a third. (The accumulators of 2 rows fit the register file with 3 segments.)
+// - The loop over a group of 3 frames (12 units) is unrolled so that a unit's ring slot, row
+//   taps and accumulator slots are constants, every LDS read is a per-lane base (one per
+//   column tap) plus an immediate, and the frame descriptors are built once per group.
 // - The B operand of a column tap dw is the 16-row LDS window starting at row 16 s + dw:
-//   one input row staged once serves all 3 column taps and, through the frame ring, all 3
-//   frame taps (9 MFMAs per window set). The 16-byte chunks of row r sit at chunk
+//   one input row staged once serves all 3 column taps, both output rows and, through the
+//   frame ring, all 3 frame taps. The 16-byte chunks of row r sit at chunk
 //   logical ^ ((r >> 1) & 3): LDS serves a 16-byte read 8 lanes (128 bytes) at a time, and
 //   any 8 consecutive rows then hit 8 distinct bank groups, whatever the window offset.
 // - Raw-buffer loads over the input frame: rows above or below the frame and columns
@@ -1597,12 +1600,16 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_slab_kernel(ConvParams
 // The epilogue adds the bias, clamps if asked, and writes the 2x2 depth-to-space video
 // (channel k = 4c + 2dy + dx) as 4-byte pairs, 64 contiguous bytes per 16 columns.
 typedef __attribute__((ext_vector_type(4))) float f32x4;
-constexpr int kHeadSeg = 4;              // 16-column segments per workgroup (W = 624: 10 blocks)
-constexpr int kHeadRows = 80;            // LDS rows per unit (66 used: 64 columns + 2 edges)
+constexpr int kHeadSeg = 3;              // 16-column segments per workgroup (W = 624: 13 blocks)
+constexpr int kHeadOut = 2;              // output rows per workgroup
+constexpr int kHeadIn = kHeadOut + 2;    // input rows per frame (units)
+constexpr int kHeadRows = 64;            // LDS rows per unit (50 used: 48 columns + 2 edges)
 constexpr int kHeadMoves = kHeadRows / 16; // 1 KB moves per unit and wave
-constexpr int kHeadRed = 1;              // reduction buffers (one: a barrier before the writes)
-constexpr int kHeadRing = 3;             // units per wave in LDS (u % 3 = the unit's row tap)
+constexpr int kHeadRing = 3;             // units per wave in LDS (unit u in slot u % 3)
 
+__host__ __device__ constexpr int head_lds_bytes(int nw) {
+  return nw * kHeadRing * kHeadRows * 64 + nw * kHeadOut * kHeadSeg * 64 * 16 + 64;
+}
 
 template <int NW>
 __global__ __launch_bounds__(64 * NW, 1) void head_kernel(ConvParams p, int wblocks) {
@@ -1612,26 +1619,25 @@ __global__ __launch_bounds__(64 * NW, 1) void head_kernel(ConvParams p, int wblo
   const int j = lane & 15, g = lane >> 4;            // row in a 16-row window, channel group
   const int C = p.C, H = p.H, W = p.W, T = p.T;
   const int HW = H * W;
+  const int HP = (H + kHeadOut - 1) / kHeadOut;      // row pairs
   const uint32_t frame_bytes = (uint32_t)HW * C * 2;
   constexpr int UNIT = kHeadRows * 64;               // bytes per unit in LDS
   char* ring = smem + wave * (kHeadRing * UNIT);
-  f32x4* red = reinterpret_cast<f32x4*>(smem + NW * kHeadRing * UNIT);   // [kHeadRed][NW][seg][64]
-  float* sbias = reinterpret_cast<float*>(red + kHeadRed * NW * kHeadSeg * 64);
+  f32x4* red = reinterpret_cast<f32x4*>(smem + NW * kHeadRing * UNIT);   // [NW][out row][seg][64]
+  float* sbias = reinterpret_cast<float*>(red + NW * kHeadOut * kHeadSeg * 64);
 
-  // Workgroup -> (n, column block, h), rows fastest and XCD-aware: each XCD takes a
-  // contiguous run, so the workgroups it runs at once are consecutive rows of one column
-  // block, and each input row -- read by the workgroups of 3 neighbouring rows -- comes
-  // from HBM about once (with columns fastest, the third reader of a row started only after
-  // the first had finished, and the row was read again).
+  // Workgroup -> (n, column block, row pair), row pairs fastest and XCD-aware: each XCD
+  // takes a contiguous run, so the workgroups it runs at once are consecutive row pairs of
+  // one column block, and the input rows two neighbouring pairs share are read from L2.
   int blk;
   {
     const int bid = blockIdx.x, nb = p.nblocks;
     const int xcd = bid & 7, idx = bid >> 3, q = nb >> 3, r = nb & 7;
     blk = xcd < r ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
   }
-  const int h = blk % H;
-  const int wb = (blk / H) % wblocks;
-  const int n = blk / (wblocks * H);
+  const int h0 = (blk % HP) * kHeadOut;
+  const int wb = (blk / HP) % wblocks;
+  const int n = blk / (wblocks * HP);
   const int w0 = wb * (16 * kHeadSeg);
 
   // Weight fragments of this wave's chunk, one per tap.
@@ -1646,7 +1652,7 @@ __global__ __launch_bounds__(64 * NW, 1) void head_kernel(ConvParams p, int wblo
   }
   if (tid < 16) sbias[tid] = (p.bias && tid < 12) ? p.bias[tid] : 0.0f;
 
-  // The 4 moves of a unit: move i writes LDS rows 16 i .. 16 i + 15; lane l fills row
+  // The moves of a unit: move i writes LDS rows 16 i .. 16 i + 15; lane l fills row
   // 16 i + l / 4 (column w0 - 1 + row) at physical chunk l & 3, i.e. it loads logical chunk
   // (l & 3) ^ ((row >> 1) & 3) = (l & 3) ^ ((l >> 3) & 3). Rows past 49 and columns outside
   // the frame get kOOB (zeros, no memory access); adding a row offset keeps them out of range.
@@ -1661,11 +1667,13 @@ __global__ __launch_bounds__(64 * NW, 1) void head_kernel(ConvParams p, int wblo
     }
   }
 
-  f32x4 acc[3][kHeadSeg];
+  f32x4 acc[kHeadOut][3][kHeadSeg];
 #pragma unroll
-  for (int r = 0; r < 3; ++r)
+  for (int o = 0; o < kHeadOut; ++o)
 #pragma unroll
-    for (int s = 0; s < kHeadSeg; ++s) acc[r][s] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int r = 0; r < 3; ++r)
+#pragma unroll
+      for (int s = 0; s < kHeadSeg; ++s) acc[o][r][s] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // Source frame pf of P = cat(cache, x): a descriptor over it (no records: zeros).
   auto frame_rsrc = [&](int pf) {
@@ -1673,16 +1681,17 @@ __global__ __launch_bounds__(64 * NW, 1) void head_kernel(ConvParams p, int wblo
     if (pf < 2 && p.cache) return make_rsrc(p.cache + ((int64_t)n * 2 + pf) * HW * C, frame_bytes);
     return make_rsrc(p.x, 0);
   };
-  // Byte offset of input row h + dh - 1 in a frame (row -1 wraps: out of range).
-  uint32_t rowoff[3];
+  // Byte offset of input row h0 - 1 + r in a frame (row -1 wraps, rows past H - 1 run past
+  // the frame: both out of range, zeros).
+  uint32_t rowoff[kHeadIn];
 #pragma unroll
-  for (int dh = 0; dh < 3; ++dh) rowoff[dh] = (uint32_t)((h + dh - 1) * W * C * 2);
-  // Unit (frame pf, row tap dh) goes to ring slot dh.
-  auto issue = [&](const Rsrc& rs, auto DH_) __attribute__((always_inline)) {
-    constexpr int DH = decltype(DH_)::value;
-    char* dst = ring + DH * UNIT;
+  for (int r = 0; r < kHeadIn; ++r) rowoff[r] = (uint32_t)((h0 - 1 + r) * W * C * 2);
+  // Unit (frame, input row R) into ring slot SL.
+  auto issue = [&](const Rsrc& rs, auto R_, auto SL_) __attribute__((always_inline)) {
+    constexpr int R = decltype(R_)::value, SL = decltype(SL_)::value;
+    char* dst = ring + SL * UNIT;
 #pragma unroll
-    for (int i = 0; i < kHeadMoves; ++i) dma16(rs, pvo[i] + rowoff[DH], 0, dst + i * 1024);
+    for (int i = 0; i < kHeadMoves; ++i) dma16(rs, pvo[i] + rowoff[R], 0, dst + i * 1024);
   };
   // Window of column tap dw in segment s: rows 16 s + dw + j at chunk g ^ ((row >> 1) & 3);
   // 16 s does not change row bits 1-2, so per lane one base per dw, plus s KB.
@@ -1692,87 +1701,102 @@ __global__ __launch_bounds__(64 * NW, 1) void head_kernel(ConvParams p, int wblo
     const int r = dw + j;
     woff[dw] = (uint32_t)(ring - smem) + r * 64 + ((g ^ ((r >> 1) & 3)) << 4);
   }
-  // Unit of frame pf = 3 q + U, row tap DH (in slot DH): 3 column taps x 3 frame taps per
-  // segment into the accumulator slots of output frames pf - dt (slot (U - dt) mod 3). All
-  // 9 windows are read before the first MFMA.
-  auto compute_unit = [&](auto U_, auto DH_) __attribute__((always_inline)) {
+  // Unit of frame pf = 3 q + U, input row R (in ring slot SL): for each output row o with
+  // row tap dh = R - o in 0..2, 3 column taps x 3 frame taps per segment into the
+  // accumulator slots of output frames pf - dt (slot (U - dt) mod 3). The windows of segment
+  // s + 1 are read while segment s's MFMAs run (two buffers of 3 fragments).
+  auto compute_unit = [&](auto U_, auto R_, auto SL_) __attribute__((always_inline)) {
     constexpr int U = decltype(U_)::value;
-    constexpr int DH = decltype(DH_)::value;
-    bf16x8 bb[kHeadSeg][3];
+    constexpr int R = decltype(R_)::value, SL = decltype(SL_)::value;
+    bf16x8 bb[2][3];
 #pragma unroll
-    for (int sg = 0; sg < kHeadSeg; ++sg)
+    for (int dw = 0; dw < 3; ++dw) bb[0][dw] = *reinterpret_cast<const bf16x8*>(smem + woff[dw] + SL * UNIT);
+#pragma unroll
+    for (int sg = 0; sg < kHeadSeg; ++sg) {
+      if (sg + 1 < kHeadSeg) {
+#pragma unroll
+        for (int dw = 0; dw < 3; ++dw)
+          bb[(sg + 1) & 1][dw] = *reinterpret_cast<const bf16x8*>(smem + woff[dw] + SL * UNIT + (sg + 1) * 1024);
+      }
 #pragma unroll
       for (int dw = 0; dw < 3; ++dw)
-        bb[sg][dw] = *reinterpret_cast<const bf16x8*>(smem + woff[dw] + DH * UNIT + sg * 1024);
-    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int sg = 0; sg < kHeadSeg; ++sg)
+        for (int o = 0; o < kHeadOut; ++o) {
+          const int dh = R - o;
+          if (dh < 0 || dh > 2) continue;            // constant after unrolling
 #pragma unroll
-      for (int dw = 0; dw < 3; ++dw) {
-#pragma unroll
-        for (int dt = 0; dt < 3; ++dt) {
-          const int slot = ((U - dt) % 3 + 3) % 3;
-          acc[slot][sg] =
-              __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[dt * 9 + DH * 3 + dw], bb[sg][dw], acc[slot][sg], 0, 0, 0);
+          for (int dt = 0; dt < 3; ++dt) {
+            const int slot = ((U - dt) % 3 + 3) % 3;
+            acc[o][slot][sg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[dt * 9 + dh * 3 + dw], bb[sg & 1][dw],
+                                                                       acc[o][slot][sg], 0, 0, 0);
+          }
         }
-      }
+    }
   };
 
   // Output frame t (accumulator slot S) is complete: add the waves' partial sums through LDS
-  // (kHeadRed buffers; with one, a barrier before the writes as well as after them), then
-  // wave w < kHeadSeg writes segment w; the slot is cleared for output frame t + 3. Slots of
-  // frames before 0 only collect the taps that reach before the first frame: they are
-  // cleared without a store.
-  int rb = 0;
+  // (one buffer: a barrier before the writes as well as after them), then wave
+  // o * kHeadSeg + s writes output row h0 + o, segment s; the slot is cleared for output
+  // frame t + 3. Slots of frames before 0 only collect the taps that reach before the first
+  // frame: they are cleared without a store.
   auto retire = [&](int t, auto S_) __attribute__((always_inline)) {
     constexpr int S = decltype(S_)::value;
     if (t < 0) {
 #pragma unroll
-      for (int sg = 0; sg < kHeadSeg; ++sg) acc[S][sg] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int o = 0; o < kHeadOut; ++o)
+#pragma unroll
+        for (int sg = 0; sg < kHeadSeg; ++sg) acc[o][S][sg] = f32x4{0.f, 0.f, 0.f, 0.f};
       return;
     }
-    f32x4* rr = red + rb * (NW * kHeadSeg * 64);
-    if (kHeadRed == 1) stage_barrier();              // every wave has read the previous frame's sums
+    stage_barrier();                                 // every wave has read the previous frame's sums
 #pragma unroll
-    for (int sg = 0; sg < kHeadSeg; ++sg) {
-      rr[(wave * kHeadSeg + sg) * 64 + lane] = acc[S][sg];
-      acc[S][sg] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+    for (int o = 0; o < kHeadOut; ++o)
+#pragma unroll
+      for (int sg = 0; sg < kHeadSeg; ++sg) {
+        red[((wave * kHeadOut + o) * kHeadSeg + sg) * 64 + lane] = acc[o][S][sg];
+        acc[o][S][sg] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
     // LDS writes complete, then the barrier: not __syncthreads, whose fence would also
     // wait for the moves in flight.
     wait_lgkm0();
     stage_barrier();
-    if (t < T && g < 3 && wave < kHeadSeg) {
-      const int sg = wave;
-      const int col = w0 + 16 * sg + j;
-      if (col < W) {
-        f32x4 v = rr[sg * 64 + lane];
+    // (output row, segment) part `part` is added and stored by wave part % NW (with 4 waves,
+    // each takes two of the 6 parts).
+    constexpr int PARTS = kHeadOut * kHeadSeg;
 #pragma unroll
-        for (int q = 1; q < NW; ++q) v += rr[(q * kHeadSeg + sg) * 64 + lane];
-        float o[4];
+    for (int part0 = 0; part0 < PARTS; part0 += NW) {
+      const int part = part0 + wave;
+      if (t >= T || g >= 3 || part >= PARTS) continue;
+      const int o = part / kHeadSeg, sg = part % kHeadSeg;
+      const int h = h0 + o;
+      const int col = w0 + 16 * sg + j;
+      if (h < H && col < W) {
+        f32x4 v = red[part * 64 + lane];
+#pragma unroll
+        for (int q = 1; q < NW; ++q) v += red[(q * PARTS + part) * 64 + lane];
+        float ov[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          o[r] = v[r] + sbias[4 * g + r];
-          if (p.clamp) o[r] = fminf(fmaxf(o[r], -1.0f), 1.0f);
+          ov[r] = v[r] + sbias[4 * g + r];
+          if (p.clamp) ov[r] = fminf(fmaxf(ov[r], -1.0f), 1.0f);
         }
         const int64_t W2 = 2 * (int64_t)W;
         const int64_t base = (((int64_t)n * 3 + g) * T + t) * (2 * (int64_t)H) * W2 + 2 * (int64_t)col;
-        *reinterpret_cast<uint32_t*>(p.y + base + (2 * h) * W2) = pack_bf16x2(o[0], o[1]);
-        *reinterpret_cast<uint32_t*>(p.y + base + (2 * h + 1) * W2) = pack_bf16x2(o[2], o[3]);
+        *reinterpret_cast<uint32_t*>(p.y + base + (2 * h) * W2) = pack_bf16x2(ov[0], ov[1]);
+        *reinterpret_cast<uint32_t*>(p.y + base + (2 * h + 1) * W2) = pack_bf16x2(ov[2], ov[3]);
       }
     }
-    rb = kHeadRed == 1 ? 0 : rb ^ 1;
   };
 
-  // Frames in groups of three; without a cache the first group skips the two zero frames
-  // (a separate copy of the group, so both keep static registers). Frames past T + 1 read
-  // zeros and store nothing. Units go in order (frame, row tap); the moves of the next two
-  // units are in flight while one computes.
+  // Frames in groups of three (12 units); without a cache the first group skips the compute
+  // of the two zero frames (a separate copy of the group, so both keep static registers).
+  // Frames past T + 1 read zeros and store nothing. Units go in order (frame, input row);
+  // the moves of the next two units are in flight while one computes.
   const int groups3 = (T + 2 + 2) / 3;
   {
     const Rsrc f0 = frame_rsrc(0);
-    issue(f0, IC<0>{});
-    issue(f0, IC<1>{});
+    issue(f0, IC<0>{}, IC<0>{});
+    issue(f0, IC<1>{}, IC<1>{});
   }
   auto group = [&](int q, auto SKIP_) __attribute__((always_inline)) {
     constexpr bool SKIP = decltype(SKIP_)::value != 0;
@@ -1781,15 +1805,13 @@ __global__ __launch_bounds__(64 * NW, 1) void head_kernel(ConvParams p, int wblo
                fr3 = frame_rsrc(3 * q + 3);
     auto step = [&](auto K_) __attribute__((always_inline)) {
       constexpr int K = decltype(K_)::value;
-      constexpr int U = K / 3, DH = K % 3;
-      constexpr int KN = K + 2, UN = KN / 3, DHN = KN % 3;   // the unit issued after this one
+      constexpr int U = K / kHeadIn, R = K % kHeadIn;
+      constexpr int KN = K + 2, UN = KN / kHeadIn, RN = KN % kHeadIn;   // the unit issued after this one
       wait_vm<kHeadMoves>();                         // this wave's moves of this unit landed
-      if (!SKIP || U == 2) compute_unit(IC<U>{}, IC<DH>{});
+      if (!SKIP || U == 2) compute_unit(IC<U>{}, IC<R>{}, IC<K % kHeadRing>{});
       const Rsrc& rn = UN == 0 ? fr0 : UN == 1 ? fr1 : UN == 2 ? fr2 : fr3;
-      issue(rn, IC<DHN>{});                          // into the slot this unit's row tap used
-      if (K == 2) retire(3 * q - 2, IC<1>{});
-      if (K == 5) retire(3 * q - 1, IC<2>{});
-      if (K == 8) retire(3 * q, IC<0>{});
+      issue(rn, IC<RN>{}, IC<KN % kHeadRing>{});     // into the slot the unit before this one used
+      if (R == kHeadIn - 1) retire(3 * q + U - 2, IC<(U + 1) % 3>{});
     };
     step(IC<0>{});
     step(IC<1>{});
@@ -1800,6 +1822,9 @@ __global__ __launch_bounds__(64 * NW, 1) void head_kernel(ConvParams p, int wblo
     step(IC<6>{});
     step(IC<7>{});
     step(IC<8>{});
+    step(IC<9>{});
+    step(IC<10>{});
+    step(IC<11>{});
   };
   if (p.cache)
     group(0, IC<0>{});
@@ -2699,16 +2724,16 @@ extern "C" int head_conv_d2s(const uint16_t* x, sgn_dims d, const uint16_t* cach
   p.mper = d.t * d.h * d.w;
   p.clamp = clamp ? 1 : 0;
   if (!fuse && (p.C == 128 || p.C == 256)) {
-    // The dedicated head kernel: one workgroup per (sample, row, 64 columns).
+    // The dedicated head kernel: one workgroup per (sample, row pair, 48 columns).
     const int wblocks = (p.W + 16 * kHeadSeg - 1) / (16 * kHeadSeg);
-    const int64_t nb = (int64_t)d.n * p.H * wblocks;
+    const int64_t nb = (int64_t)d.n * ((p.H + kHeadOut - 1) / kHeadOut) * wblocks;
     if (nb >= ((int64_t)1 << 31)) {
       set_error("%s: problem too large for one launch", fn);
       return SGN_ELAUNCH;
     }
     p.nblocks = (int)nb;
     const int nw = p.C / 32;
-    const int lds = nw * kHeadRing * kHeadRows * 64 + kHeadRed * nw * kHeadSeg * 64 * 16 + 64;
+    const int lds = head_lds_bytes(nw);
     const void* fn_ptr = nw == 4 ? (const void*)head_kernel<4> : (const void*)head_kernel<8>;
     hipError_t e = hipFuncSetAttribute(fn_ptr, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) {
