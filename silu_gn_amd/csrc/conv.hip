@@ -1420,26 +1420,28 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_slab_kernel(ConvParams
     if (NRD > PAIRS) __builtin_amdgcn_sched_group_barrier(0x100, NRD - PAIRS, 0);
     if (NMF > PAIRS) __builtin_amdgcn_sched_group_barrier(0x008, NMF - PAIRS, 0);
   };
-  // Steady-state second phase: the iteration's moves, then the next fragments, each placed
-  // after one MFMA.
+  // Steady-state second phase: the next stage's fragment reads first (the next phase's
+  // first MFMA needs them), then the iteration's moves (needed L stages later), each placed
+  // after one MFMA. The reads come first in program order too: a move writes LDS, so the
+  // scheduler would not lift a read above it.
   constexpr int NV = DW + SPW;
-  constexpr int PV = NV < NMF ? NV : NMF;
-  constexpr int RM = NMF - PV;
-  constexpr int PD = NRD < RM ? NRD : RM;
+  constexpr int PD = NRD < NMF ? NRD : NMF;
+  constexpr int RM = NMF - PD;
+  constexpr int PV = NV < RM ? NV : RM;
   auto interleave_moves = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int r = 0; r < PV; ++r) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // one MFMA
-      __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);     // one global -> LDS move
-    }
-    if (NV > PV) __builtin_amdgcn_sched_group_barrier(0x010, NV - PV, 0);
-#pragma unroll
     for (int r = 0; r < PD; ++r) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // one MFMA
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);     // one DS read
     }
     if (NRD > PD) __builtin_amdgcn_sched_group_barrier(0x100, NRD - PD, 0);
-    if (RM > PD) __builtin_amdgcn_sched_group_barrier(0x008, RM - PD, 0);
+#pragma unroll
+    for (int r = 0; r < PV; ++r) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);     // one global -> LDS move
+    }
+    if (NV > PV) __builtin_amdgcn_sched_group_barrier(0x010, NV - PV, 0);
+    if (RM > PV) __builtin_amdgcn_sched_group_barrier(0x008, RM - PV, 0);
   };
 
   // Prologue: the bias load, slab 0, then iterations -L .. -1 (weights of stage u = i + L,
@@ -1475,8 +1477,9 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_slab_kernel(ConvParams
   load_frags(IC<0>{}, a0, b0, 0, 0, 0);
   int wbuf = 0, sbuf = 0;
   // Iteration s: second phase's fragments of stage s, first-phase MFMAs; wait for the own
-  // moves of stage s + 1; barrier: stage s + 1 published, stage s - 1 retired; the moves of
-  // iteration s; first phase's fragments of stage s + 1 during the second-phase MFMAs.
+  // moves of stage s + 1; barrier: stage s + 1 published, stage s - 1 retired; first
+  // phase's fragments of stage s + 1 and the moves of iteration s during the second-phase
+  // MFMAs.
   auto step = [&](auto i_c, auto steady_c, int s) __attribute__((always_inline)) {
     constexpr int IV = decltype(i_c)::value;
     constexpr int NXT = IV == INNER - 1 ? 0 : IV + 1;
@@ -1492,6 +1495,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_slab_kernel(ConvParams
     wbuf = wbuf == NS - 1 ? 0 : wbuf + 1;
     if (IV == INNER - 1) sbuf = sbuf == NSL - 1 ? 0 : sbuf + 1;
     if constexpr (decltype(steady_c)::value) {
+      load_frags(IC<NXT>{}, a0, b0, wbuf, sbuf, 0);
       // the weights of stage s + L and the slab blocks both exist
       issue_w();
       issue_s(IC<(IV + L) % INNER>{});
@@ -1499,8 +1503,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_slab_kernel(ConvParams
       if (s + L < KS) issue_w();
       if ((s + L) / INNER + 1 < NG) issue_s(IC<(IV + L) % INNER>{});
       __builtin_amdgcn_sched_barrier(0);
+      load_frags(IC<NXT>{}, a0, b0, wbuf, sbuf, 0);
     }
-    load_frags(IC<NXT>{}, a0, b0, wbuf, sbuf, 0);
     mfmas(a1, b1);
     if constexpr (decltype(steady_c)::value)
       interleave_moves();
