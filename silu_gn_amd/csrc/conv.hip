@@ -229,7 +229,7 @@ struct Sums {
   double s, q;
 };
 
-template <int MODE, int TN, int TM, int WTM, int WTN>
+template <int MODE, int TN, int TM, int WTM, int WTN, bool SC>
 __device__ __forceinline__ Sums store_tile_staged(const f32x16 (&acc)[TN][TM], const ConvParams& p, int n,
                                                   int t, int pos0, int kbase, int wm, int lane,
                                                   int phase, const float* lbias, char* stage) {
@@ -267,7 +267,7 @@ __device__ __forceinline__ Sums store_tile_staged(const f32x16 (&acc)[TN][TM], c
   // o = (a 2 + pa) 2 + pb, a = (t + first (ft - 1)) % ft and rep = K F / Cs. The host admits
   // Cs = K (source channel c) and Cs = 2K (source channel 2c + o / rep): a lane's 8 output
   // channels read 16 or 32 contiguous source bytes. Uniform per tile.
-  const bool shortcut = MODE == kPhase && p.sc != nullptr;
+  const bool shortcut = MODE == kPhase && SC && p.sc != nullptr;
   Rsrc scs = make_rsrc(p.y, 0);
   int sc_step = 1, sc_e = 0;
   if (shortcut) {
@@ -297,6 +297,16 @@ __device__ __forceinline__ Sums store_tile_staged(const f32x16 (&acc)[TN][TM], c
       }
   }
   stage_barrier();                                   // every wave is done with the operand stages
+  // The biases of this lane's 8 channels, read once: the staging writes below could alias
+  // the bias area as far as the compiler knows, so a bias read per staged fragment would
+  // wait for its data before each write.
+  float bsv[8];
+  {
+    const float4 b0 = *reinterpret_cast<const float4*>(lbias + 8 * g);
+    const float4 b1 = *reinterpret_cast<const float4*>(lbias + 8 * g + 4);
+    bsv[0] = b0.x, bsv[1] = b0.y, bsv[2] = b0.z, bsv[3] = b0.w;
+    bsv[4] = b1.x, bsv[5] = b1.y, bsv[6] = b1.z, bsv[7] = b1.w;
+  }
 #pragma unroll
   for (int j = 0; j < TM; ++j) {
     // Shortcut rows of this fragment row block, issued before its staging writes.
@@ -317,22 +327,31 @@ __device__ __forceinline__ Sums store_tile_staged(const f32x16 (&acc)[TN][TM], c
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int kr = i * 32 + 8 * q + 4 * (lane >> 5);
-          const float4 b = *reinterpret_cast<const float4*>(lbias + kr);
           float4 v;
-          v.x = acc[i][j][4 * q + 0] + b.x;
-          v.y = acc[i][j][4 * q + 1] + b.y;
-          v.z = acc[i][j][4 * q + 2] + b.z;
-          v.w = acc[i][j][4 * q + 3] + b.w;
+          v.x = acc[i][j][4 * q + 0];
+          v.y = acc[i][j][4 * q + 1];
+          v.z = acc[i][j][4 * q + 2];
+          v.w = acc[i][j][4 * q + 3];
           *reinterpret_cast<float4*>(stage + r * ROW + (((kr >> 2) ^ (r & SWZ)) << 4)) = v;
         }
     }
     wait_lgkm0();                                    // this wave's rows are in its area
+    // All of the block's staged rows are read before the first store: one LDS round trip
+    // per block instead of one per row group.
+    float4 lov[NI], hiv[NI];
 #pragma unroll
     for (int it = 0; it < NI; ++it) {
       const int r = it * RPI + lane / LPR;
-      const float4 lo = *reinterpret_cast<const float4*>(stage + r * ROW + (((2 * g) ^ (r & SWZ)) << 4));
-      const float4 hi = *reinterpret_cast<const float4*>(stage + r * ROW + (((2 * g + 1) ^ (r & SWZ)) << 4));
+      lov[it] = *reinterpret_cast<const float4*>(stage + r * ROW + (((2 * g) ^ (r & SWZ)) << 4));
+      hiv[it] = *reinterpret_cast<const float4*>(stage + r * ROW + (((2 * g + 1) ^ (r & SWZ)) << 4));
+    }
+#pragma unroll
+    for (int it = 0; it < NI; ++it) {
+      const int r = it * RPI + lane / LPR;
+      const float4 lo = lov[it], hi = hiv[it];
       float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] += bsv[e];    // acc + bias, as before the residual
       if (MODE == kCausal && p.res) {
         const u32x4 rr = rv[MODE == kCausal ? j : 0][MODE == kCausal ? it : 0];
 #pragma unroll
@@ -508,6 +527,14 @@ __device__ __forceinline__ void store_tile_rms(const f32x16 (&acc)[TN][TM], cons
 #pragma unroll
   for (int q = 0; q < (WTN + 63) / 64; ++q)
     if (q * 64 + lane < WTN) lgain[q * 64 + lane] = gload[q];
+  // this lane's 8 biases, read once (as in store_tile_staged)
+  float bsv[8];
+  {
+    const float4 b0 = *reinterpret_cast<const float4*>(lbias + 8 * g);
+    const float4 b1 = *reinterpret_cast<const float4*>(lbias + 8 * g + 4);
+    bsv[0] = b0.x, bsv[1] = b0.y, bsv[2] = b0.z, bsv[3] = b0.w;
+    bsv[4] = b1.x, bsv[5] = b1.y, bsv[6] = b1.z, bsv[7] = b1.w;
+  }
 #pragma unroll
   for (int j = 0; j < TM; ++j) {
     {
@@ -517,12 +544,11 @@ __device__ __forceinline__ void store_tile_rms(const f32x16 (&acc)[TN][TM], cons
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int kr = i * 32 + 8 * q + 4 * (lane >> 5);
-          const float4 b = *reinterpret_cast<const float4*>(lbias + kr);
           float4 v;
-          v.x = acc[i][j][4 * q + 0] + b.x;
-          v.y = acc[i][j][4 * q + 1] + b.y;
-          v.z = acc[i][j][4 * q + 2] + b.z;
-          v.w = acc[i][j][4 * q + 3] + b.w;
+          v.x = acc[i][j][4 * q + 0];
+          v.y = acc[i][j][4 * q + 1];
+          v.z = acc[i][j][4 * q + 2];
+          v.w = acc[i][j][4 * q + 3];
           *reinterpret_cast<float4*>(stage + r * ROW + (((kr >> 2) ^ (r & SWZ)) << 4)) = v;
         }
     }
@@ -544,6 +570,8 @@ __device__ __forceinline__ void store_tile_rms(const f32x16 (&acc)[TN][TM], cons
       const float4 lo = *reinterpret_cast<const float4*>(stage + r * ROW + (((2 * g) ^ (r & SWZ)) << 4));
       const float4 hi = *reinterpret_cast<const float4*>(stage + r * ROW + (((2 * g + 1) ^ (r & SWZ)) << 4));
       float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] += bsv[e];    // acc + bias, as before the residual
       if (p.res) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -1083,7 +1111,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_kernel(ConvParams p) {
                                        ntile * BN + wn * WTN, wm, lane, phase, lbias + wn * WTN);
   } else if (K % 8 == 0) {                           // rows of y 16-byte aligned
     static_assert(NW * 32 * WTN * 4 + NW * 64 * 16 <= NS * STAGE, "epilogue staging fits the stages");
-    const Sums sums = store_tile_staged<MODE, TN, TM, WTM, WTN>(
+    const Sums sums = store_tile_staged<MODE, TN, TM, WTM, WTN, true>(
         acc, p, n, t, mt * BM, ntile * BN + wn * WTN, wm, lane, phase, lbias + wn * WTN,
         smem + wave * (32 * WTN * 4));
     if (MODE == kCausal && p.nws)
@@ -1185,9 +1213,10 @@ __device__ __forceinline__ void wait_vm_n(int n) {
   }
 }
 
-// RMS: the instantiation that can apply the next RMS norm in its epilogue (a separate one,
-// so that the plain convolution keeps its spill-free register allocation).
-template <int BM, int BN, int WGM, int WGN, int NS, int MODE, bool RMS = false>
+// EPI: the instantiation with the epilogue's extra work -- the next RMS norm (causal) or the
+// DupUp3D shortcut (phases). A separate one, so that the plain convolution keeps its
+// spill-free register allocation and its stores need no wait for the extra loads.
+template <int BM, int BN, int WGM, int WGN, int NS, int MODE, bool EPI = false>
 __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_slab_kernel(ConvParams p) {
   static_assert(MODE == kCausal || MODE == kPhase || MODE == kTime || MODE == kWino, "slab modes");
   constexpr bool TEMPORAL = MODE == kTime || MODE == kWino;   // 3 frame taps, one row, no column taps
@@ -1537,7 +1566,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_slab_kernel(ConvParams
   // The next RMS norm in the epilogue (LDS: the waves' staging areas, the row sums, then
   // each wave's parked outputs, NI x 64 lanes x 16 bytes).
   bool rms_done = false;
-  if constexpr (MODE == kCausal && RMS) {
+  if constexpr (MODE == kCausal && EPI) {
     if (p.act) {
       constexpr int RSUM = NW * 32 * WTN * 4, PARK = RSUM + 2 * NW * 32 * 8;
       constexpr int NIP = 32 / (64 / (WTN / 8));
@@ -1555,16 +1584,17 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_slab_kernel(ConvParams
   } else if constexpr (MODE == kWino) {
     store_tile_f32<TN, TM, WTM, WTN>(acc, p, n, t, pos0, ntile * BN + wn * WTN, wm, lane,
                                      smem + wave * (32 * WTN * 4));
-  } else if (K % 8 == 0) {                           // rows of y 16-byte aligned
-    const Sums sums = store_tile_staged<MODE, TN, TM, WTM, WTN>(
+  } else {
+    // K % 8 == 0 (the host takes this kernel only then): rows of y are 16-byte aligned. With
+    // the staged epilogue as the only one, the accumulators reach LDS straight from the
+    // accumulator registers; a second epilogue that adds to them in vector registers would
+    // make the compiler copy all of them out of the accumulator file and spill.
+    const Sums sums = store_tile_staged<MODE, TN, TM, WTM, WTN, MODE == kPhase && EPI>(
         acc, p, n, t, pos0, ntile * BN + wn * WTN, wm, lane, phase, lb, smem + wave * (32 * WTN * 4));
     static_assert(NW * 32 * WTN * 4 + NW * 64 * 16 <= SLABS + NSL * SLAB, "statistics area");
     if (MODE == kCausal && p.nws)
       next_stats_partials<NW, WGM, WTN, BN>(p, n, t, mt, ntile, wave, lane, sums,
                                             reinterpret_cast<double*>(smem + NW * 32 * WTN * 4));
-  } else if constexpr (MODE != kTime && MODE != kWino) {   // the temporal x2 needs K % 16 == 0
-    store_tile<MODE, TN, TM, WTM, WTN>(acc, p, n, (int64_t)t * HW + pos0, (int64_t)(t + 1) * HW,
-                                       ntile * BN + wn * WTN, wm, lane, phase, lb);
   }
 }
 
@@ -2018,6 +2048,7 @@ struct TileCfg {
   int lds;
   int threads;
   bool rms_epilogue;   // the kernel applies the next RMS norm in its epilogue when p.act is set
+  bool shortcut;       // a phase kernel adds the DupUp3D shortcut when p.sc is set
   bool slab;           // conv_slab_kernel (else conv_kernel)
 };
 
@@ -2030,19 +2061,21 @@ static TileCfg make_cfg(int c) {
   t.lds = NS * (BM + BN) * kPK * 2 + (FUSE ? c * 16 : 0) + BN * 4;
   t.threads = 64 * WGM * WGN;
   t.rms_epilogue = false;
+  t.shortcut = true;
   t.slab = false;
   return t;
 }
 
-template <int BM, int BN, int WGM, int WGN, int MODE, bool RMS = false>
+template <int BM, int BN, int WGM, int WGN, int MODE, bool EPI = false>
 static TileCfg make_slab_cfg() {
   TileCfg t;
   t.bm = BM;
   t.bn = BN;
-  t.fn = conv_slab_kernel<BM, BN, WGM, WGN, kSlabStages, MODE, RMS>;
+  t.fn = conv_slab_kernel<BM, BN, WGM, WGN, kSlabStages, MODE, EPI>;
   t.lds = slab_lds_bytes<BM, BN, kSlabStages, MODE>();
   t.threads = 64 * WGM * WGN;
-  t.rms_epilogue = MODE == kCausal && RMS;
+  t.rms_epilogue = MODE == kCausal && EPI;
+  t.shortcut = MODE != kPhase || EPI;
   t.slab = true;
   return t;
 }
@@ -2089,7 +2122,15 @@ template <int MODE, bool FUSE>
 static TileCfg choose_tile(int64_t hw, int64_t frames, int k, int c, int64_t groups_of_tiles) {
   const int bn = k > 128 ? 256 : k > 64 ? 128 : k > 32 ? 64 : 32;
   TileCfg cand[4];
-  const int nc = candidates<MODE, FUSE>(bn, c, cand);
+  int nc = candidates<MODE, FUSE>(bn, c, cand);
+  if constexpr ((MODE == kCausal || MODE == kPhase) && !FUSE) {
+    // the slab kernel has only the staged epilogue (16-byte rows of y): K % 8 != 0 takes
+    // the generic tile
+    if (bn == 256 && k % 8 != 0) {
+      cand[0] = make_cfg<256, 256, 2, 4, kStages, MODE, FUSE>(c);
+      nc = 1;
+    }
+  }
   TileCfg best = cand[0];
   double best_cost = 1e300;
   for (int i = 0; i < nc; ++i) {
@@ -2596,7 +2637,13 @@ static int upsample_impl(const char* fn, const uint16_t* x, sgn_dims d, const ui
   p.C = (int)d.c;
   p.K = k;
   p.mper = d.t * d.h * d.w;
-  const TileCfg cfg = choose_tile<kPhase, false>(d.h * d.w, d.t, k, p.C, d.n * 4);
+  TileCfg cfg = choose_tile<kPhase, false>(d.h * d.w, d.t, k, p.C, d.n * 4);
+  if (sc && cfg.slab)   // the same tile, in its instantiation with the shortcut epilogue
+    cfg = cfg.bm == 256 ? make_slab_cfg<256, 256, 2, 2, kPhase, true>() : make_slab_cfg<224, 256, 1, 4, kPhase, true>();
+  if (sc && !cfg.shortcut) {
+    set_error("%s: internal: the chosen tile cannot add the shortcut", fn);
+    return SGN_EINVAL;
+  }
   if (!launch_conv(cfg, p, d.n, 4, stream, fn)) return SGN_ELAUNCH;
   return SGN_OK;
 }
