@@ -1617,10 +1617,12 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_slab_kernel(ConvParams
 //   r - 1. Its 50 input columns w0 - 1 .. w0 + 48 (64-byte rows) move global -> LDS with
 //   buffer_load ... lds into the wave's own ring of 3 units, two units ahead; each wave waits
 //   only for its own moves (counted vmcnt), so the ring needs no barrier.
-// - The kernel is bound by these moves, not by the matrix pipe: with every MFMA removed it
-//   runs as long. Two output rows per workgroup stage 4 input rows per frame for 2 output
-//   rows, where one row per workgroup staged 3 for each; the moves per output pixel drop by
-//   about a third. (The accumulators of 2 rows fit the register file with 3 segments.)
+// - The matrix work and the moves overlap (together they take only a little more cycles
+//   than either alone), but together they draw enough power that the board lowers the
+//   clock: energy per output is what bounds the kernel. Two output rows per workgroup stage
+//   4 input rows per frame for 2 output rows, where one row per workgroup staged 3 for
+//   each; the moves per output pixel drop by about a third. (The accumulators of 2 rows fit
+//   the register file with 3 segments.)
 // - The loop over a group of 3 frames (12 units) is unrolled so that a unit's ring slot, row
 //   taps and accumulator slots are constants, every LDS read is a per-lane base (one per
 //   column tap) plus an immediate, and the frame descriptors are built once per group.
