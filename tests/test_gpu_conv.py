@@ -44,6 +44,11 @@ def _gn_params(c, seed):
     (1, 2, 3, 4, 4096, 64, True, True, False),       # the largest C: cache rows of 512 packets
     (2, 1, 3, 4, 4096, 128, False, False, True),     # ... without a cache (zeros), two samples
     (1, 2, 3, 5, 64, 4096, True, True, True),        # the largest K: 16 N tiles
+    (1, 2, 1, 1, 64, 256, True, True, True),         # a single pixel (slab kernel): 26 of 27 taps padding
+    (1, 3, 1, 9, 128, 256, True, False, True),       # one row: the row taps above and below read zeros
+    (1, 2, 7, 1, 64, 256, True, True, False),        # one column: every output at both row edges
+    (1, 1, 1, 1, 64, 64, False, True, False),        # a single pixel, K <= 128, no cache
+    (2, 1, 1, 5, 64, 128, False, False, True),       # one row, T = 1 without a cache, two samples
 ])
 def test_conv_small(n, t, h, w, c, k, cache, bias, res):
     print("case", (n, t, h, w, c, k, cache, bias, res), flush=True)
@@ -77,6 +82,8 @@ def _fused_case(shape, k, groups, seed, cache=True):
     ((2, 1, 7, 9, 256), 32, 32),
     ((1, 3, 5, 37, 1024), 256, 32),
     ((1, 2, 3, 4, 2048), 64, 32),                   # the largest C the fused load takes
+    ((1, 2, 1, 1, 64), 64, 32),                     # a single pixel
+    ((1, 3, 1, 7, 128), 256, 16),                   # one row, K = 256
 ])
 def test_fused_equals_apply_then_conv_and_oracle(shape, k, groups):
     print("case fused", shape, k, groups, flush=True)

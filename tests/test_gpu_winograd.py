@@ -70,6 +70,8 @@ def _split_ws(ws, n, t, h, w, c, k):
     (2, 2, 7, 9, 128, 264, True, True, True),       # ragged tiles, two N tiles (the second ragged)
     (1, 1, 5, 6, 64, 192, False, True, False),      # T = 1, zero cache, K = 192
     (1, 4, 17, 30, 256, 256, True, True, True),     # several tile rows, ragged
+    (1, 2, 1, 1, 64, 256, True, True, True),        # a single pixel: one tile, 15 of its 16 outputs past the frame
+    (2, 1, 3, 2, 128, 256, False, True, True),      # less than one tile, T = 1 without a cache
 ])
 def test_winograd_small(n, t, h, w, c, k, cache, bias, res):
     print("case winograd", (n, t, h, w, c, k, cache, bias, res), flush=True)
@@ -101,7 +103,11 @@ def test_winograd_small(n, t, h, w, c, k, cache, bias, res):
     # the products (fp32 on the GPU, fp64 here from the same bf16 operands)
     mg = m_gpu.cpu().double().numpy().reshape(m.shape)
     scale = np.sqrt(np.mean(m ** 2, axis=(2, 3, 4, 5, 6)))                  # per component
-    err = np.sqrt(np.mean((mg - m) ** 2, axis=(2, 3, 4, 5, 6))) / scale
+    # a component that is exactly zero (inputs all padding, e.g. the first row and column
+    # of a one-pixel frame's transform) must be zero on the GPU too
+    zero = scale == 0
+    assert np.all(mg[zero] == 0)
+    err = np.sqrt(np.mean((mg - m) ** 2, axis=(2, 3, 4, 5, 6))) / np.where(zero, 1.0, scale)
     print("  M: worst component rel rms %.3e at %s" % (err.max(), np.unravel_index(err.argmax(), err.shape)),
           flush=True)
     if err.max() > 1e-5:
