@@ -190,7 +190,9 @@ def up_block_extras(wl, dev, iters):
     latent: time_upsample_conv (3x1x1 causal conv C -> 2C, halves to frames, steady-state
     pass with a cache); upsample: the phases with the DupUp3D shortcut of a block input of
     x's shape (ft = 1) against the phases alone; full-resolution block: the conv with the
-    RMS norm of its output in the epilogue against the conv followed by rms_silu."""
+    RMS norm of its output in the epilogue against the conv followed by rms_silu, the conv
+    with the RMS norm of its input in the operand load against rms_silu followed by the conv,
+    and the conv through Winograd against the direct conv."""
     if wl.kind == "latent":
         x = wl.x(dev)
         wt = sg.normal((2 * wl.c, 3, wl.c), wl.seed, sg.W_TIME, std=1 / math.sqrt(3 * wl.c), device=dev)
@@ -230,6 +232,22 @@ def up_block_extras(wl, dev, iters):
         epi = time_loop(lambda: sga.causal_conv3d_rms(x, w, gain, 1e-6, act=act, store_y=False), iters)
         out = {"conv_rms_epilogue": {"ms": round(epi, 4), "ms_separate": round(sep, 4),
                                      "form": "causal_conv3d_rms, y not stored (vs causal_conv3d + rms_silu)"}}
+        # the RMS norm of the conv's input in its operand load: rms_silu_rstd, then
+        # causal_conv3d_rms_input, against rms_silu, then causal_conv3d
+        rstd = torch.empty(tuple(x.shape[:4]), dtype=torch.float64, device=dev)
+
+        def separate_in():
+            sga.rms_silu(x, gain, 1e-6, y=act)
+            sga.causal_conv3d(act, w, y=y)
+
+        def operand_load():
+            sga.rms_silu_rstd(x, 1e-6, rstd=rstd)
+            sga.causal_conv3d_rms_input(x, w, rstd, gain, y=y)
+        sep_in = time_loop(separate_in, iters)
+        ol = time_loop(operand_load, iters)
+        out["conv_rms_operand_load"] = {"ms": round(ol, 4), "ms_separate": round(sep_in, 4),
+                                        "form": "rms_silu_rstd + causal_conv3d_rms_input (vs rms_silu + causal_conv3d)"}
+        del rstd
         # the same conv through Winograd F(4x4,3x3) (input transform, 36 component products,
         # output transform) against the direct conv, both on the GroupNorm+SiLU output of x
         st = sga.gn_silu_stats(x, wl.groups)

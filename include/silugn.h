@@ -142,6 +142,20 @@ int rms_silu(const uint16_t* x, sgn_dims d, const float* gain, float eps, uint16
              hipStream_t stream);
 
 /*
+ * rms_silu_rstd -- the per-position factor of rms_silu: rstd[p] = 1 / sqrt(mean_c x[p,:]^2
+ * + eps) in fp64, bitwise the value rms_silu applies (the same kernel and launch, which
+ * writes rstd instead of y). It is what a convolution needs to apply the RMS norm in its
+ * operand load (causal_conv3d_rms_input): the norm has no statistics across positions, so
+ * this one fp64 per position is all that has to be formed before the convolution.
+ * Defined by: binding.cpp page, the comment above Decoder::output_head (the decoder's RMS
+ * norm + SiLU, norm_pad); the formula is rms_silu's.
+ *   x     bf16 (N,T,H,W,C), 16-byte aligned; C % 64 == 0, C <= 4096 (else SGN_EINVAL)
+ *   rstd  device fp64 [N][T][H][W], 8-byte aligned, written; must not overlap x (SGN_EALIAS)
+ *   eps   > 0, used as its exact fp64 value
+ */
+int rms_silu_rstd(const uint16_t* x, sgn_dims d, float eps, double* rstd, hipStream_t stream);
+
+/*
  * causal_conv3d -- causal 3x3x3 convolution with a 2-frame temporal cache.
  * Defined by: FastVideo wan22_vae_decode binding.cpp page, Decoder::conv (front
  * temporal padding of kt-1 = 2 frames taken from the per-conv cache, spatial
@@ -191,6 +205,31 @@ int causal_conv3d_rms(const uint16_t* x, sgn_dims d, const uint16_t* cache_in,
                       const uint16_t* w, int k, const float* bias, const uint16_t* residual,
                       const sgn_gn* fuse, const float* gain, float eps, uint16_t* y,
                       uint16_t* act, uint16_t* cache_out, hipStream_t stream);
+
+/*
+ * causal_conv3d_rms_input -- causal_conv3d of the decoder's RMS norm + SiLU of x, the norm
+ * applied in the convolution's operand load (the consumer side; causal_conv3d_rms is the
+ * producer side).
+ * Defined by: binding.cpp page, the comment above Decoder::output_head and Decoder::conv's
+ * norm_pad(x, gain, cache, ...) (normalise, activate and pad the convolution's input); the
+ * norm is rms_silu's.
+ *
+ *   a = rms_silu(x, gain, eps)   with rstd = rms_silu_rstd(x, eps) passed in
+ *   y = causal_conv3d(a, cache_in, w, k, bias, residual)
+ * Bitwise equal to rms_silu followed by causal_conv3d (fuse == NULL): the rows of x are
+ * activated with rms_silu's arithmetic as they are loaded, and the accumulation order is
+ * the unfused convolution's. cache_out (if not NULL) = the last 2 frames of cat(cache_in,
+ * a), i.e. activated; cache_in holds activated frames.
+ *   rstd  device fp64 [N][T][H][W] from rms_silu_rstd on the same x and eps (8-byte aligned)
+ *   gain  device fp32 [C] (4-byte aligned)
+ * Other arguments and errors as causal_conv3d; C <= 2048 (else SGN_EINVAL); y and
+ * cache_out must not overlap rstd or gain (SGN_EALIAS). It runs the per-tap kernel
+ * (sgn_conv_plan with fused != 0 names its tile), which activates each row once per tap.
+ */
+int causal_conv3d_rms_input(const uint16_t* x, sgn_dims d, const uint16_t* cache_in,
+                            const uint16_t* w, int k, const float* bias, const uint16_t* residual,
+                            const double* rstd, const float* gain, uint16_t* y,
+                            uint16_t* cache_out, hipStream_t stream);
 
 /*
  * causal_conv3d_eligible -- 1 if causal_conv3d takes input dims d and K = k output

@@ -29,3 +29,10 @@ def rms_silu(x, gain, eps: float):
     ms = np.mean(x * x, axis=-1, keepdims=True)          # mean of squares over the channels
     z = x * g / np.sqrt(ms + eps)
     return silu(z)
+
+
+def rms_rstd(x, eps: float):
+    """float64 1 / sqrt(mean_c(x^2) + eps) per position (the factor rms_silu applies with the
+    gain): shape x.shape[:-1]. x holds exact bf16 values (any float dtype)."""
+    x = np.asarray(x, dtype=np.float64)
+    return 1.0 / np.sqrt(np.mean(x * x, axis=-1) + eps)

@@ -45,8 +45,8 @@ class sgn_plan(ctypes.Structure):
 SGN_OP_CAUSAL, SGN_OP_PHASES, SGN_OP_TIME = 0, 1, 2
 SGN_KERNELS = {1: "slab", 2: "generic"}
 
-EXPORTS = ["sgn_last_error", "gn_silu_eligible", "causal_conv3d_eligible", "sgn_conv_plan", "gn_silu_stats_workspace", "gn_silu_stats", "gn_silu_stats_noalloc", "gn_silu_apply", "rms_silu",
-           "causal_conv3d", "causal_conv3d_rms", "causal_conv3d_next_stats_workspace", "causal_conv3d_next_stats",
+EXPORTS = ["sgn_last_error", "gn_silu_eligible", "causal_conv3d_eligible", "sgn_conv_plan", "gn_silu_stats_workspace", "gn_silu_stats", "gn_silu_stats_noalloc", "gn_silu_apply", "rms_silu", "rms_silu_rstd",
+           "causal_conv3d", "causal_conv3d_rms", "causal_conv3d_rms_input", "causal_conv3d_next_stats_workspace", "causal_conv3d_next_stats",
            "winograd_prepare_weights", "causal_conv3d_winograd_workspace", "causal_conv3d_winograd",
            "upsample2x_prepare_weights", "upsample2x_conv_phases", "upsample2x_conv_phases_shortcut",
            "time_upsample_conv", "head_conv_d2s"]
@@ -74,8 +74,10 @@ def load_library(path: str = LIB_PATH):
         "gn_silu_stats_noalloc": (i32, [vp, sgn_dims, i32, vp, vp]),
         "gn_silu_apply": (i32, [vp, sgn_dims, i32, vp, vp, vp, f32, vp, vp]),
         "rms_silu": (i32, [vp, sgn_dims, vp, f32, vp, vp]),
+        "rms_silu_rstd": (i32, [vp, sgn_dims, f32, vp, vp]),
         "causal_conv3d": (i32, [vp, sgn_dims, vp, vp, i32, vp, vp, gnp, vp, vp, vp]),
         "causal_conv3d_rms": (i32, [vp, sgn_dims, vp, vp, i32, vp, vp, gnp, vp, f32, vp, vp, vp, vp]),
+        "causal_conv3d_rms_input": (i32, [vp, sgn_dims, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp]),
         "causal_conv3d_next_stats_workspace": (sz, [sgn_dims, i32, i32]),
         "causal_conv3d_next_stats": (i32, [vp, sgn_dims, vp, vp, i32, vp, vp, gnp, vp, vp, i32, vp, vp,
                                            sz, vp]),
@@ -242,6 +244,17 @@ def rms_silu(x, gain, eps: float, y=None):
     return y
 
 
+def rms_silu_rstd(x, eps: float, rstd=None):
+    """fp64 [N, T, H, W]: each position's 1 / sqrt(mean_c x^2 + eps), the factor rms_silu applies."""
+    lib = load_library()
+    _act(x)
+    if rstd is None:
+        rstd = torch.empty(tuple(x.shape[:4]), dtype=torch.float64, device=x.device)
+    _arg(rstd, "rstd", torch.float64, tuple(x.shape[:4]), x.device)
+    _check(lib.rms_silu_rstd(_ptr(x), _dims(x), float(eps), _ptr(rstd), _stream(x)))
+    return rstd
+
+
 def _conv_args(x, w, cache_in, bias, residual, y, cache_out, k=None):
     """Checks shared by the causal convolutions; returns (K, y)."""
     _act(x)
@@ -288,6 +301,20 @@ def causal_conv3d_rms(x, w, gain, eps: float, cache_in=None, bias=None, residual
     _check(lib.causal_conv3d_rms(_ptr(x), _dims(x), _ptr(cache_in), _ptr(w), k, _ptr(bias), _ptr(residual), gp,
                                  _ptr(gain), float(eps), _ptr(y), _ptr(act), _ptr(cache_out), _stream(x)))
     return y, act
+
+
+def causal_conv3d_rms_input(x, w, rstd, gain, cache_in=None, bias=None, residual=None, y=None, cache_out=None):
+    """causal_conv3d of rms_silu(x, gain) with the norm applied as the rows of x load; ``rstd`` from
+    rms_silu_rstd(x, eps). Returns y; ``cache_out`` (if given) receives the activated last 2 frames."""
+    lib = load_library()
+    k = _conv_args(x, w, cache_in, bias, residual, y, cache_out)
+    _arg(rstd, "rstd", torch.float64, tuple(x.shape[:4]), x.device)
+    _arg(gain, "gain", torch.float32, (x.shape[4],), x.device)
+    if y is None:
+        y = torch.empty(x.shape[:4] + (k,), dtype=torch.bfloat16, device=x.device)
+    _check(lib.causal_conv3d_rms_input(_ptr(x), _dims(x), _ptr(cache_in), _ptr(w), k, _ptr(bias), _ptr(residual),
+                                       _ptr(rstd), _ptr(gain), _ptr(y), _ptr(cache_out), _stream(x)))
+    return y
 
 
 def causal_conv3d_next_stats_workspace(dims, k: int, next_groups: int) -> int:

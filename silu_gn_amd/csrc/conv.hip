@@ -12,7 +12,8 @@
 // (conv_kernel below describes the pipeline). With GroupNorm fused, position rows go
 // through VGPRs instead of straight to LDS: loaded, activated by the same
 // activate_packet() as gn_silu_apply (so the result is bitwise that of
-// apply-then-convolve), and written to the same swizzled slots.
+// apply-then-convolve), and written to the same swizzled slots; the decoder's RMS norm is
+// applied the same way from a per-position rstd (rms_silu's arithmetic).
 //
 // Pages: FastVideo wan22_vae_decode binding.cpp -- Decoder::conv (causal front padding
 // of kt-1 frames from the cache, 1-pixel spatial zero padding, the cache keeps the last
@@ -20,8 +21,9 @@
 // Decoder::up (the four 2x2 phase convolutions of nearest-x2 + 3x3, interleaved with the
 // bias), Decoder::output_head (the head convolution to 12 = 3 x 2 x 2 channels, bias,
 // clamp) and decode_video's write of the 2x2-unfolded RGB video; Decoder::up_block (the
-// temporal x2 after the resnets, the DupUp3D shortcut in the resampler's last pass) and
-// Decoder's `prepared` edge (the next norm applied by the producing convolution).
+// temporal x2 after the resnets, the DupUp3D shortcut in the resampler's last pass),
+// Decoder's `prepared` edge (the next norm applied by the producing convolution) and
+// norm_pad (the RMS norm + SiLU of a convolution's input).
 #include <math.h>
 #include <stdio.h>
 
@@ -85,7 +87,14 @@ struct ConvParams {
   // go to yf (N x T frames of H x W positions -- the tiles -- by K channels).
   int wino_n;
   float* yf;
+  // The RMS norm + SiLU applied in the operand load (conv_kernel with FUSE == kFuseRms):
+  // rstd[n][t][h][w] of x (fp64, as rms_silu forms it), the gain in gamma.
+  const double* rstd;
 };
+
+// What conv_kernel applies to x while loading it: nothing, silu(group_norm(x)) or
+// silu(rms_norm(x)).
+enum Fuse { kFuseNone = 0, kFuseGn = 1, kFuseRms = 2 };
 
 
 constexpr int kRsrcFlags = 0x00020000;   // descriptor dword 3 (gfx9 raw buffer, 32-bit data)
@@ -697,12 +706,12 @@ struct BiasStage {
 
 // cache_out = the last 2 frames of P = cat(cache_in, a), a = frames x0 .. x0 + T - 1 of the
 // Tx frames per sample of x; frames of x are activated when fused (same per-thread column
-// layout and activate_packet as gn_silu_apply). A row of cp packets is covered by
+// layout and activate_packet as gn_silu_apply; with rstd, rms_silu's per-position affine). A row of cp packets is covered by
 // tpr = min(cp, 256) threads, each taking every tpr-th packet; rstep rows per block pass.
 __global__ __launch_bounds__(256) void cache_out_kernel(
     const uint4* x, const uint4* cache_in, uint4* cache_out, int T, int Tx, int x0, int64_t hw, int cp,
     int rstep, int64_t rows_per_block, const double* stats, const float* gamma, const float* beta,
-    double eps, int groups) {
+    double eps, int groups, const double* rstd) {
   const int tid = threadIdx.x, n = blockIdx.y;
   const int tpr = cp < 256 ? cp : 256;
   if (tid >= rstep * tpr) return;
@@ -725,7 +734,18 @@ __global__ __launch_bounds__(256) void cache_out_kernel(
       uint4 v;
       if (pf >= 2) {
         v = x[(((int64_t)n * Tx + x0 + pf - 2) * hw + s) * cp + col];
-        if (stats) v = activate_packet(v, a);
+        if (stats) {
+          v = activate_packet(v, a);
+        } else if (rstd) {                           // the RMS norm: gain (in gamma) * rstd
+          const double r = rstd[((int64_t)n * Tx + x0 + pf - 2) * hw + s];
+          Affine ar[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            ar[i].s = (double)gamma[col * 8 + i] * r;
+            ar[i].b = 0.0;
+          }
+          v = activate_packet(v, ar);
+        }
       } else if (cache_in) {
         v = cache_in[(((int64_t)n * 2 + pf) * hw + s) * cp + col];
       } else {
@@ -790,8 +810,9 @@ __device__ __forceinline__ uint4 load16(Rsrc r, uint32_t voff, uint32_t soff) {
 }
 
 
-template <int BM, int BN, int WGM, int WGN, int NS, int MODE, bool FUSE>
+template <int BM, int BN, int WGM, int WGN, int NS, int MODE, int FUSE>
 __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_kernel(ConvParams p) {
+  constexpr bool RMS = FUSE == kFuseRms;
   constexpr int NW = WGM * WGN;
   constexpr int TAPS = MODE == kPhase ? 4 : MODE == kTime ? 3 : 27;
   constexpr int INNER = MODE == kCausal || MODE == kHead ? 3 : 1;   // taps sharing a channel chunk in a row
@@ -852,6 +873,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_kernel(ConvParams p) {
   // Position rows this lane moves: byte offset in the frame, and which row / column
   // neighbours exist.
   uint32_t pvo[IBW];
+  int ppos[RMS ? IBW : 1];                           // RMS: the row's position in the frame
   bool wl[IBW], wrt[IBW], hu[IBW], hd[IBW];
 #pragma unroll
   for (int j = 0; j < IBW; ++j) {
@@ -859,6 +881,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_kernel(ConvParams p) {
     if (pos > HW - 1) pos = HW - 1;                  // rows past the frame: computed, never stored
     const int h_ = pos / W, w_ = pos - h_ * W;
     pvo[j] = ((uint32_t)pos * C + lc * 8) * 2;
+    if constexpr (RMS) ppos[j] = pos;
     wl[j] = w_ > 0;
     wrt[j] = w_ < W - 1;
     hu[j] = h_ > 0;
@@ -869,8 +892,9 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_kernel(ConvParams p) {
   // it is a frame of x (fused: activate), the tap's byte offset within the frame and its
   // row and column offsets dh, dw (0 = one before).
   Rsrc prs = make_rsrc(p.x, 0);
+  Rsrc rrs = make_rsrc(p.x, 0);                      // RMS: the source frame's rstd (x frames only)
   bool from_x = false;
-  int pdelta = 0, tdh = 1, tdw = 1;
+  int pdelta = 0, rdelta = 0, tdh = 1, tdw = 1;
   auto set_tap = [&](int tap) {
     int dt, dh, dw;
     if (MODE == kPhase) {
@@ -895,13 +919,17 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_kernel(ConvParams p) {
       prs = make_rsrc(p.cache + ((int64_t)n * 2 + tf + 2) * HW * C, frame_bytes);
     else
       prs = make_rsrc(p.x, 0);                       // no cache: zero frames
+    if constexpr (RMS)
+      rrs = tf >= 0 ? make_rsrc(p.rstd + ((int64_t)n * T + tf) * HW, (uint32_t)HW * 8) : make_rsrc(p.rstd, 0);
     pdelta = ((dh - 1) * W + (dw - 1)) * C * 2;
+    rdelta = (dh - 1) * W + (dw - 1);
     tdh = dh;
     tdw = dw;
   };
 
   uint4 held[FUSE ? IBW : 1];
   bool hact[FUSE ? IBW : 1];                         // fused: activate (a row of x in the frame)
+  double hr[RMS ? IBW : 1];                          // RMS: the held row's rstd
 
   // Stage cursors (uniform): inner tap i, channel chunk ch, tap group o; stage (o, ch, i)
   // is tap o * INNER + i over channels ch * 32 .. ch * 32 + 31.
@@ -943,6 +971,12 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_kernel(ConvParams p) {
         if (FUSE) {
           held[j] = load16(prs, voff, 0);
           hact[j] = from_x && okw && (tdh != 0 || hu[j]) && (tdh != 2 || hd[j]);
+          if constexpr (RMS) {
+            // the row's rstd (positions outside the frame, which are never activated, read 0)
+            const uint32_t roff = okw ? (uint32_t)(ppos[j] + rdelta) * 8u : kOOB;
+            const auto rv = __builtin_amdgcn_raw_buffer_load_b64(rrs, roff, 0, 0);
+            hr[j] = __builtin_bit_cast(double, rv);
+          }
         } else {
           dma16(prs, voff, 0, lp + qi * 1024);
         }
@@ -952,9 +986,10 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_kernel(ConvParams p) {
     next_stage(pi, pch, po);
     if ((INNER > 1 || pch == 0) && po < TAPS / INNER) set_tap(po * INNER + pi);
   };
-  // Fused: per-channel fp64 affines of this sample, in LDS after the stage buffers; the held
-  // rows of stage s are activated into its buffer (calls come in stage order). The bias of
-  // the tile's BN output channels follows.
+  // Fused: per-channel fp64 affines of this sample (GroupNorm), or the fp64 gains (RMS, the
+  // affine of a row being gain * its rstd), in LDS after the stage buffers; the held rows of
+  // stage s are activated into its buffer (calls come in stage order). The bias of the
+  // tile's BN output channels follows.
   double* tab = reinterpret_cast<double*>(smem + NS * STAGE);
   float* lbias = reinterpret_cast<float*>(smem + NS * STAGE + (FUSE ? C * 16 : 0));
   int ci = 0, cch = 0, co = 0;
@@ -974,7 +1009,20 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_kernel(ConvParams p) {
       const int qi = wave + NW * j;
       if (IB % NW == 0 || qi < IB) {
         uint4 v = held[j];
-        if (hact[j]) v = activate_packet(v, a);
+        if (hact[j]) {
+          if constexpr (RMS) {
+            // rms_silu's affine: (double) gain * rstd, no shift
+            Affine ar[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              ar[i].s = a[i].s * hr[j];
+              ar[i].b = 0.0;
+            }
+            v = activate_packet(v, ar);
+          } else {
+            v = activate_packet(v, a);
+          }
+        }
         *reinterpret_cast<uint4*>(lp + qi * 1024 + lane * 16) = v;
       }
     }
@@ -1036,11 +1084,18 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void conv_kernel(ConvParams p) {
   BiasStage<BN> bias;
   bias.issue(p, ntile, tid);                         // before any move: the waits below cover it
   if (FUSE) {
-    const int cg = C / p.groups;
-    for (int c = tid; c < C; c += 64 * NW) {
-      const Affine a = channel_affine(p.stats, p.gamma, p.beta, p.eps, p.groups, cg, n, c);
-      tab[2 * c] = a.s;
-      tab[2 * c + 1] = a.b;
+    if constexpr (RMS) {
+      for (int c = tid; c < C; c += 64 * NW) {
+        tab[2 * c] = (double)p.gamma[c];
+        tab[2 * c + 1] = 0.0;
+      }
+    } else {
+      const int cg = C / p.groups;
+      for (int c = tid; c < C; c += 64 * NW) {
+        const Affine a = channel_affine(p.stats, p.gamma, p.beta, p.eps, p.groups, cg, n, c);
+        tab[2 * c] = a.s;
+        tab[2 * c + 1] = a.b;
+      }
     }
 #pragma unroll
     for (int s = 0; s < NS - 2; ++s) issue_w(s);
@@ -2054,7 +2109,7 @@ struct TileCfg {
   bool slab;           // conv_slab_kernel (else conv_kernel)
 };
 
-template <int BM, int BN, int WGM, int WGN, int NS, int MODE, bool FUSE>
+template <int BM, int BN, int WGM, int WGN, int NS, int MODE, int FUSE>
 static TileCfg make_cfg(int c) {
   TileCfg t;
   t.bm = BM;
@@ -2083,7 +2138,7 @@ static TileCfg make_slab_cfg() {
 }
 
 // Candidate tiles for N-tile width bn (largest M tile first).
-template <int MODE, bool FUSE>
+template <int MODE, int FUSE>
 static int candidates(int bn, int c, TileCfg* out) {
   int n = 0;
   if constexpr (MODE == kWino) {                    // K > 128 only: the slab tiles
@@ -2120,7 +2175,7 @@ static int candidates(int bn, int c, TileCfg* out) {
 
 // Pick the M tile that minimises (waves of workgroups over 256 CUs) x (work per tile).
 // Tiles do not straddle frames: hw positions per frame, frames frames in all.
-template <int MODE, bool FUSE>
+template <int MODE, int FUSE>
 static TileCfg choose_tile(int64_t hw, int64_t frames, int k, int c, int64_t groups_of_tiles) {
   const int bn = k > 128 ? 256 : k > 64 ? 128 : k > 32 ? 64 : 32;
   TileCfg cand[4];
@@ -2174,7 +2229,8 @@ static bool launch_conv(const TileCfg& cfg, ConvParams& p, int64_t n_samples, in
 
 // cache_out of a causal convolution over frames x0 .. x0 + T - 1 (T = d.t - x0) of x.
 static bool launch_cache_out(const uint16_t* x, sgn_dims d, const uint16_t* cache_in,
-                             const sgn_gn* fuse, uint16_t* cache_out, hipStream_t stream, int x0 = 0) {
+                             const sgn_gn* fuse, uint16_t* cache_out, hipStream_t stream, int x0 = 0,
+                             const double* rms_rstd = nullptr, const float* rms_gain = nullptr) {
   const int cp = (int)(d.c / 8);
   int rstep = 256 / cp;
   if (rstep < 1) rstep = 1;
@@ -2188,8 +2244,8 @@ static bool launch_cache_out(const uint16_t* x, sgn_dims d, const uint16_t* cach
   cache_out_kernel<<<dim3((unsigned)blocks, (unsigned)d.n), 256, 0, stream>>>(
       reinterpret_cast<const uint4*>(x), reinterpret_cast<const uint4*>(cache_in),
       reinterpret_cast<uint4*>(cache_out), (int)d.t - x0, (int)d.t, x0, hw, cp, rstep, rows,
-      fuse ? fuse->stats : nullptr, fuse ? fuse->gamma : nullptr, fuse ? fuse->beta : nullptr,
-      fuse ? (double)fuse->eps : 0.0, fuse ? fuse->groups : 1);
+      fuse ? fuse->stats : nullptr, fuse ? fuse->gamma : rms_gain, fuse ? fuse->beta : nullptr,
+      fuse ? (double)fuse->eps : 0.0, fuse ? fuse->groups : 1, fuse ? nullptr : rms_rstd);
   return launch_ok("cache_out");
 }
 
@@ -2292,6 +2348,13 @@ struct RmsOut {
   uint16_t* act;
 };
 
+// The RMS norm + SiLU a convolution applies to x in its operand load
+// (causal_conv3d_rms_input): rstd per position of x from rms_silu_rstd, the gain.
+struct RmsIn {
+  const double* rstd;
+  const float* gain;
+};
+
 // causal_conv3d_rms computes act in the epilogue for an unfused convolution whose one N
 // tile holds all K channels (128 < K <= 256, the 224-row slab tile); y may then be NULL.
 static bool rms_in_epilogue(int k, const sgn_gn* fuse) { return !fuse && k > 128 && k <= 256 && k % 8 == 0; }
@@ -2299,12 +2362,30 @@ static bool rms_in_epilogue(int k, const sgn_gn* fuse) { return !fuse && k > 128
 static int causal_conv_impl(const char* fn, const uint16_t* x, sgn_dims d, const uint16_t* cache_in,
                             const uint16_t* w, int k, const float* bias, const uint16_t* residual,
                             const sgn_gn* fuse, uint16_t* y, uint16_t* cache_out, const NextStats* ns,
-                            hipStream_t stream, const RmsOut* ro = nullptr) {
+                            hipStream_t stream, const RmsOut* ro = nullptr, const RmsIn* ri = nullptr) {
+  if (ri && (fuse || ro)) {
+    set_error("%s: internal: an RMS-normalised input takes no GroupNorm and no RMS epilogue", fn);
+    return SGN_EINVAL;
+  }
   const bool rms_epi = ro && rms_in_epilogue(k, fuse);
   uint16_t* yo = y ? y : (rms_epi ? ro->act : nullptr);   // the conv's primary output
   if (!conv_common_checks(x, d, w, k, yo, fn)) return SGN_EINVAL;
   int rc = check_fuse(fuse, d, fn);
   if (rc) return rc;
+  if (ri) {
+    if (!ri->rstd || !ri->gain) {
+      set_error("%s: rstd and gain are required", fn);
+      return SGN_EINVAL;
+    }
+    if (d.c > 2048) {
+      set_error("%s: the RMS norm in the operand load supports C <= 2048", fn);
+      return SGN_EINVAL;
+    }
+    if (((uintptr_t)ri->rstd & 7) || ((uintptr_t)ri->gain & 3)) {
+      set_error("%s: rstd must be 8-byte and gain 4-byte aligned", fn);
+      return SGN_EALIGN;
+    }
+  }
   if (!aligned16(x) || !aligned16(w) || !aligned16(y) || (cache_in && !aligned16(cache_in)) ||
       (residual && !aligned16(residual)) || (cache_out && !aligned16(cache_out)) ||
       (bias && !aligned16(bias))) {
@@ -2313,6 +2394,15 @@ static int causal_conv_impl(const char* fn, const uint16_t* x, sgn_dims d, const
   }
   const size_t xb = (size_t)(d.n * d.t * d.h * d.w * d.c) * 2;
   const size_t yb = (size_t)(d.n * d.t * d.h * d.w) * k * 2;
+  if (ri) {
+    const size_t rb = (size_t)(d.n * d.t * d.h * d.w) * 8, gb = (size_t)d.c * 4;
+    const size_t cob = (size_t)(d.n * 2 * d.h * d.w * d.c) * 2;
+    if (overlap(y, yb, ri->rstd, rb) || overlap(y, yb, ri->gain, gb) ||
+        (cache_out && (overlap(cache_out, cob, ri->rstd, rb) || overlap(cache_out, cob, ri->gain, gb)))) {
+      set_error("%s: an output overlaps rstd or gain", fn);
+      return SGN_EALIAS;
+    }
+  }
   const size_t cb = (size_t)(d.n * 2 * d.h * d.w * d.c) * 2;
   const size_t wb = (size_t)k * 27 * d.c * 2;
   if (overlap(yo, yb, x, xb) || overlap(yo, yb, w, wb) || (cache_in && overlap(yo, yb, cache_in, cb)) ||
@@ -2351,8 +2441,13 @@ static int causal_conv_impl(const char* fn, const uint16_t* x, sgn_dims d, const
   p.C = (int)d.c;
   p.K = k;
   p.mper = d.t * d.h * d.w;
-  TileCfg cfg = fuse ? choose_tile<kCausal, true>(d.h * d.w, d.t, k, p.C, d.n)
-                     : choose_tile<kCausal, false>(d.h * d.w, d.t, k, p.C, d.n);
+  if (ri) {
+    p.rstd = ri->rstd;
+    p.gamma = ri->gain;
+  }
+  TileCfg cfg = fuse ? choose_tile<kCausal, kFuseGn>(d.h * d.w, d.t, k, p.C, d.n)
+                : ri ? choose_tile<kCausal, kFuseRms>(d.h * d.w, d.t, k, p.C, d.n)
+                     : choose_tile<kCausal, kFuseNone>(d.h * d.w, d.t, k, p.C, d.n);
   if (rms_epi)      // the same tile, in its instantiation with the RMS epilogue
     cfg = cfg.bm == 256 ? make_slab_cfg<256, 256, 2, 2, kCausal, true>() : make_slab_cfg<224, 256, 1, 4, kCausal, true>();
   if (rms_epi) {
@@ -2376,7 +2471,9 @@ static int causal_conv_impl(const char* fn, const uint16_t* x, sgn_dims d, const
     p.ncg = ncg;
   }
   if (!launch_conv(cfg, p, d.n, 1, stream, fn)) return SGN_ELAUNCH;
-  if (cache_out && !launch_cache_out(x, d, cache_in, fuse, cache_out, stream)) return SGN_ELAUNCH;
+  if (cache_out && !launch_cache_out(x, d, cache_in, fuse, cache_out, stream, 0, ri ? ri->rstd : nullptr,
+                                     ri ? ri->gain : nullptr))
+    return SGN_ELAUNCH;
   if (ro && !rms_epi) {                              // act from y by the RMS norm kernel
     sgn_dims yd = d;
     yd.c = k;
@@ -2436,13 +2533,13 @@ extern "C" int sgn_conv_plan(int op, sgn_dims d, int k, int fused, sgn_plan* pla
         set_error("%s: fused GroupNorm supports C <= 2048", fn);
         return SGN_EINVAL;
       }
-      cfg = fused ? choose_tile<kCausal, true>(d.h * d.w, d.t, k, (int)d.c, d.n)
-                  : choose_tile<kCausal, false>(d.h * d.w, d.t, k, (int)d.c, d.n);
+      cfg = fused ? choose_tile<kCausal, kFuseGn>(d.h * d.w, d.t, k, (int)d.c, d.n)
+                  : choose_tile<kCausal, kFuseNone>(d.h * d.w, d.t, k, (int)d.c, d.n);
       break;
     case SGN_OP_PHASES:
       if (!conv_shape_ok(d, k, fn)) return SGN_EINVAL;
       units = d.n * 4;
-      cfg = choose_tile<kPhase, false>(d.h * d.w, d.t, k, (int)d.c, units);
+      cfg = choose_tile<kPhase, kFuseNone>(d.h * d.w, d.t, k, (int)d.c, units);
       break;
     case SGN_OP_TIME:
       if (!dims_ok(d, fn)) return SGN_EINVAL;
@@ -2452,7 +2549,7 @@ extern "C" int sgn_conv_plan(int op, sgn_dims d, int k, int fused, sgn_plan* pla
       }
       kk = 2 * (int)d.c;
       if (!conv_shape_ok(d, kk, fn)) return SGN_EINVAL;
-      cfg = choose_tile<kTime, false>(d.h * d.w, d.t, kk, (int)d.c, d.n);
+      cfg = choose_tile<kTime, kFuseNone>(d.h * d.w, d.t, kk, (int)d.c, d.n);
       break;
     default:
       set_error("%s: unknown op %d", fn, op);
@@ -2503,6 +2600,16 @@ extern "C" int causal_conv3d_rms(const uint16_t* x, sgn_dims d, const uint16_t* 
   }
   const RmsOut ro = {gain, eps, act};
   return causal_conv_impl(fn, x, d, cache_in, w, k, bias, residual, fuse, y, cache_out, nullptr, stream, &ro);
+}
+
+extern "C" int causal_conv3d_rms_input(const uint16_t* x, sgn_dims d, const uint16_t* cache_in,
+                                       const uint16_t* w, int k, const float* bias, const uint16_t* residual,
+                                       const double* rstd, const float* gain, uint16_t* y,
+                                       uint16_t* cache_out, hipStream_t stream) {
+  clear_error();
+  const RmsIn ri = {rstd, gain};
+  return causal_conv_impl("causal_conv3d_rms_input", x, d, cache_in, w, k, bias, residual, nullptr, y,
+                          cache_out, nullptr, stream, nullptr, &ri);
 }
 
 extern "C" size_t causal_conv3d_next_stats_workspace(sgn_dims d, int k, int next_groups) {
@@ -2639,7 +2746,7 @@ static int upsample_impl(const char* fn, const uint16_t* x, sgn_dims d, const ui
   p.C = (int)d.c;
   p.K = k;
   p.mper = d.t * d.h * d.w;
-  TileCfg cfg = choose_tile<kPhase, false>(d.h * d.w, d.t, k, p.C, d.n * 4);
+  TileCfg cfg = choose_tile<kPhase, kFuseNone>(d.h * d.w, d.t, k, p.C, d.n * 4);
   if (sc && cfg.slab)   // the same tile, in its instantiation with the shortcut epilogue
     cfg = cfg.bm == 256 ? make_slab_cfg<256, 256, 2, 2, kPhase, true>() : make_slab_cfg<224, 256, 1, 4, kPhase, true>();
   if (sc && !cfg.shortcut) {
@@ -2717,7 +2824,7 @@ extern "C" int time_upsample_conv(const uint16_t* x, sgn_dims d, const uint16_t*
     p.x0 = first;
     p.To = (int)to;
     p.first = first;
-    const TileCfg cfg = choose_tile<kTime, false>(hw, nf, k, p.C, d.n);
+    const TileCfg cfg = choose_tile<kTime, kFuseNone>(hw, nf, k, p.C, d.n);
     if (!launch_conv(cfg, p, d.n, 1, stream, fn)) return SGN_ELAUNCH;
   }
   if (first) {
@@ -2799,8 +2906,8 @@ extern "C" int head_conv_d2s(const uint16_t* x, sgn_dims d, const uint16_t* cach
       head_kernel<8><<<dim3((unsigned)nb), 512, lds, stream>>>(p, wblocks);
     if (!launch_ok(fn)) return SGN_ELAUNCH;
   } else {
-    const TileCfg cfg = fuse ? make_cfg<256, 32, 4, 1, kStages, kHead, true>(p.C)
-                             : make_cfg<256, 32, 4, 1, kStages, kHead, false>(p.C);
+    const TileCfg cfg = fuse ? make_cfg<256, 32, 4, 1, kStages, kHead, kFuseGn>(p.C)
+                             : make_cfg<256, 32, 4, 1, kStages, kHead, kFuseNone>(p.C);
     if (!launch_conv(cfg, p, d.n, 1, stream, fn)) return SGN_ELAUNCH;
   }
   if (cache_out && !launch_cache_out(x, d, cache_in, fuse, cache_out, stream)) return SGN_ELAUNCH;
@@ -2914,7 +3021,7 @@ extern "C" int causal_conv3d_winograd(const uint16_t* x, sgn_dims d, const uint1
     p.Tx = (int)d.t + 2;
     p.x0 = 2;
     p.wino_n = (int)d.n;
-    const TileCfg cfg = choose_tile<kWino, false>(tp, d.t, k, p.C, 36 * d.n);
+    const TileCfg cfg = choose_tile<kWino, kFuseNone>(tp, d.t, k, p.C, 36 * d.n);
     if (!launch_conv(cfg, p, 36 * d.n, 1, stream, fn)) return SGN_ELAUNCH;
   }
   {

@@ -12,7 +12,9 @@
 // its 8 channels once and then streams packets through activate_packet().
 //
 // RMS norm + SiLU (rms_silu): the decoder's per-position norm, one read and one write,
-// the same activate_packet() with the affine gain * rstd.
+// the same activate_packet() with the affine gain * rstd; rms_silu_rstd runs the same
+// kernel writing each position's rstd instead (for a convolution that applies the norm in
+// its operand load).
 //
 // Pages: WanGP group_norm_silu.py (module docstring: exact partial sums reduced in
 // fp64 in a fixed order, one rounding to the output dtype; its apply kernel: biased
@@ -281,12 +283,13 @@ static bool gn_shape_ok(sgn_dims d, int groups, const char* fn) {
 // Each lane sums the exact squares of its values in fp64 (x*x has 16 significant bits) and
 // the LPP lanes add their sums by a xor butterfly: the same order for every position. The
 // pre-activation x * (gain * rstd) is formed in fp64 and the SiLU in fp32 by
-// activate_packet, as in gn_silu_apply.
-template <int LPP, int PPL, int U>
+// activate_packet, as in gn_silu_apply. RSTD: the same launch writes each position's rstd
+// (fp64) instead of y -- the bits the activation would have used (rms_silu_rstd).
+template <int LPP, int PPL, int U, bool RSTD = false>
 __global__ __launch_bounds__(kThreads) void rms_silu_kernel(const uint4* __restrict__ x, uint4* __restrict__ y,
                                                             int64_t positions, int cp,
                                                             const float* __restrict__ gain, double eps,
-                                                            double channels) {
+                                                            double channels, double* __restrict__ rstd_out) {
   constexpr int PPW = 64 / LPP;                      // positions per wave
   const int lane = threadIdx.x & 63;
   const int sub = lane / LPP, li = lane % LPP;
@@ -295,7 +298,7 @@ __global__ __launch_bounds__(kThreads) void rms_silu_kernel(const uint4* __restr
   for (int j = 0; j < PPL; ++j) {
     const int col = li + j * LPP;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) g[j][i] = col < cp ? gain[col * 8 + i] : 0.0f;
+    for (int i = 0; i < 8; ++i) g[j][i] = !RSTD && col < cp ? gain[col * 8 + i] : 0.0f;
   }
   const int64_t wave = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
   const int64_t stride = (int64_t)gridDim.x * (kThreads / 64) * U * PPW;
@@ -327,6 +330,10 @@ __global__ __launch_bounds__(kThreads) void rms_silu_kernel(const uint4* __restr
 #pragma unroll
       for (int o = LPP / 2; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
       const double rstd = 1.0 / sqrt(ss / channels + eps);
+      if constexpr (RSTD) {
+        if (li == 0 && pos < positions) rstd_out[pos] = rstd;
+        continue;
+      }
 #pragma unroll
       for (int j = 0; j < PPL; ++j) {
         const int col = li + j * LPP;
@@ -540,6 +547,35 @@ extern "C" int gn_silu_apply(const uint16_t* x, sgn_dims d, int groups, const do
   return SGN_OK;
 }
 
+// rms_silu (rstd_out == null) or rms_silu_rstd (rstd_out != null): the same kernel and
+// launch shape, so the rstd the second writes is the one the first applies.
+static void launch_rms(const uint16_t* x, sgn_dims d, const float* gain, float eps, uint16_t* y,
+                       double* rstd_out, hipStream_t stream) {
+  const int64_t positions = d.n * d.t * d.h * d.w;
+  const int cp = (int)(d.c / 8);
+  const uint4* xp = reinterpret_cast<const uint4*>(x);
+  uint4* yp = reinterpret_cast<uint4*>(y);
+  const double e = (double)eps, c = (double)d.c;
+  // LPP = the power of two >= C/8 (8 .. 64), then PPL packets per lane past 64 lanes;
+  // per block: 4 waves x (64 / LPP positions) x U groups.
+  // The grid sweeps the positions as the GroupNorm apply does (up to kApplyBlocks workgroups).
+  auto launch = [&](auto plain, auto rstd_only, int64_t per_block) {
+    int64_t blocks = (positions + per_block - 1) / per_block;
+    if (blocks > kApplyBlocks) blocks = kApplyBlocks;
+    if (rstd_out)
+      rstd_only<<<dim3((unsigned)blocks), kThreads, 0, stream>>>(xp, yp, positions, cp, gain, e, c, rstd_out);
+    else
+      plain<<<dim3((unsigned)blocks), kThreads, 0, stream>>>(xp, yp, positions, cp, gain, e, c, rstd_out);
+  };
+  if (cp <= 8) launch(rms_silu_kernel<8, 1, 4>, rms_silu_kernel<8, 1, 4, true>, 4 * 8 * 4);
+  else if (cp <= 16) launch(rms_silu_kernel<16, 1, 4>, rms_silu_kernel<16, 1, 4, true>, 4 * 4 * 4);
+  else if (cp <= 32) launch(rms_silu_kernel<32, 1, 4>, rms_silu_kernel<32, 1, 4, true>, 4 * 2 * 4);
+  else if (cp <= 64) launch(rms_silu_kernel<64, 1, 4>, rms_silu_kernel<64, 1, 4, true>, 4 * 1 * 4);
+  else if (cp <= 128) launch(rms_silu_kernel<64, 2, 2>, rms_silu_kernel<64, 2, 2, true>, 4 * 1 * 2);
+  else if (cp <= 256) launch(rms_silu_kernel<64, 4, 1>, rms_silu_kernel<64, 4, 1, true>, 4);
+  else launch(rms_silu_kernel<64, 8, 1>, rms_silu_kernel<64, 8, 1, true>, 4);
+}
+
 extern "C" int rms_silu(const uint16_t* x, sgn_dims d, const float* gain, float eps, uint16_t* y,
                         hipStream_t stream) {
   clear_error();
@@ -565,26 +601,37 @@ extern "C" int rms_silu(const uint16_t* x, sgn_dims d, const float* gain, float 
     set_error("rms_silu: y partially overlaps x (only y == x is allowed)");
     return SGN_EALIAS;
   }
-  const int64_t positions = d.n * d.t * d.h * d.w;
-  const int cp = (int)(d.c / 8);
-  const uint4* xp = reinterpret_cast<const uint4*>(x);
-  uint4* yp = reinterpret_cast<uint4*>(y);
-  const double e = (double)eps, c = (double)d.c;
-  // LPP = the power of two >= C/8 (8 .. 64), then PPL packets per lane past 64 lanes;
-  // per block: 4 waves x (64 / LPP positions) x U groups.
-  // The grid sweeps the positions as the GroupNorm apply does (up to kApplyBlocks workgroups).
-  auto launch = [&](auto kernel, int64_t per_block) {
-    int64_t blocks = (positions + per_block - 1) / per_block;
-    if (blocks > kApplyBlocks) blocks = kApplyBlocks;
-    kernel<<<dim3((unsigned)blocks), kThreads, 0, stream>>>(xp, yp, positions, cp, gain, e, c);
-  };
-  if (cp <= 8) launch(rms_silu_kernel<8, 1, 4>, 4 * 8 * 4);
-  else if (cp <= 16) launch(rms_silu_kernel<16, 1, 4>, 4 * 4 * 4);
-  else if (cp <= 32) launch(rms_silu_kernel<32, 1, 4>, 4 * 2 * 4);
-  else if (cp <= 64) launch(rms_silu_kernel<64, 1, 4>, 4 * 1 * 4);
-  else if (cp <= 128) launch(rms_silu_kernel<64, 2, 2>, 4 * 1 * 2);
-  else if (cp <= 256) launch(rms_silu_kernel<64, 4, 1>, 4);
-  else launch(rms_silu_kernel<64, 8, 1>, 4);
+  launch_rms(x, d, gain, eps, y, nullptr, stream);
   if (!launch_ok("rms_silu")) return SGN_ELAUNCH;
+  return SGN_OK;
+}
+
+extern "C" int rms_silu_rstd(const uint16_t* x, sgn_dims d, float eps, double* rstd, hipStream_t stream) {
+  const char* fn = "rms_silu_rstd";
+  clear_error();
+  if (!dims_ok(d, fn)) return SGN_EINVAL;
+  if (d.c % 64 != 0 || d.c > 4096) {
+    set_error("%s: C=%lld must be a multiple of 64, at most 4096", fn, (long long)d.c);
+    return SGN_EINVAL;
+  }
+  if (!x || !rstd) {
+    set_error("%s: x and rstd are required", fn);
+    return SGN_EINVAL;
+  }
+  if (!(eps > 0.0f) || !isfinite(eps)) {
+    set_error("%s: eps must be a positive finite number", fn);
+    return SGN_EINVAL;
+  }
+  if (!aligned16(x) || ((uintptr_t)rstd & 7)) {
+    set_error("%s: x must be 16-byte and rstd 8-byte aligned", fn);
+    return SGN_EALIGN;
+  }
+  const int64_t positions = d.n * d.t * d.h * d.w;
+  if (overlap(x, (size_t)(positions * d.c) * 2, rstd, (size_t)positions * 8)) {
+    set_error("%s: rstd overlaps x", fn);
+    return SGN_EALIAS;
+  }
+  launch_rms(x, d, nullptr, eps, nullptr, rstd, stream);
+  if (!launch_ok(fn)) return SGN_ELAUNCH;
   return SGN_OK;
 }

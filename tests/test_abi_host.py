@@ -154,6 +154,30 @@ def test_conv_rms_rejects():
     _err(call(a=FAKE + 64), EALIAS)                     # act inside x
 
 
+def test_rms_input_rejects():
+    lib = sga.load_library()
+    far = FAKE + (1 << 32)
+    w = FAKE + (1 << 30)
+    rstd, gain = FAKE + (1 << 35), FAKE + (1 << 36)
+    _err(lib.rms_silu_rstd(FAKE, D(c=96), 1e-6, rstd, None), EINVAL)          # C % 64
+    _err(lib.rms_silu_rstd(FAKE, D(), 1e-6, None, None), EINVAL)
+    _err(lib.rms_silu_rstd(FAKE, D(), 0.0, rstd, None), EINVAL)               # eps
+    _err(lib.rms_silu_rstd(FAKE + 8, D(), 1e-6, rstd, None), EALIGN)
+    _err(lib.rms_silu_rstd(FAKE, D(), 1e-6, rstd + 4, None), EALIGN)
+    _err(lib.rms_silu_rstd(FAKE, D(), 1e-6, FAKE + 64, None), EALIAS)         # rstd inside x
+
+    def call(d=D(), k=64, r=rstd, g=gain, y=far, co=None):
+        return lib.causal_conv3d_rms_input(FAKE, d, None, w, k, None, None, r, g, y, co, None)
+    _err(call(r=None), EINVAL)
+    _err(call(g=None), EINVAL)
+    _err(call(d=D(c=4096)), EINVAL)                     # C > 2048 in the operand-load form
+    _err(call(k=6), EINVAL)                             # K % 4
+    _err(call(r=rstd + 4), EALIGN)
+    _err(call(g=gain + 2), EALIGN)
+    _err(call(y=rstd), EALIAS)                          # y over rstd
+    _err(call(y=FAKE + 64), EALIAS)                     # y inside x
+
+
 def test_next_stats_workspace_size():
     lib = sga.load_library()
     ws = lib.causal_conv3d_next_stats_workspace(D(), 256, 32)

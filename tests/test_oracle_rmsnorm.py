@@ -75,3 +75,32 @@ def test_against_torch_rms_norm_fp64(shape, eps):
     xt, gt = torch.from_numpy(x), torch.from_numpy(g)
     want = torch.nn.functional.silu(torch.nn.functional.rms_norm(xt, (shape[-1],), weight=gt, eps=eps)).numpy()
     np.testing.assert_allclose(rmsnorm.rms_silu(x, g, eps), want, rtol=1e-14, atol=1e-14)
+
+
+def test_rstd_closed_forms_and_exact_tiny():
+    """rms_rstd: a constant position of a power of two with eps = 0 gives 1/|c| exactly; a tiny
+    input against its exact rational mean of squares (Fractions), within one rounding of the
+    square root and one of the division."""
+    from fractions import Fraction
+    for c in (0.5, -4.0, 2.0 ** -10):
+        r = rmsnorm.rms_rstd(np.full((2, 64), c), 0.0)
+        assert np.array_equal(r, np.full(2, 1.0 / abs(c)))
+    x = _x((1, 1, 2, 3, 8), 7)
+    eps = 1e-5
+    r = rmsnorm.rms_rstd(x, eps)
+    assert r.shape == (1, 1, 2, 3)
+    for idx in np.ndindex(r.shape):
+        ms = sum(Fraction(v) ** 2 for v in x[idx]) / 8 + Fraction(eps)
+        want = 1.0 / math.sqrt(float(ms))
+        assert abs(r[idx] - want) <= 4e-16 * want
+
+
+def test_rstd_against_torch_rsqrt_fp64():
+    """Against torch's float64 rsqrt of the mean of squares (an independent library routine), and
+    rms_silu as the SiLU of x * gain * rstd (the two forms of the same norm, to fp64 rounding)."""
+    x, g = _x((2, 2, 5, 3, 256), 3, mean=0.3), _g(256, 3)
+    r = rmsnorm.rms_rstd(x, 1e-6)
+    t = torch.rsqrt(torch.from_numpy(x).pow(2).mean(dim=-1) + 1e-6).numpy()
+    assert np.allclose(r, t, rtol=1e-14, atol=0)
+    via = groupnorm.silu(x * g * r[..., None])
+    assert np.allclose(via, rmsnorm.rms_silu(x, g, 1e-6), rtol=1e-13, atol=1e-300)
