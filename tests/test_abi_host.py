@@ -314,6 +314,14 @@ def test_binding_rejects_bad_tensors():
         sga.upsample2x_conv_phases_shortcut(x, _bf(2, 2, 64, 2, 2, 64), _bf(1, 2, 4, 5, 64), 1, False)
     with pytest.raises(ValueError, match="y must have shape"):
         sga.time_upsample_conv(x, _bf(128, 3, 64), True, y=_bf(1, 4, 4, 4, 64))
+    with pytest.raises(TypeError, match="rstd must be torch.float64"):
+        sga.causal_conv3d_rms_input(x, w, torch.zeros(1, 2, 4, 4), torch.ones(64))
+    with pytest.raises(ValueError, match="rstd must have shape"):
+        sga.causal_conv3d_rms_input(x, w, torch.zeros(1, 2, 4, 5, dtype=torch.float64), torch.ones(64))
+    with pytest.raises(ValueError, match="gain must have shape"):
+        sga.causal_conv3d_rms_input(x, w, torch.zeros(1, 2, 4, 4, dtype=torch.float64), torch.ones(32))
+    with pytest.raises(ValueError, match="rstd must have shape"):
+        sga.rms_silu_rstd(x, 1e-6, rstd=torch.zeros(1, 2, 4, dtype=torch.float64))
     with pytest.raises(ValueError, match="act must have shape"):
         sga.causal_conv3d_rms(x, w, torch.ones(64), 1e-6, act=_bf(1, 2, 4, 4, 32))
     with pytest.raises(ValueError, match="stats must have shape"):
