@@ -287,6 +287,29 @@ def time_loop(fn, iters):
     return s.elapsed_time(e) / iters
 
 
+def time_each(fn, iters):
+    """Per-launch ms of fn() over iters launches (an event pair around each, current stream)."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in ev]
+
+
+def head_hbm_roofline(n, t, h, w, c, flops):
+    """The output head's arithmetic intensity is near the ridge, so its roofline is
+    min(MFMA peak, AI x HBM peak): AI = FLOPs / the bytes it must move (x read, video
+    written, weights), in FLOP/byte and the TFLOP/s that HBM allows."""
+    moved = n * t * h * w * c * 2.0 + n * 3 * t * 4 * h * w * 2.0 + 12 * 27 * c * 2.0
+    ai = flops / moved
+    hbm_tf = ai * PEAK_HBM_GBPS / 1e3
+    return {"ai_flop_per_byte": round(ai, 1), "hbm_bound_TFLOP/s": round(hbm_tf, 1),
+            "roofline_TFLOP/s": round(min(PEAK_BF16_TFLOPS, hbm_tf), 1)}
+
+
 def _oracle_cores():
     try:
         from threadpoolctl import threadpool_info
@@ -406,6 +429,9 @@ def other_configs(index, dev, iters):
             rec["phases"] = {"ms": round(pms, 4), "TFLOP/s": round(ptf, 2), "frac": round(ptf / PEAK_BF16_TFLOPS, 4),
                              "flop_per_launch": pfl}
             del x, u
+        if wl.kind == "head":
+            rec.update(head_hbm_roofline(wl.n, wl.t, wl.h, wl.w, wl.c, launch_flops))
+            rec["frac_of_roofline"] = round(tf / rec["roofline_TFLOP/s"], 4)
         out[wl.name] = rec
         del step, conv_only
         torch.cuda.synchronize()
@@ -578,7 +604,8 @@ def main():
     # GroupNorm+SiLU unfused on the same tensor
     iters = max(args.steps, 10)
     extras = up_block_extras(wl, dev, iters)
-    conv_ms = time_loop(conv_only, iters)
+    each = sorted(time_each(conv_only, iters))             # per-launch: median and min beside the mean
+    conv_ms = time_loop(conv_only, iters)                  # the mean (the kernel trace's last launches)
     x, gc = gn_in
     g = wl.groups
     yb = torch.empty_like(x)
@@ -640,7 +667,8 @@ def main():
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": read_traffic(kernel_tag),
                      "kernel": "%s (%s)" % (kernel_tag.split("_" + wl.name)[0], conv_name),
-                     "kernel_ms": round(conv_ms, 4), "flop_per_launch": conv_launch_flops},
+                     "kernel_ms": round(conv_ms, 4), "flop_per_launch": conv_launch_flops,
+                     "kernel_ms_median": round(each[len(each) // 2], 4), "kernel_ms_min": round(each[0], 4)},
         "gn_silu": {"GB/s": round(gn_gbps, 1), "peak": PEAK_HBM_GBPS, "frac": round(gn_gbps / PEAK_HBM_GBPS, 4),
                     "stats_ms": round(stats_ms, 4), "apply_ms": round(apply_ms, 4),
                     "stats_GB/s": round(2.0 * x.numel() / (stats_ms * 1e-3) / 1e9, 1),
@@ -667,6 +695,9 @@ def main():
         out["gn_silu"]["frac_of_box"] = round(gn_gbps / (gn_bytes / box_s / 1e9), 4)
         if rms_ms:
             out["rms_silu"]["frac_of_box"] = round(rms_gbps / ceilings["hbm_copy_GB/s"], 4)
+    if wl.kind == "head":
+        out["roofline"].update(head_hbm_roofline(wl.n, wl.t, wl.h, wl.w, wl.c, conv_launch_flops))
+        out["roofline"]["frac_of_roofline"] = round(achieved / out["roofline"]["roofline_TFLOP/s"], 4)
     mf = read_mfma(kernel_tag)
     if mf:
         out["roofline"].update(mf)
