@@ -695,6 +695,12 @@ def main():
         out["gn_silu"]["frac_of_box"] = round(gn_gbps / (gn_bytes / box_s / 1e9), 4)
         if rms_ms:
             out["rms_silu"]["frac_of_box"] = round(rms_gbps / ceilings["hbm_copy_GB/s"], 4)
+    # HBM bytes per launch of the two GroupNorm kernels from their committed counter summaries
+    # (FETCH_SIZE + WRITE_SIZE of the same step's launches), while gn.hip is unchanged
+    gs, ga = read_traffic("gn_stats_partial_" + wl.name), read_traffic("gn_apply_kernel_" + wl.name)
+    if gs and ga:
+        out["gn_silu"]["traffic"] = {"stats_bytes": gs, "apply_bytes": ga,
+                                     "bytes_per_element": round((gs + ga) / x.numel(), 3)}
     if wl.kind == "head":
         out["roofline"].update(head_hbm_roofline(wl.n, wl.t, wl.h, wl.w, wl.c, conv_launch_flops))
         out["roofline"]["frac_of_roofline"] = round(achieved / out["roofline"]["roofline_TFLOP/s"], 4)
