@@ -598,6 +598,23 @@ def main():
     for tm in timers:
         for (_, a), (name, b) in zip(tm[:-1], tm[1:]):
             stages[name] = stages.get(name, 0.0) + a.elapsed_time(b) / args.steps
+    # launch-bound workloads: the same step captured once in a HIP graph and replayed (the
+    # library's launches are plain stream-ordered kernels, so they capture as they are)
+    graph = None
+    if wl.kind in ("block", "latent") and not args.fused:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        g.replay()
+        graph = {"ms_per_step": round(time_loop(g.replay, args.steps), 4), "replays": args.steps,
+                 "form": "the step captured in one HIP graph (torch.cuda.graph), replayed"}
+        del g
 
     # the path's other steps at this shape first (so that the conv kernel's last launches
     # are the timed ones below), then the conv kernel alone (no cache write), and
@@ -677,6 +694,8 @@ def main():
         "stages_ms": {k: round(v, 4) for k, v in stages.items()},
     }
     out.update(extras)
+    if graph:
+        out["graph"] = graph
     if rms_ms:
         rms_gbps = 4.0 * x.numel() / (rms_ms * 1e-3) / 1e9
         out["rms_silu"] = {"GB/s": round(rms_gbps, 1), "peak": PEAK_HBM_GBPS,
