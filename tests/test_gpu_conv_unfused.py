@@ -219,3 +219,39 @@ def test_fullres_block_chain_as_benched():
     _sampled_conv(vals32(a1), vals32(c0), w1, h, seed=10, what="chain conv1")
     del hv
     _sampled_conv(vals32(a2), vals32(c1), w2, y, residual=x, seed=11, what="chain conv2 + residual")
+
+
+@pytest.mark.slow
+def test_upsample_block_chain_as_benched():
+    """The upsample block exactly as bench.py's step runs it: upsample2x_conv_phases of x
+    [1,8,88,156,512], gn_silu_stats + gn_silu_apply of the upsampled u [1,8,176,312,512], then
+    the unfused conv (zero cache). Stage-wise against the oracle: the upsample at sampled
+    positions against the direct form, the statistics against the oracle's over the GPU's u,
+    the apply within 1 ulp and the conv at sampled positions."""
+    wl = WORKLOADS[3]
+    g, eps = wl.groups, wl.eps
+    x = wl.x(device=DEV)
+    w3 = wl.up_weight()
+    gamma, beta, wt = wl.gamma(), wl.beta(), wl.conv_weight()
+    wp = sga.upsample2x_prepare_weights(w3).to(DEV)
+    ushape = (1, wl.t, 2 * wl.h, 2 * wl.w, wl.c)
+    print("case upsample-block chain", flush=True)
+    u = torch.empty(ushape, dtype=torch.bfloat16, device=DEV)
+    sga.upsample2x_conv_phases(x, wp, y=u)
+    act, st = _apply(u, g, gamma.to(DEV), beta.to(DEV), eps)
+    y = sga.causal_conv3d(act, wt.to(DEV))
+    torch.cuda.synchronize()
+    pos = sample_positions(wl.t, 2 * wl.h, 2 * wl.w, 8192, seed=12)
+    idx = tuple(torch.from_numpy(pos[:, i]) for i in range(4))
+    o = oconv.upsample2x_conv_at(vals32(x), vals(w3), pos)
+    assert_conv_close(bits(u.cpu()[idx]), o, "chain upsample")
+    del x
+    uv = vals32(u)
+    del u
+    mean, var = ogn.group_stats(uv, g)
+    st = st.cpu().numpy()
+    np.testing.assert_allclose(st[..., 0], mean, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(st[..., 1], var, rtol=1e-10, atol=1e-12)
+    _sampled_apply(uv, act, g, gamma, beta, eps, stats=(mean, var), seed=13)
+    del uv
+    _sampled_conv(vals32(act), None, wt, y, seed=14, what="chain conv")
