@@ -706,52 +706,79 @@ struct BiasStage {
 
 // cache_out = the last 2 frames of P = cat(cache_in, a), a = frames x0 .. x0 + T - 1 of the
 // Tx frames per sample of x; frames of x are activated when fused (same per-thread column
-// layout and activate_packet as gn_silu_apply; with rstd, rms_silu's per-position affine). A row of cp packets is covered by
-// tpr = min(cp, 256) threads, each taking every tpr-th packet; rstep rows per block pass.
+// layout and activate_packet as gn_silu_apply; with rstd, rms_silu's per-position affine).
+// Grid: (blocks over the H x W positions of a frame, sample n, cache frame f): the source
+// frame of a block -- a frame of x, of cache_in, or zeros -- is uniform, and no thread
+// divides by the frame size. A row of cp packets is covered by tpr = min(cp, 256) threads,
+// each taking every tpr-th packet; rstep rows per block pass. A thread moves kCacheRows rows
+// per iteration with all loads issued before the first store. ACT = false is the plain copy
+// (no activation, few registers: more rows in flight per thread).
+template <bool ACT>
 __global__ __launch_bounds__(256) void cache_out_kernel(
-    const uint4* x, const uint4* cache_in, uint4* cache_out, int T, int Tx, int x0, int64_t hw, int cp,
-    int rstep, int64_t rows_per_block, const double* stats, const float* gamma, const float* beta,
-    double eps, int groups, const double* rstd) {
-  const int tid = threadIdx.x, n = blockIdx.y;
+    const uint4* __restrict__ x, const uint4* __restrict__ cache_in, uint4* __restrict__ cache_out, int T,
+    int Tx, int x0, int64_t hw, int cp, int rstep, int64_t rows_per_block, const double* __restrict__ stats,
+    const float* __restrict__ gamma, const float* __restrict__ beta, double eps, int groups,
+    const double* __restrict__ rstd) {
+  const int tid = threadIdx.x, n = blockIdx.y, f = blockIdx.z;
   const int tpr = cp < 256 ? cp : 256;
   if (tid >= rstep * tpr) return;
+  constexpr int kCacheRows = ACT ? 4 : 8;
   const int c0 = tid % tpr;
-  const int64_t positions = 2 * hw;
   const int64_t start = (int64_t)blockIdx.x * rows_per_block;
   int64_t end = start + rows_per_block;
-  if (end > positions) end = positions;
+  if (end > hw) end = hw;
+  const int pf = T + f;                              // frame of P = cat(cache_in, x)
+  const uint4* src = nullptr;
+  const double* rs = nullptr;
+  if (pf >= 2) {
+    const int64_t fx = (int64_t)n * Tx + x0 + pf - 2;
+    src = x + fx * hw * cp;
+    if (!stats && rstd) rs = rstd + fx * hw;
+  } else if (cache_in) {
+    src = cache_in + ((int64_t)n * 2 + pf) * hw * cp;
+  }
+  const bool act = ACT && pf >= 2 && (stats || rs);
+  uint4* dst = cache_out + ((int64_t)n * 2 + f) * hw * cp;
   for (int col = c0; col < cp; col += tpr) {
     Affine a[8];
-    if (stats) {
+    if (ACT && stats && pf >= 2) {
       const int cg = cp * 8 / groups;
 #pragma unroll
       for (int i = 0; i < 8; ++i) a[i] = channel_affine(stats, gamma, beta, eps, groups, cg, n, col * 8 + i);
     }
-    for (int64_t q = start + tid / tpr; q < end; q += rstep) {
-      const int f = (int)(q / hw);                   // 0 or 1
-      const int64_t s = q - f * hw;
-      const int pf = T + f;                          // frame of P = cat(cache_in, x)
-      uint4 v;
-      if (pf >= 2) {
-        v = x[(((int64_t)n * Tx + x0 + pf - 2) * hw + s) * cp + col];
-        if (stats) {
-          v = activate_packet(v, a);
-        } else if (rstd) {                           // the RMS norm: gain (in gamma) * rstd
-          const double r = rstd[((int64_t)n * Tx + x0 + pf - 2) * hw + s];
-          Affine ar[8];
+    for (int64_t q0 = start + tid / tpr; q0 < end; q0 += kCacheRows * rstep) {
+      uint4 v[kCacheRows];
+      double r[kCacheRows];
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            ar[i].s = (double)gamma[col * 8 + i] * r;
-            ar[i].b = 0.0;
-          }
-          v = activate_packet(v, ar);
+      for (int u = 0; u < kCacheRows; ++u) {
+        const int64_t q = q0 + (int64_t)u * rstep;
+        v[u] = make_uint4(0, 0, 0, 0);
+        r[u] = 0.0;
+        if (q < end && src) {
+          v[u] = src[q * cp + col];
+          if (ACT && rs) r[u] = rs[q];
         }
-      } else if (cache_in) {
-        v = cache_in[(((int64_t)n * 2 + pf) * hw + s) * cp + col];
-      } else {
-        v = make_uint4(0, 0, 0, 0);
       }
-      cache_out[(((int64_t)n * 2 + f) * hw + s) * cp + col] = v;
+#pragma unroll
+      for (int u = 0; u < kCacheRows; ++u) {
+        const int64_t q = q0 + (int64_t)u * rstep;
+        if (q >= end) continue;
+        uint4 o = v[u];
+        if (act) {
+          if (stats) {
+            o = activate_packet(o, a);
+          } else {                                   // the RMS norm: gain (in gamma) * rstd
+            Affine ar[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              ar[i].s = (double)gamma[col * 8 + i] * r[u];
+              ar[i].b = 0.0;
+            }
+            o = activate_packet(o, ar);
+          }
+        }
+        dst[q * cp + col] = o;
+      }
     }
   }
 }
@@ -2235,13 +2262,14 @@ static bool launch_cache_out(const uint16_t* x, sgn_dims d, const uint16_t* cach
   int rstep = 256 / cp;
   if (rstep < 1) rstep = 1;
   const int64_t hw = d.h * d.w;
-  const int64_t positions = 2 * hw;
-  int64_t blocks = (positions + rstep * 8 - 1) / (rstep * 8);
-  if (blocks > 1024) blocks = 1024;
-  int64_t rows = (positions + blocks - 1) / blocks;
+  int64_t blocks = (hw + rstep * 16 - 1) / (rstep * 16);  // 16 rows per thread
+  if (blocks > 2048) blocks = 2048;
+  int64_t rows = (hw + blocks - 1) / blocks;
   rows = (rows + rstep - 1) / rstep * rstep;
-  blocks = (positions + rows - 1) / rows;
-  cache_out_kernel<<<dim3((unsigned)blocks, (unsigned)d.n), 256, 0, stream>>>(
+  blocks = (hw + rows - 1) / rows;
+  const bool act = fuse || rms_rstd;
+  auto kern = act ? cache_out_kernel<true> : cache_out_kernel<false>;
+  kern<<<dim3((unsigned)blocks, (unsigned)d.n, 2), 256, 0, stream>>>(
       reinterpret_cast<const uint4*>(x), reinterpret_cast<const uint4*>(cache_in),
       reinterpret_cast<uint4*>(cache_out), (int)d.t - x0, (int)d.t, x0, hw, cp, rstep, rows,
       fuse ? fuse->stats : nullptr, fuse ? fuse->gamma : rms_gain, fuse ? fuse->beta : nullptr,
