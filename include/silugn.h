@@ -37,7 +37,7 @@ enum {
   SGN_EINVAL = -1,      /* bad size, null required pointer, unsupported shape */
   SGN_EALIGN = -2,      /* a tensor pointer is not 16-byte aligned */
   SGN_EALIAS = -3,      /* an output overlaps an input it may not overlap */
-  SGN_ELAUNCH = -4,     /* the HIP runtime refused a launch (message has the HIP error) */
+  SGN_ELAUNCH = -4,     /* a launch failed (message has the HIP error), or the problem exceeds one launch's grid */
   SGN_EWORKSPACE = -5   /* workspace missing or smaller than *_workspace() asks for */
 };
 

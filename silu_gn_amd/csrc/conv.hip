@@ -2234,7 +2234,8 @@ static bool launch_conv(const TileCfg& cfg, ConvParams& p, int64_t n_samples, in
   p.tiles_n = (p.K + cfg.bn - 1) / cfg.bn;
   const int64_t tiles_f = ((int64_t)p.H * p.W + cfg.bm - 1) / cfg.bm;
   const int64_t nb = tiles_f * p.T * p.tiles_n * phases * n_samples;
-  if (tiles_f > (1 << 30) || nb >= (int64_t)1 << 31) {
+  // A launch holds fewer than 2^32 work-items.
+  if (tiles_f > (1 << 30) || nb * cfg.threads >= (int64_t)1 << 32) {
     set_error("%s: problem too large for one launch", fn);
     return false;
   }
@@ -2958,6 +2959,10 @@ static bool wino_shape_ok(sgn_dims d, int k, const char* fn) {
   if (!conv_shape_ok(d, k, fn)) return false;
   if (k <= 128 || k % 8 != 0) {
     set_error("%s: K=%d must be a multiple of 8 above 128 (the slab kernel's tiles)", fn, k);
+    return false;
+  }
+  if (d.t + 2 > 65535) {                             // the transforms' grids take a frame per y index
+    set_error("%s: T=%lld exceeds the transforms' limit of 65533 frames", fn, (long long)d.t);
     return false;
   }
   const int64_t tp = ((d.h + 3) / 4) * ((d.w + 3) / 4);

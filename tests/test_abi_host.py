@@ -400,6 +400,7 @@ def test_winograd_rejects():
     assert need > 0
     assert lib.causal_conv3d_winograd_workspace(D(c=64), 128) == 0                 # K <= 128
     assert lib.causal_conv3d_winograd_workspace(D(c=72), 256) == 0                 # C % 64
+    assert lib.causal_conv3d_winograd_workspace(D(t=65534, c=64), 256) == 0        # T + 2 frames per grid
     _err(lib.causal_conv3d_winograd(FAKE, D(), None, far, 120, None, None, far + (1 << 30), None, ws, need, None),
          EINVAL)                                                                      # K % 8, K <= 128
     _err(lib.causal_conv3d_winograd(None, D(), None, far, 256, None, None, far + (1 << 30), None, ws, need, None),
@@ -415,3 +416,13 @@ def test_winograd_rejects():
     _err(lib.winograd_prepare_weights(None, 4, 64, FAKE), EINVAL)
     buf = np.zeros(36 * 4 * 3 * 64, dtype=np.uint16)
     _err(lib.winograd_prepare_weights(buf.ctypes.data, 4, 64, buf.ctypes.data + 64), EALIAS)
+
+
+def test_conv_too_large_for_one_launch():
+    """A shape every check admits (4e12 elements) whose tile grid would exceed 2^32 work-items:
+    refused on the host with SGN_ELAUNCH before any HIP call."""
+    lib = sga.load_library()
+    d = sga.sgn_dims(1, 62500, 1000, 1000, 64)
+    _err(lib.causal_conv3d(FAKE, d, None, FAKE + (1 << 45), 64, None, None, None, FAKE + (1 << 44), None, None),
+         -4)
+    assert "too large" in lib.sgn_last_error().decode()
