@@ -2916,12 +2916,12 @@ extern "C" int head_conv_d2s(const uint16_t* x, sgn_dims d, const uint16_t* cach
     // The dedicated head kernel: one workgroup per (sample, row pair, 48 columns).
     const int wblocks = (p.W + 16 * kHeadSeg - 1) / (16 * kHeadSeg);
     const int64_t nb = (int64_t)d.n * ((p.H + kHeadOut - 1) / kHeadOut) * wblocks;
-    if (nb >= ((int64_t)1 << 31)) {
+    const int nw = p.C / 32;
+    if (nb * nw * 64 >= ((int64_t)1 << 32)) {        // a launch holds fewer than 2^32 work-items
       set_error("%s: problem too large for one launch", fn);
       return SGN_ELAUNCH;
     }
     p.nblocks = (int)nb;
-    const int nw = p.C / 32;
     const int lds = head_lds_bytes(nw);
     const void* fn_ptr = nw == 4 ? (const void*)head_kernel<4> : (const void*)head_kernel<8>;
     hipError_t e = hipFuncSetAttribute(fn_ptr, hipFuncAttributeMaxDynamicSharedMemorySize, lds);

@@ -420,9 +420,13 @@ def test_winograd_rejects():
 
 def test_conv_too_large_for_one_launch():
     """A shape every check admits (4e12 elements) whose tile grid would exceed 2^32 work-items:
-    refused on the host with SGN_ELAUNCH before any HIP call."""
+    refused on the host with SGN_ELAUNCH before any HIP call (the slab conv's and the head's grids)."""
     lib = sga.load_library()
     d = sga.sgn_dims(1, 62500, 1000, 1000, 64)
     _err(lib.causal_conv3d(FAKE, d, None, FAKE + (1 << 45), 64, None, None, None, FAKE + (1 << 44), None, None),
          -4)
+    assert "too large" in lib.sgn_last_error().decode()
+    # the head kernel's grid (one workgroup per sample, row pair and 48 columns) likewise
+    d = sga.sgn_dims(7000, 1, 2048, 2048, 128)
+    _err(lib.head_conv_d2s(FAKE, d, None, FAKE + (1 << 45), None, None, 0, FAKE + (1 << 44), None, None), -4)
     assert "too large" in lib.sgn_last_error().decode()
