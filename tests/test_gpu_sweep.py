@@ -7,7 +7,9 @@ below 128 and K % 8 != 0 (the generic tile), one- and multi-tile frames, ragged 
 T = 1, two samples, with or without cache, bias and residual.
 
 Gates as in the fixed tests: relative L2 <= 1e-2 and max abs <= 4e-2 against the unrounded
-oracle; cache_out bit-exact; the fused GroupNorm form bitwise equal to apply-then-conv.
+oracle; cache_out bit-exact; the fused GroupNorm form bitwise equal to apply-then-conv; the
+conv with the next norm's statistics bitwise equal to the plain conv, its statistics equal
+to gn_silu_stats of its output up to fp64 summation order.
 """
 import math
 
@@ -58,6 +60,14 @@ def test_conv_sweep(i):
     dev = lambda v: v.to(DEV) if v is not None else None   # noqa: E731
     co = torch.empty((n, 2, h, w, c), dtype=torch.bfloat16, device=DEV)
     y = sga.causal_conv3d(dev(a), dev(wt), dev(ci), dev(b), dev(r), cache_out=co)
+    # the same conv emitting the next GroupNorm's statistics of y (from the epilogue where
+    # K / G allows, else by a statistics pass over y): y bitwise, the statistics against
+    # gn_silu_stats(y)
+    # (GroupNorm takes K % 8 == 0: 8-channel packets)
+    gy = next((g_ for g_ in range(32, 0, -1) if sga.gn_silu_eligible((n, t, h, w, k), g_)), None)
+    if gy is not None:
+        y_s, st_y = sga.causal_conv3d_next_stats(dev(a), dev(wt), gy, dev(ci), dev(b), dev(r))
+        ref_y = sga.gn_silu_stats(y_s, gy)
     if fused:
         # the same conv with GroupNorm+SiLU in its operand load == apply, then the conv
         gamma = sg.normal((c,), seed, sg.GAMMA1, std=0.1, mean=1.0, dtype=torch.float32).to(DEV)
@@ -75,6 +85,9 @@ def test_conv_sweep(i):
                                      b.numpy() if bias else None, vals(r) if res else None)
     assert_conv_close(bits(y), o, "conv sweep %d" % i)
     assert np.array_equal(vals(co), cache_o)
+    if gy is not None:
+        assert np.array_equal(bits(y_s), bits(y))
+        np.testing.assert_allclose(st_y.cpu().numpy(), ref_y.cpu().numpy(), rtol=1e-12, atol=1e-14)
     if fused:
         assert np.array_equal(bits(y_f), bits(y_a))
         assert np.array_equal(bits(co_f), bits(co_a))
