@@ -1,5 +1,6 @@
 """Seeded sweeps of small shapes: every entry point on many shape combinations the fixed cases
-do not name, against the fp64 oracle.
+do not name, against the fp64 oracle. The Winograd form, the phases with the DupUp3D
+shortcut and the RMS norm in the operand load run through their fixed-case tests' checks.
 
 Each case draws its shape and options from its own seed, so a failure names a reproducible
 case (printed before the launch). The draws cover both kernels of each operation: K above and
@@ -164,3 +165,46 @@ def test_time_upsample_sweep(i):
     if o.shape[1] > start:
         assert_conv_close(yb[:, start:], o[:, start:], "time_upsample sweep %d" % i)
     assert np.array_equal(bits(co), bits(torch.from_numpy(oc).to(torch.bfloat16)))
+
+
+# The entry points with their own fixed-case tests, over drawn shapes through the same checks.
+def _bools(rng, m):
+    return tuple(bool(rng.integers(0, 2)) for _ in range(m))
+
+
+@pytest.mark.parametrize("i", range(8))
+def test_winograd_sweep(i):
+    from tests.test_gpu_winograd import test_winograd_small
+    rng = np.random.default_rng(7900 + i)
+    n, t = int(rng.integers(1, 3)), int(rng.integers(1, 4))
+    h, w = int(rng.integers(1, 15)), int(rng.integers(1, 31))
+    c = _pick(rng, [64, 128, 192, 256])
+    k = _pick(rng, [136, 192, 256, 264, 320])
+    cache, bias, res = _bools(rng, 3)
+    test_winograd_small(n, t, h, w, c, k, cache, bias, res)
+
+
+@pytest.mark.parametrize("i", range(8))
+def test_upsample_shortcut_sweep(i):
+    from tests.test_gpu_upblock import test_upsample_shortcut_small
+    rng = np.random.default_rng(8100 + i)
+    n, ts = int(rng.integers(1, 3)), int(rng.integers(1, 3))
+    h, w = int(rng.integers(1, 12)), int(rng.integers(1, 24))
+    c = _pick(rng, [64, 128])
+    k = _pick(rng, [64, 128, 192, 264] if c == 128 else [64, 128, 192, 256, 264])
+    cs = k * (1 + int(rng.integers(0, 2)))             # the source has K or 2K channels
+    ft = 1 + int(rng.integers(0, 2))
+    first, bias = _bools(rng, 2)
+    test_upsample_shortcut_small(n, ts, h, w, c, k, cs, ft, first, bias)
+
+
+@pytest.mark.parametrize("i", range(8))
+def test_conv_rms_input_sweep(i):
+    from tests.test_gpu_rms import test_conv_rms_input_equals_rms_then_conv
+    rng = np.random.default_rng(8300 + i)
+    n, t = int(rng.integers(1, 3)), int(rng.integers(1, 4))
+    h, w = int(rng.integers(1, 12)), int(rng.integers(1, 30))
+    c = _pick(rng, [64, 128, 192, 256])
+    k = _pick(rng, [12, 64, 96, 192, 256, 264])
+    cache, bias, res = _bools(rng, 3)
+    test_conv_rms_input_equals_rms_then_conv(n, t, h, w, c, k, cache, bias, res)
