@@ -15,7 +15,7 @@ the committed rocprofv3 counter summaries when the kernel's sources are unchange
 they were taken; ``gn_silu`` is gn_silu_stats + gn_silu_apply on the same tensor at 6
 bytes/element against HBM peak; ``rms_silu`` is the output head's RMS norm + SiLU on
 that tensor at 4 bytes/element; ``other_configs`` is the dominant kernel of every
-other workload, launched alone; ``box_ceilings`` is what this GPU sustains for those
+other workload, launched alone; ``gpu_ceilings`` is what this GPU sustains for those
 two resources (libsgnprobe.so: bf16 MFMA with random and with constant operand bits,
 HBM streaming read and copy), with each fraction repeated against it;
 ``cpu_baseline`` is the fp64 oracle on the host over a bounded sample (rank 0, N=1
@@ -439,7 +439,7 @@ def other_configs(index, dev, iters):
     return out
 
 
-def box_ceilings(dev):
+def gpu_ceilings(dev):
     """Sustained bf16 MFMA (random / constant operands) and HBM read / copy rates of this GPU,
     from the probe kernels in libsgnprobe.so (about a second in all)."""
     import ctypes
@@ -539,7 +539,7 @@ def main():
     ap.add_argument("--config", type=int, default=4, choices=sorted(WORKLOADS),
                     help="workload (default 4: the full-resolution residual block, the largest)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-ceilings", action="store_true", help="skip the box-ceiling probes")
+    ap.add_argument("--no-ceilings", action="store_true", help="skip the GPU-ceiling probes")
     ap.add_argument("--no-other-configs", action="store_true",
                     help="skip timing the other workloads' dominant kernels")
     ap.add_argument("--fused", action="store_true",
@@ -656,7 +656,7 @@ def main():
         flushed = {"stats_ms": round(fs, 4), "apply_ms": round(fa, 4),
                    "GB/s": round(gn_bytes / ((fs + fa) * 1e-3) / 1e9, 1)}
         del scratch
-    ceilings = None if args.no_ceilings else box_ceilings(dev)
+    ceilings = None if args.no_ceilings else gpu_ceilings(dev)
     # the kernel the dominant launch runs (the library's dispatch rules)
     if wl.kind == "head":
         kname = "head_kernel" if not args.fused and wl.c in (128, 256) else "conv_kernel"
@@ -704,16 +704,16 @@ def main():
     if flushed:
         out["gn_silu"]["cold_cache"] = flushed
     if ceilings:
-        out["box_ceilings"] = ceilings
-        out["roofline"]["frac_of_box_mfma_random"] = round(achieved / ceilings["mfma_bf16_random_TFLOP/s"], 4)
-        # the box's rate for this access pattern: the stats' 2 B/element at the read
+        out["gpu_ceilings"] = ceilings
+        out["roofline"]["frac_of_mfma_random"] = round(achieved / ceilings["mfma_bf16_random_TFLOP/s"], 4)
+        # this GPU's rate for this access pattern: the stats' 2 B/element at the read
         # ceiling, the apply's 4 B/element at the copy ceiling
-        box_s = (2.0 * x.numel() / (ceilings["hbm_read_GB/s"] * 1e9) +
+        ceil_s = (2.0 * x.numel() / (ceilings["hbm_read_GB/s"] * 1e9) +
                  4.0 * x.numel() / (ceilings["hbm_copy_GB/s"] * 1e9))
-        out["gn_silu"]["box_GB/s"] = round(gn_bytes / box_s / 1e9, 1)
-        out["gn_silu"]["frac_of_box"] = round(gn_gbps / (gn_bytes / box_s / 1e9), 4)
+        out["gn_silu"]["ceiling_GB/s"] = round(gn_bytes / ceil_s / 1e9, 1)
+        out["gn_silu"]["frac_of_ceiling"] = round(gn_gbps / (gn_bytes / ceil_s / 1e9), 4)
         if rms_ms:
-            out["rms_silu"]["frac_of_box"] = round(rms_gbps / ceilings["hbm_copy_GB/s"], 4)
+            out["rms_silu"]["frac_of_ceiling"] = round(rms_gbps / ceilings["hbm_copy_GB/s"], 4)
     # HBM bytes per launch of the two GroupNorm kernels from their committed counter summaries
     # (FETCH_SIZE + WRITE_SIZE of the same step's launches), while gn.hip is unchanged
     gs, ga = read_traffic("gn_stats_partial_" + wl.name), read_traffic("gn_apply_kernel_" + wl.name)
