@@ -47,7 +47,7 @@ def _conv_case(i):
     return n, t, h, w, c, k, cache, bias, res, fused
 
 
-@pytest.mark.parametrize("i", range(24))
+@pytest.mark.parametrize("i", range(48))
 def test_conv_sweep(i):
     n, t, h, w, c, k, cache, bias, res, fused = _conv_case(i)
     print("case conv sweep", i, (n, t, h, w, c, k), "cache", cache, "bias", bias, "res", res,
@@ -94,7 +94,7 @@ def test_conv_sweep(i):
         assert np.array_equal(bits(co_f), bits(co_a))
 
 
-@pytest.mark.parametrize("i", range(12))
+@pytest.mark.parametrize("i", range(20))
 def test_upsample_sweep(i):
     rng = np.random.default_rng(7300 + i)
     n, t = int(rng.integers(1, 3)), int(rng.integers(1, 3))
@@ -115,7 +115,7 @@ def test_upsample_sweep(i):
     assert_conv_close(bits(y), o, "upsample sweep %d" % i)
 
 
-@pytest.mark.parametrize("i", range(10))
+@pytest.mark.parametrize("i", range(16))
 def test_head_sweep(i):
     rng = np.random.default_rng(7500 + i)
     n, t = int(rng.integers(1, 3)), int(rng.integers(1, 5))
@@ -138,7 +138,7 @@ def test_head_sweep(i):
     assert np.array_equal(bits(co), bits(torch.from_numpy(oc).to(torch.bfloat16)))
 
 
-@pytest.mark.parametrize("i", range(10))
+@pytest.mark.parametrize("i", range(16))
 def test_time_upsample_sweep(i):
     rng = np.random.default_rng(7700 + i)
     n, t = int(rng.integers(1, 3)), int(rng.integers(1, 5))
@@ -172,7 +172,7 @@ def _bools(rng, m):
     return tuple(bool(rng.integers(0, 2)) for _ in range(m))
 
 
-@pytest.mark.parametrize("i", range(8))
+@pytest.mark.parametrize("i", range(12))
 def test_winograd_sweep(i):
     from tests.test_gpu_winograd import test_winograd_small
     rng = np.random.default_rng(7900 + i)
@@ -184,7 +184,7 @@ def test_winograd_sweep(i):
     test_winograd_small(n, t, h, w, c, k, cache, bias, res)
 
 
-@pytest.mark.parametrize("i", range(8))
+@pytest.mark.parametrize("i", range(12))
 def test_upsample_shortcut_sweep(i):
     from tests.test_gpu_upblock import test_upsample_shortcut_small
     rng = np.random.default_rng(8100 + i)
@@ -198,7 +198,7 @@ def test_upsample_shortcut_sweep(i):
     test_upsample_shortcut_small(n, ts, h, w, c, k, cs, ft, first, bias)
 
 
-@pytest.mark.parametrize("i", range(8))
+@pytest.mark.parametrize("i", range(12))
 def test_conv_rms_input_sweep(i):
     from tests.test_gpu_rms import test_conv_rms_input_equals_rms_then_conv
     rng = np.random.default_rng(8300 + i)
